@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+A step is one call of the verify hot path on one batch of synthetic input
+that is already resident in device memory.  The default workload is the
+linear verify B=32, gamma=5, V=32000 bf16 (160 draft positions per step).
+Other workloads (--workload) measure the remaining configurations.
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by
+torch.cuda.synchronize().  The dominant kernel's duration comes from HIP
+events recorded on the call's own stream around that kernel, in every
+timed step (one-shot hook of the library, or events around the call when
+the call is one kernel).  Inputs rotate over enough copies to exceed the
+256 MB Infinity Cache, so the logits come from HBM.
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("verified draft positions/sec + achieved HBM GB/s (% of peak), "
+          "B×γ×V verify")
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="linear_v32k",
+                    choices=["linear_v1000", "linear_v32k", "linear_v128k", "bimodal_v152k",
+                             "tree_v32k", "attn_tree"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="per-launch HBM bytes measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def copies_for(nbytes):
+    return max(1, min(64, -(-2 * MALL_BYTES // max(nbytes, 1))))
+
+
+def to_dev_logits(torch, arr, dtype_code):
+    if dtype_code == 1:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def cpu_baseline_linear(d, seconds):
+    """The oracle on a bounded sample of the same workload: whole batch rows until ~seconds."""
+    import oracle
+    off = d["offsets"]
+    B = len(off) - 1
+    done_pos = 0
+    rows = 0
+    t0 = time.perf_counter()
+    b = 0
+    while time.perf_counter() - t0 < seconds and rows < 10 * B:
+        bb = b % B
+        o0, o1 = int(off[bb]), int(off[bb + 1])
+        t = o0 + bb
+        oracle.verify_linear(d["target"][t:t + o1 - o0 + 1], d["draft"][o0:o1], d["dtype"],
+                             np.array([0, o1 - o0]), d["tokens"][o0:o1],
+                             d["temp_target"][bb:bb + 1], d["temp_draft"][bb:bb + 1],
+                             seed=0, step=0, row_ids=np.array([bb]))
+        done_pos += o1 - o0
+        rows += 1
+        b += 1
+    dt = time.perf_counter() - t0
+    return dict(value=done_pos / dt, unit="verified draft positions/s", cores=1, kind="oracle",
+                sample="%d batch rows (%d draft positions) of the same workload in %.1f s, "
+                       "single-threaded NumPy float64" % (rows, done_pos, dt))
+
+
+def cpu_baseline_tree(d, seconds):
+    import oracle
+    B = d["B"]
+    t0 = time.perf_counter()
+    rows = nodes = 0
+    while time.perf_counter() - t0 < seconds and rows < 10 * B:
+        b = rows % B
+        oracle.verify_tree_topk(d["target"][b:b + 1], d["dtype"], d["parents"][b:b + 1],
+                                d["tokens"][b:b + 1], d["n_nodes"][b:b + 1],
+                                d["temp_target"][b:b + 1], row_ids=np.array([b]))
+        nodes += int(d["n_nodes"][b]) - 1
+        rows += 1
+    dt = time.perf_counter() - t0
+    return dict(value=nodes / dt, unit="verified draft nodes/s", cores=1, kind="oracle",
+                sample="%d trees (%d draft nodes) of the same workload in %.1f s, "
+                       "single-threaded NumPy float64" % (rows, nodes, dt))
+
+
+def cpu_baseline_attn(q, k, v, L, parents, seconds):
+    import oracle
+    B, H, N, dd = q.shape
+    t0 = time.perf_counter()
+    heads = 0
+    while time.perf_counter() - t0 < seconds and heads < B * H:
+        b, h = divmod(heads, H)
+        mask = oracle.ancestor_mask(parents[b], N)
+        oracle.attention_head(oracle.bf16_bits_to_f64(q[b, h]), oracle.bf16_bits_to_f64(k[b, h]),
+                              oracle.bf16_bits_to_f64(v[b, h]), int(L[b]), mask, dd ** -0.5)
+        heads += 1
+    dt = time.perf_counter() - t0
+    threads = os.environ.get("OMP_NUM_THREADS")
+    return dict(value=heads * N / dt, unit="verified query tokens/s",
+                cores=int(threads) if threads else len(os.sched_getaffinity(0)), kind="oracle",
+                sample="%d (b, h) heads of the same workload in %.1f s, NumPy float64 "
+                       "(BLAS matmul threads)" % (heads, dt))
+
+
+def load_traffic(path, workload):
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        return t.get(workload)
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import rejection_sampling_verify_04_amd as sv
+
+    torch.cuda.set_device(0)
+    wl = args.workload
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda", 0)
+
+    if wl == "attn_tree":
+        B, H, N, dd, L = 64, 32, 64, 128, 4096
+        tree = synth.tree_v32k(seed=4, B=B, N=N, V=64)
+        q, k, v, pl = synth.attn_tensors(B=B, H=H, N=N, L=L)
+        qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+        kd = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda()
+        vd = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
+        pld = torch.from_numpy(pl).cuda()
+        par = torch.from_numpy(tree["parents"]).cuda()
+        outs = dict(out=torch.empty_like(qd),
+                    lse=torch.empty((B, H, N), dtype=torch.float32, device=dev))
+        kv_bytes = 2 * B * H * (L + N) * dd * 2
+        qo_bytes = 2 * B * H * N * dd * 2
+        alg_bytes = kv_bytes + qo_bytes
+        flops = 0
+        anc = [synth_anc(tree["parents"][b]) for b in range(B)]
+        for b in range(B):
+            keys = L * N + int(sum(anc[b]))
+            flops += 2 * 2 * H * keys * dd
+        units = B * N
+
+        def step(i, ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            sv.verify_attn(qd, kd, vd, pld, par, outputs=outs)
+            if ev is not None:
+                ev[1].record(stream)
+        config = dict(workload=wl, B=B, H=H, N=N, head_dim=dd, prefix_len=L,
+                      mask="tree (64-node best-first top-4 trees)", input_dtype="bf16")
+        unit = "verified query tokens/s"
+        metric = "verify-attention query tokens/sec + achieved HBM GB/s (% of peak)"
+    else:
+        d = synth.WORKLOADS[wl]()
+        per_call = synth.logits_bytes(d)
+        nc = copies_for(per_call)
+        if d["kind"] == "linear":
+            sets = []
+            for c in range(nc):
+                sets.append(dict(
+                    t=to_dev_logits(torch, d["target"], d["dtype"]),
+                    d=to_dev_logits(torch, d["draft"], d["dtype"])))
+            off = torch.from_numpy(d["offsets"].astype(np.int32)).cuda()
+            tok = torch.from_numpy(d["tokens"].astype(np.int32)).cuda()
+            tt = torch.from_numpy(d["temp_target"]).cuda()
+            td = torch.from_numpy(d["temp_draft"]).cuda()
+            total = int(d["offsets"][-1])
+            Bn = d["B"]
+            outs = dict(num_accepted=torch.empty(Bn, dtype=torch.int32, device=dev),
+                        out_tokens=torch.empty(total + Bn, dtype=torch.int32, device=dev),
+                        p_at_draft=torch.empty(total, dtype=torch.float32, device=dev),
+                        q_at_draft=torch.empty(total, dtype=torch.float32, device=dev),
+                        row_status=torch.empty(Bn, dtype=torch.int32, device=dev))
+            ws = torch.empty(sv.linear_workspace_size(Bn, total, d["V"], d["dtype"]),
+                             dtype=torch.uint8, device=dev)
+            units = total
+
+            def step(i, ev=None):
+                s = sets[i % nc]
+                if ev is not None:
+                    sv.profile_next(ev[0], ev[1])
+                sv.verify_linear(s["t"], s["d"], off, tok, tt, td, seed=0, step=i, workspace=ws,
+                                 outputs=outs)
+            config = dict(workload=wl, B=Bn, gamma=("ragged 2/4/8" if wl == "bimodal_v152k"
+                                                    else int(d["gammas"][0])),
+                          total_draft=total, V=d["V"],
+                          input_dtype="bf16" if d["dtype"] == 1 else "fp32",
+                          input_copies=nc)
+            unit = "verified draft positions/s"
+        else:
+            sets = [to_dev_logits(torch, d["target"], d["dtype"]) for _ in range(nc)]
+            par = torch.from_numpy(d["parents"]).cuda()
+            tok = torch.from_numpy(d["tokens"]).cuda()
+            nn = torch.from_numpy(d["n_nodes"]).cuda()
+            tt = torch.from_numpy(d["temp_target"]).cuda()
+            Bn, N = d["B"], d["N"]
+            outs = dict(num_accepted=torch.empty(Bn, dtype=torch.int32, device=dev),
+                        path_nodes=torch.empty((Bn, N - 1), dtype=torch.int32, device=dev),
+                        out_tokens=torch.empty((Bn, N), dtype=torch.int32, device=dev),
+                        p_at_node=torch.empty((Bn, N), dtype=torch.float32, device=dev),
+                        row_status=torch.empty(Bn, dtype=torch.int32, device=dev))
+            ws = torch.empty(sv.tree_workspace_size(Bn, N, d["V"], d["dtype"]),
+                             dtype=torch.uint8, device=dev)
+            units = int(d["n_nodes"].sum()) - Bn
+
+            def step(i, ev=None):
+                if ev is not None:
+                    sv.profile_next(ev[0], ev[1])
+                sv.verify_tree(sets[i % nc], par, tok, tt, n_nodes=nn, seed=0, step=i,
+                               workspace=ws, outputs=outs)
+            config = dict(workload=wl, B=Bn, nodes=N, V=d["V"], mode="TOPK", input_dtype="bf16",
+                          input_copies=nc)
+            unit = "verified draft nodes/s"
+        alg_bytes = per_call
+        flops = 0
+        metric = METRIC
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    avg_kern_s = float(np.mean(kern_ms)) / 1e3
+    ms_per_step = wall * 1e3 / args.steps
+
+    achieved = alg_bytes / avg_kern_s / 1e9
+    traffic = load_traffic(args.traffic_json, wl)
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=traffic,
+                kernel=("attn_kernel" if wl == "attn_tree" else "stats_kernel"),
+                algorithmic_bytes_per_launch=int(alg_bytes),
+                avg_kernel_us=round(avg_kern_s * 1e6, 2))
+    if flops:
+        roof["mfma_tflops"] = round(flops / avg_kern_s / 1e12, 2)
+        roof["mfma_util"] = round(flops / avg_kern_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+
+    out = dict(metric=metric, value=round(units / (ms_per_step / 1e3), 1), unit=unit, n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_per_step, 5),
+               higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+               data="synthetic", config=config, roofline=roof)
+    if not args.no_cpu_baseline:
+        if wl == "attn_tree":
+            out["cpu_baseline"] = cpu_baseline_attn(q, k, v, pl, tree["parents"], args.cpu_seconds)
+        elif d["kind"] == "linear":
+            out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline_tree(d, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def synth_anc(parents):
+    """Number of visible new-token keys per query (ancestors plus itself)."""
+    N = len(parents)
+    out = []
+    for i in range(N):
+        c, j = 0, i
+        while j >= 0:
+            c += 1
+            j = int(parents[j]) if j > 0 else -1
+        out.append(c)
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verify step on MI355X (gfx950).
+ *
+ * The verify step of speculative decoding: after a draft model proposes
+ * gamma tokens (or a tree of tokens), the target model scores them in one
+ * forward pass; each draft token d is accepted with probability
+ * min(1, p(d)/q(d)), the first rejection ends the round, and the round
+ * emits one more token drawn from the normalised residual max(0, p - q)
+ * after a rejection, or from p after the last draft when every draft was
+ * accepted.  Sources (page address, section):
+ *   - kwkr.cn/news/620872 §2.1 (one target pass scores all positions under a
+ *     causal mask), §2.3 and §4.1 (accept when p >= q, else with probability
+ *     p/q; the result keeps the target law), §4.3 (greedy decoding turns the
+ *     test into exact match; stop at the first rejection), §5.3 (tree
+ *     verification);
+ *   - cf-1.com/news/5632551 §2.2 (probability-ratio test), §2.3 (gamma,
+ *     alpha, c; expected tokens per round), §3.3 (all-accept / all-reject
+ *     cases and KV rollback), §5.4 (token trees and their mask matrix);
+ *   - blog.lonae.com/posts/2026-draft-model-kv-jDwzYp ("推测解码的工程真相
+ *     2026"), formal-definition paragraph (verify gamma drafts plus one
+ *     bonus position; residual max(0, pi_t - pi_d)), tree-attention
+ *     paragraphs (top-k or sampled children; per-tree causal mask).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is device memory unless stated otherwise, owned by the
+ *     caller.  The library allocates nothing and keeps no state between
+ *     calls (the one-shot timing hook below aside); scratch space is the
+ *     caller's workspace.
+ *   - Calls are asynchronous on `stream` and never synchronise the host.
+ *     Argument checks that need no device data happen on the host before
+ *     anything is enqueued; a non-zero return means nothing was enqueued,
+ *     except SV_ERR_HIP, which reports a failed kernel launch.
+ *   - Contract violations found in device data (a token outside [0, V), a
+ *     bad offset or parent, a negative or non-finite temperature, a row whose
+ *     logits have no finite maximum) are reported per batch row in
+ *     `row_status` and do not stop the other rows.  An error row gets
+ *     num_accepted = -1 and -1 in every output token slot it owns.  NaN
+ *     logits are undefined behaviour (no fault, unspecified outputs).
+ *   - Outputs are a pure function of (inputs, seed, step, row ids): the same
+ *     call gives the same bits on every run and for any launch geometry.
+ *   - Draft and target share one vocabulary of size V.
+ *   - A workspace must not be shared by calls that may run concurrently.
+ *
+ * Randoms: Philox-4x32-10 (Salmon et al., SC'11), key = (seed low word,
+ * seed high word), counter = (slot, row id, step low word, step high word).
+ * u_acc = (x0 >> 8) * 2^-24 decides the acceptance of the token in `slot`;
+ * u_smp = (x1 >> 8) * 2^-24 drives the inverse-CDF draw made after `slot`.
+ * Slot 0 is the last committed token; draft d_i of the linear verify sits in
+ * slot i + 1; a tree node's slot is its node index.  The row id is
+ * row_ids[b] (or b when row_ids is NULL), never a packed index, so packing
+ * does not change a row's randoms.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define SV_OK 0
+#define SV_ERR_INVALID_ARG (-1) /* null pointer, bad size, dtype, N > 64, ... */
+#define SV_ERR_UNSUPPORTED (-2) /* valid request this build does not implement */
+#define SV_ERR_WORKSPACE (-3)   /* workspace missing, too small or misaligned */
+#define SV_ERR_HIP (-4)         /* a kernel launch failed */
+
+/* Logit element types. */
+#define SV_F32 0
+#define SV_BF16 1
+
+/* Tree candidate modes. */
+#define SV_TREE_TOPK 0        /* children are the draft's deterministic top-k */
+#define SV_TREE_SAMPLED_WOR 1 /* children drawn from q without replacement (not built yet) */
+
+/* Per-row status bits.  Bits 0-7 are errors, bits 8+ are warnings. */
+#define SV_ROW_OK 0
+#define SV_ROW_BAD_TOKEN 1      /* a draft / node token outside [0, V) */
+#define SV_ROW_BAD_SHAPE 2      /* bad offsets (gamma_b < 0 or > 64) or parents / n_nodes */
+#define SV_ROW_NONFINITE 4      /* a logit row without a finite maximum */
+#define SV_ROW_BAD_TEMP 8       /* negative or non-finite temperature */
+#define SV_ROW_WARN_QZERO 256   /* q(d) = 0 for a draft token (ratio taken as +inf or 0) */
+#define SV_ROW_WARN_RZERO 512   /* rejection with zero residual mass: drew from p instead */
+
+#define SV_MAX_GAMMA 64
+#define SV_MAX_TREE_NODES 64
+#define SV_WORKSPACE_ALIGN 256
+
+/* Library version, (major << 16) | minor. */
+int spec_verify_version(void);
+
+/* Static, human-readable text for a return code. */
+const char* spec_verify_status_string(int status);
+
+/*
+ * Linear verify (kwkr §2.3, §4.1, §4.3; cf-1 §2.2; lonae formal-definition
+ * paragraph).  Batch row b has gamma_b = draft_offsets[b+1] - draft_offsets[b]
+ * draft tokens (0 <= gamma_b <= 64).
+ *
+ *   target_logits  [sum_b (gamma_b + 1), V], row-major, `dtype` elements.
+ *                  The gamma_b + 1 target rows of b start at row
+ *                  draft_offsets[b] + b; row i is the target's distribution
+ *                  for slot i + 1 (row gamma_b follows the last draft).
+ *   draft_logits   [total_draft, V]; the draft rows of b start at row
+ *                  draft_offsets[b]; row i is the distribution d_i was drawn
+ *                  from.
+ *   dtype          SV_F32 or SV_BF16.  Rows whose byte length is not a
+ *                  multiple of 16 are handled, more slowly.
+ *   B, V           batch rows (>= 0; 0 is a no-op) and vocabulary size (>= 1).
+ *   total_draft    draft_offsets[B] (host copy, sizes the launch).
+ *   draft_offsets  [B + 1] int32, non-decreasing, draft_offsets[0] = 0.
+ *   draft_tokens   [total_draft] int32 draft token ids.
+ *   temp_target, temp_draft  [B] float temperatures; 0 means greedy (a
+ *                  one-hot at the first maximum, kwkr §4.3).
+ *   seed, step, row_ids  Philox key / counter words (row_ids may be NULL).
+ * Outputs:
+ *   num_accepted   [B] int32: accepted drafts, or -1 for an error row.
+ *   out_tokens     [sum_b (gamma_b + 1)] int32, same packing as the target
+ *                  rows: the accepted drafts, then the residual or bonus
+ *                  token, then -1.
+ *   p_at_draft, q_at_draft  [total_draft] float p_i(d_i), q_i(d_i); may be NULL.
+ *   row_status     [B] int32 SV_ROW_* bits; may be NULL.
+ *   workspace      device scratch of spec_verify_linear_workspace_size()
+ *                  bytes, SV_WORKSPACE_ALIGN-aligned; contents need no
+ *                  initialisation and are clobbered.
+ * Returns SV_OK or a negative SV_ERR_* code.
+ */
+size_t spec_verify_linear_workspace_size(int B, int total_draft, int V, int dtype);
+int spec_verify_linear(const void* target_logits, const void* draft_logits, int dtype,
+                       int B, int V, int total_draft,
+                       const int32_t* draft_offsets, const int32_t* draft_tokens,
+                       const float* temp_target, const float* temp_draft,
+                       uint64_t seed, uint64_t step, const uint32_t* row_ids,
+                       int32_t* num_accepted, int32_t* out_tokens,
+                       float* p_at_draft, float* q_at_draft, int32_t* row_status,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Tree verify (kwkr §5.3; cf-1 §5.4; lonae tree-attention paragraphs), TOPK
+ * mode: the children of a node are tested in node-index order; child c_j is
+ * accepted when u_acc(c_j) < p'(c_j), p' being the node's target
+ * distribution with the tokens of the already-rejected siblings removed and
+ * renormalised; on acceptance the walk descends; when every child is
+ * rejected the emitted token is drawn from p with all of them removed; at a
+ * leaf the bonus token is drawn from p (draws use u_smp of the stop node).
+ *
+ *   target_logits  [B, N, V] `dtype`; row n is the target's distribution for
+ *                  the token that follows node n (node 0 = root = the last
+ *                  committed token).
+ *   draft_logits   [B, N, V] or NULL; read only by SV_TREE_SAMPLED_WOR.
+ *   N              nodes per tree including the root, 1..64.
+ *   parents        [B, N] int32; parents[b][0] is ignored; for 0 < i <
+ *                  n_nodes[b], 0 <= parents[b][i] < i.
+ *   node_tokens    [B, N] int32; node 0's entry is ignored.
+ *   n_nodes        [B] int32 in 1..N, or NULL for N everywhere.
+ *   cand_mode      SV_TREE_TOPK (SV_TREE_SAMPLED_WOR returns SV_ERR_UNSUPPORTED).
+ *   temp_target    [B]; temp_draft [B] or NULL (read by SAMPLED_WOR only).
+ * Outputs:
+ *   num_accepted   [B] depth of the accepted path, -1 for an error row.
+ *   path_nodes     [B, N-1] node ids of the accepted path, then -1.
+ *   out_tokens     [B, N] tokens of the accepted path, then the drawn token, then -1.
+ *   p_at_node      [B, N] p_parent(n)(token_n) for 0 < n < n_nodes, else 0; may be NULL.
+ *   row_status     [B]; may be NULL.
+ *   workspace      spec_verify_tree_workspace_size() bytes, as for the linear call.
+ */
+size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype);
+int spec_verify_tree(const void* target_logits, const void* draft_logits, int dtype,
+                     int B, int N, int V,
+                     const int32_t* parents, const int32_t* node_tokens, const int32_t* n_nodes,
+                     int cand_mode, const float* temp_target, const float* temp_draft,
+                     uint64_t seed, uint64_t step, const uint32_t* row_ids,
+                     int32_t* num_accepted, int32_t* path_nodes, int32_t* out_tokens,
+                     float* p_at_node, int32_t* row_status,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal- or tree-masked verify attention (kwkr §2.1; cf-1 §5.4; lonae
+ * tree-attention paragraphs).  For batch row b with prefix length
+ * L = prefix_len[b] and N query tokens whose keys/values are already stored
+ * at cache slots [L, L+N):
+ *   O[b,h,i] = sum_j softmax_j(Q[b,h,i] . K[b,h,j] * scale + M_ij) V[b,h,j],
+ * j over the prefix [0, L) and over L + t for every new token t that is i
+ * itself or an ancestor of i in the tree given by `parents` (a chain, i.e. a
+ * causal mask, when parents is NULL).  Every head has its own K/V.
+ *
+ *   q              [B, H, N, d] bf16 (after any positional encoding).
+ *   k_cache, v_cache [B, H, S_max, d] bf16.
+ *   prefix_len     [B] int32 with 0 <= L and L + N <= S_max (checked on the
+ *                  device: a violating row gets zero output and NaN LSE).
+ *   parents        [B, N] int32 or NULL; same rules as spec_verify_tree.
+ *   N 1..64, d 128, H >= 1, scale usually 1/sqrt(d).
+ *   out            [B, H, N, d] bf16.
+ *   lse            [B, H, N] float natural-log sum of exp(scores); may be NULL.
+ * Arithmetic: bf16 MFMA products, float32 accumulation and softmax; the
+ * softmax weights are rounded to bf16 for the P.V product.
+ */
+int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* prefix_len, const int32_t* parents,
+                     int B, int H, int N, int d, int S_max, float scale,
+                     void* out, float* lse, hipStream_t stream);
+
+/*
+ * Diagnostic: the raw Philox-4x32-10 words the verify calls draw, for
+ * n_rows rows (row id row_ids[r], or r when NULL) and slots 0..n_slots-1:
+ * out_words[(r * n_slots + s) * 4 + w] = word w of counter
+ * (s, row id, step low, step high) under key (seed low, seed high).
+ */
+int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids,
+                             int n_rows, int n_slots, uint32_t* out_words, hipStream_t stream);
+
+/*
+ * Diagnostic timing hook (for benchmarks and profilers): the next
+ * spec_verify_linear or spec_verify_tree call records `begin` on its stream
+ * right before its vocabulary pass and `end` right after it, then forgets
+ * both.  Either may be NULL to clear the hook.  Process-wide and not
+ * thread-safe; it changes no output and skips no work.
+ */
+int spec_verify_profile_next(hipEvent_t begin, hipEvent_t end);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

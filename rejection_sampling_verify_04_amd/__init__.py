@@ -1,0 +1,257 @@
+"""Python binding of libspecverify.so, the MI355X verify step of speculative decoding.
+
+Argument marshalling only: every step of the verify runs in the HIP kernels
+behind the C ABI declared in include/spec_verify.h.  PyTorch supplies device
+memory and the current stream.  There is no fallback: if the library is not
+built, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecverify.so")
+
+SV_OK = 0
+SV_F32 = 0
+SV_BF16 = 1
+SV_TREE_TOPK = 0
+SV_TREE_SAMPLED_WOR = 1
+SV_WORKSPACE_ALIGN = 256
+
+ROW_BAD_TOKEN = 1
+ROW_BAD_SHAPE = 2
+ROW_NONFINITE = 4
+ROW_BAD_TEMP = 8
+ROW_WARN_QZERO = 256
+ROW_WARN_RZERO = 512
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s: %s (status %d)" % (what, status_string(status), status))
+        self.status = status
+
+
+def library():
+    """Load libspecverify.so (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libspecverify.so is not built; run "
+                           "`python -m rejection_sampling_verify_04_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
+    L.spec_verify_version.restype = i32
+    L.spec_verify_status_string.restype = ctypes.c_char_p
+    L.spec_verify_status_string.argtypes = [i32]
+    L.spec_verify_linear_workspace_size.restype = sz
+    L.spec_verify_linear_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.spec_verify_linear.restype = i32
+    L.spec_verify_linear.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, u64, u64, vp,
+                                     vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_tree_workspace_size.restype = sz
+    L.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.spec_verify_tree.restype = i32
+    L.spec_verify_tree.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, u64, u64,
+                                   vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_attn.restype = i32
+    L.spec_verify_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
+                                   vp, vp, vp]
+    L.spec_verify_profile_next.restype = i32
+    L.spec_verify_profile_next.argtypes = [vp, vp]
+    L.spec_verify_philox_words.restype = i32
+    L.spec_verify_philox_words.argtypes = [u64, u64, vp, i32, i32, vp, vp]
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return library().spec_verify_status_string(int(status)).decode()
+
+
+def version():
+    return library().spec_verify_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a CUDA tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+def _logit_code(t, name):
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise ValueError("%s must be bfloat16 or float32" % name)
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(int(nbytes), SV_WORKSPACE_ALIGN), dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace", torch.uint8)
+    return workspace
+
+
+def linear_workspace_size(B, total_draft, V, dtype_code=SV_BF16):
+    return library().spec_verify_linear_workspace_size(B, total_draft, V, dtype_code)
+
+
+def tree_workspace_size(B, N, V, dtype_code=SV_BF16):
+    return library().spec_verify_tree_workspace_size(B, N, V, dtype_code)
+
+
+def verify_linear(target_logits, draft_logits, draft_offsets, draft_tokens, temp_target,
+                  temp_draft, seed=0, step=0, row_ids=None, want_probs=True, workspace=None,
+                  outputs=None, stream=None):
+    """Linear verify (see spec_verify_linear).  Returns a dict of output tensors.
+
+    target_logits [sum(gamma_b + 1), V] and draft_logits [sum(gamma_b), V]
+    (bf16 or fp32, same dtype); draft_offsets [B+1], draft_tokens
+    [sum(gamma_b)] int32; temp_target, temp_draft [B] float32; row_ids [B]
+    int32 (reinterpreted as uint32) or None.
+    """
+    L = library()
+    _dev(target_logits, "target_logits")
+    _dev(draft_logits, "draft_logits", target_logits.dtype)
+    dt = _logit_code(target_logits, "target_logits")
+    _dev(draft_offsets, "draft_offsets", torch.int32)
+    _dev(draft_tokens, "draft_tokens", torch.int32)
+    _dev(temp_target, "temp_target", torch.float32)
+    _dev(temp_draft, "temp_draft", torch.float32)
+    if row_ids is not None:
+        _dev(row_ids, "row_ids", torch.int32)
+    B = draft_offsets.numel() - 1
+    total = draft_tokens.numel()
+    V = target_logits.shape[-1]
+    dev = target_logits.device
+    if outputs is None:
+        outputs = dict(
+            num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+            out_tokens=torch.empty(total + B, dtype=torch.int32, device=dev),
+            row_status=torch.empty(B, dtype=torch.int32, device=dev))
+        if want_probs:
+            outputs["p_at_draft"] = torch.empty(total, dtype=torch.float32, device=dev)
+            outputs["q_at_draft"] = torch.empty(total, dtype=torch.float32, device=dev)
+    need = L.spec_verify_linear_workspace_size(B, total, V, dt)
+    ws = _workspace(need, dev, workspace)
+    st = L.spec_verify_linear(
+        _ptr(target_logits), _ptr(draft_logits), dt, B, V, total, _ptr(draft_offsets),
+        _ptr(draft_tokens), _ptr(temp_target), _ptr(temp_draft), int(seed), int(step),
+        _ptr(row_ids), _ptr(outputs["num_accepted"]), _ptr(outputs["out_tokens"]),
+        _ptr(outputs.get("p_at_draft")), _ptr(outputs.get("q_at_draft")),
+        _ptr(outputs.get("row_status")), _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_linear")
+    return outputs
+
+
+def verify_tree(target_logits, parents, node_tokens, temp_target, n_nodes=None, seed=0, step=0,
+                row_ids=None, cand_mode=SV_TREE_TOPK, draft_logits=None, temp_draft=None,
+                want_probs=True, workspace=None, outputs=None, stream=None):
+    """Tree verify (see spec_verify_tree).  target_logits [B, N, V]; parents,
+    node_tokens [B, N] int32; n_nodes [B] int32 or None."""
+    L = library()
+    _dev(target_logits, "target_logits")
+    dt = _logit_code(target_logits, "target_logits")
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, N, V]")
+    B, N, V = target_logits.shape
+    _dev(parents, "parents", torch.int32)
+    _dev(node_tokens, "node_tokens", torch.int32)
+    _dev(temp_target, "temp_target", torch.float32)
+    if n_nodes is not None:
+        _dev(n_nodes, "n_nodes", torch.int32)
+    if row_ids is not None:
+        _dev(row_ids, "row_ids", torch.int32)
+    dev = target_logits.device
+    if outputs is None:
+        outputs = dict(
+            num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+            path_nodes=torch.empty((B, max(N - 1, 1)), dtype=torch.int32, device=dev),
+            out_tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+            row_status=torch.empty(B, dtype=torch.int32, device=dev))
+        if want_probs:
+            outputs["p_at_node"] = torch.empty((B, N), dtype=torch.float32, device=dev)
+    need = L.spec_verify_tree_workspace_size(B, N, V, dt)
+    ws = _workspace(need, dev, workspace)
+    st = L.spec_verify_tree(
+        _ptr(target_logits), _ptr(draft_logits), dt, B, N, V, _ptr(parents), _ptr(node_tokens),
+        _ptr(n_nodes), int(cand_mode), _ptr(temp_target), _ptr(temp_draft), int(seed), int(step),
+        _ptr(row_ids), _ptr(outputs["num_accepted"]), _ptr(outputs["path_nodes"]),
+        _ptr(outputs["out_tokens"]), _ptr(outputs.get("p_at_node")),
+        _ptr(outputs.get("row_status")), _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_tree")
+    return outputs
+
+
+def verify_attn(q, k_cache, v_cache, prefix_len, parents=None, scale=None, want_lse=True,
+                outputs=None, stream=None):
+    """Verify attention (see spec_verify_attn).  q [B,H,N,d], k/v [B,H,S_max,d] bf16."""
+    L = library()
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_cache, "k_cache", torch.bfloat16)
+    _dev(v_cache, "v_cache", torch.bfloat16)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    if parents is not None:
+        _dev(parents, "parents", torch.int32)
+    B, H, N, d = q.shape
+    S_max = k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, H, S_max, d) or tuple(v_cache.shape) != (B, H, S_max, d):
+        raise ValueError("k_cache / v_cache must be [B, H, S_max, d] matching q")
+    if scale is None:
+        scale = d ** -0.5
+    dev = q.device
+    if outputs is None:
+        outputs = dict(out=torch.empty_like(q))
+        if want_lse:
+            outputs["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    st = L.spec_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+                            _ptr(parents), B, H, N, d, S_max, float(scale),
+                            _ptr(outputs["out"]), _ptr(outputs.get("lse")), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_attn")
+    return outputs
+
+
+def profile_next(begin_event, end_event):
+    """Have the next linear/tree call record two torch.cuda.Events around its vocabulary pass."""
+    begin_event.record()   # make sure both HIP events exist
+    end_event.record()
+    library().spec_verify_profile_next(ctypes.c_void_p(begin_event.cuda_event),
+                                       ctypes.c_void_p(end_event.cuda_event))
+
+
+def philox_words(seed, step, n_rows, n_slots, row_ids=None, stream=None):
+    """Raw Philox words [n_rows, n_slots, 4] (uint32 stored in int32)."""
+    L = library()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if row_ids is not None:
+        _dev(row_ids, "row_ids", torch.int32)
+    out = torch.empty((n_rows, n_slots, 4), dtype=torch.int32, device=dev)
+    st = L.spec_verify_philox_words(int(seed), int(step), _ptr(row_ids), n_rows, n_slots,
+                                    _ptr(out), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_philox_words")
+    return out

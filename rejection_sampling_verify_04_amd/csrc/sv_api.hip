@@ -1,0 +1,280 @@
+// C ABI of the verify library: host-side argument checks, workspace layout
+// and kernel launches.  Declarations and contracts are in include/spec_verify.h.
+#include "spec_verify.h"
+#include "sv_common.h"
+#include "sv_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = SV_WORKSPACE_ALIGN;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int n_chunks_for(int V) { return (V + sv::kChunk - 1) / sv::kChunk; }
+
+// Workspace: [partials | chunk masses | per-row counters], each aligned.
+struct Layout {
+  size_t part, mass, counter, total;
+};
+
+Layout layout(long long n_rows, int B, int V) {
+  const int nc = n_chunks_for(V);
+  Layout l;
+  l.part = 0;
+  l.mass = align_up((size_t)n_rows * nc * sizeof(sv::Partial));
+  l.counter = l.mass + align_up((size_t)B * nc * sizeof(double));
+  l.total = l.counter + align_up((size_t)B * sizeof(int));
+  if (l.total == 0) l.total = kAlign;
+  return l;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// One-shot timing hook (spec_verify_profile_next).
+hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
+
+hipError_t launch_stats_timed(int dtype, const sv::StatsArgs& s, long long n_items,
+                              hipStream_t stream) {
+  hipEvent_t b = g_prof_begin, e = g_prof_end;
+  g_prof_begin = g_prof_end = nullptr;
+  if (b && e && hipEventRecord(b, stream) != hipSuccess) return hipErrorUnknown;
+  const hipError_t err = sv::launch_stats(dtype, s, n_items, stream);
+  if (err != hipSuccess) return err;
+  if (b && e && hipEventRecord(e, stream) != hipSuccess) return hipErrorUnknown;
+  return hipSuccess;
+}
+
+int check_workspace(void* ws, size_t bytes, size_t need) {
+  if (!ws || ((uintptr_t)ws % kAlign) != 0 || bytes < need) return SV_ERR_WORKSPACE;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_version(void) { return (0 << 16) | 1; }
+
+const char* spec_verify_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported request";
+    case SV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case SV_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t spec_verify_linear_workspace_size(int B, int total_draft, int V, int dtype) {
+  (void)dtype;
+  if (B < 0 || total_draft < 0 || V < 1) return 0;
+  return layout(2LL * total_draft + B, B, V).total;
+}
+
+int spec_verify_linear(const void* target_logits, const void* draft_logits, int dtype, int B,
+                       int V, int total_draft, const int32_t* draft_offsets,
+                       const int32_t* draft_tokens, const float* temp_target,
+                       const float* temp_draft, uint64_t seed, uint64_t step,
+                       const uint32_t* row_ids, int32_t* num_accepted, int32_t* out_tokens,
+                       float* p_at_draft, float* q_at_draft, int32_t* row_status,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
+  if (B < 0 || V < 1 || total_draft < 0) return SV_ERR_INVALID_ARG;
+  if ((long long)total_draft > (long long)B * SV_MAX_GAMMA) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (n_chunks_for(V) > sv::kMaxChunks) return SV_ERR_UNSUPPORTED;
+  if (!target_logits || !draft_offsets || !temp_target || !temp_draft || !num_accepted ||
+      !out_tokens)
+    return SV_ERR_INVALID_ARG;
+  if (total_draft > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_INVALID_ARG;
+  const long long n_t = (long long)total_draft + B;
+  const long long n_rows = n_t + total_draft;
+  const int nc = n_chunks_for(V);
+  if (n_rows * nc >= (1LL << 31) || (long long)B * nc >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  const Layout l = layout(n_rows, B, V);
+  const int wst = check_workspace(workspace, workspace_bytes, l.total);
+  if (wst != SV_OK) return wst;
+
+  const int es = dtype == SV_BF16 ? 2 : 4;
+  const int vec_ok = ((long long)V * es) % 16 == 0 && aligned16(target_logits) &&
+                     (total_draft == 0 || aligned16(draft_logits));
+  char* ws = (char*)workspace;
+
+  sv::StatsArgs s{};
+  s.rows_a = target_logits;
+  s.rows_b = draft_logits;
+  s.n_a = n_t;
+  s.n_rows = n_rows;
+  s.V = V;
+  s.n_chunks = nc;
+  s.tree = 0;
+  s.offsets = draft_offsets;
+  s.B = B;
+  s.N = 0;
+  s.n_nodes = nullptr;
+  s.temp_a = temp_target;
+  s.temp_b = temp_draft;
+  s.part = (sv::Partial*)(ws + l.part);
+  s.zero = (int*)(ws + l.counter);
+  s.n_zero = B;
+  s.vec_ok = vec_ok;
+  if (launch_stats_timed(dtype, s, n_rows * nc, stream) != hipSuccess) return SV_ERR_HIP;
+
+  sv::LinearArgs f{};
+  f.target = target_logits;
+  f.draft = draft_logits;
+  f.V = V;
+  f.n_chunks = nc;
+  f.B = B;
+  f.total_draft = total_draft;
+  f.n_target_rows = n_t;
+  f.off = draft_offsets;
+  f.tokens = draft_tokens;
+  f.temp_t = temp_target;
+  f.temp_d = temp_draft;
+  f.seed = seed;
+  f.step = step;
+  f.row_ids = row_ids;
+  f.part = s.part;
+  f.mass = (double*)(ws + l.mass);
+  f.counter = (int*)(ws + l.counter);
+  f.num_accepted = num_accepted;
+  f.out_tokens = out_tokens;
+  f.p_at = p_at_draft;
+  f.q_at = q_at_draft;
+  f.row_status = row_status;
+  f.vec_ok = vec_ok;
+  if (sv::launch_linear_finish(dtype, f, (long long)B * nc, stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype) {
+  (void)dtype;
+  if (B < 0 || N < 1 || V < 1) return 0;
+  return layout((long long)B * N, B, V).total;
+}
+
+int spec_verify_tree(const void* target_logits, const void* draft_logits, int dtype, int B,
+                     int N, int V, const int32_t* parents, const int32_t* node_tokens,
+                     const int32_t* n_nodes, int cand_mode, const float* temp_target,
+                     const float* temp_draft, uint64_t seed, uint64_t step,
+                     const uint32_t* row_ids, int32_t* num_accepted, int32_t* path_nodes,
+                     int32_t* out_tokens, float* p_at_node, int32_t* row_status,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)draft_logits;
+  (void)temp_draft;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
+  if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1) return SV_ERR_INVALID_ARG;
+  if (cand_mode == SV_TREE_SAMPLED_WOR) return SV_ERR_UNSUPPORTED;
+  if (cand_mode != SV_TREE_TOPK) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (n_chunks_for(V) > sv::kMaxChunks) return SV_ERR_UNSUPPORTED;
+  if (!target_logits || !parents || !node_tokens || !temp_target || !num_accepted ||
+      !path_nodes || !out_tokens)
+    return SV_ERR_INVALID_ARG;
+  const long long n_rows = (long long)B * N;
+  const int nc = n_chunks_for(V);
+  if (n_rows * nc >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  const Layout l = layout(n_rows, B, V);
+  const int wst = check_workspace(workspace, workspace_bytes, l.total);
+  if (wst != SV_OK) return wst;
+  const int es = dtype == SV_BF16 ? 2 : 4;
+  const int vec_ok = ((long long)V * es) % 16 == 0 && aligned16(target_logits);
+  char* ws = (char*)workspace;
+
+  sv::StatsArgs s{};
+  s.rows_a = target_logits;
+  s.rows_b = nullptr;
+  s.n_a = n_rows;
+  s.n_rows = n_rows;
+  s.V = V;
+  s.n_chunks = nc;
+  s.tree = 1;
+  s.offsets = nullptr;
+  s.B = B;
+  s.N = N;
+  s.n_nodes = n_nodes;
+  s.temp_a = temp_target;
+  s.temp_b = temp_target;
+  s.part = (sv::Partial*)(ws + l.part);
+  s.zero = (int*)(ws + l.counter);
+  s.n_zero = B;
+  s.vec_ok = vec_ok;
+  if (launch_stats_timed(dtype, s, n_rows * nc, stream) != hipSuccess) return SV_ERR_HIP;
+
+  sv::TreeArgs f{};
+  f.target = target_logits;
+  f.V = V;
+  f.n_chunks = nc;
+  f.B = B;
+  f.N = N;
+  f.parents = parents;
+  f.tokens = node_tokens;
+  f.n_nodes = n_nodes;
+  f.temp = temp_target;
+  f.seed = seed;
+  f.step = step;
+  f.row_ids = row_ids;
+  f.part = s.part;
+  f.mass = (double*)(ws + l.mass);
+  f.counter = (int*)(ws + l.counter);
+  f.num_accepted = num_accepted;
+  f.path_nodes = path_nodes;
+  f.out_tokens = out_tokens;
+  f.p_at = p_at_node;
+  f.row_status = row_status;
+  f.vec_ok = vec_ok;
+  if (sv::launch_tree_finish(dtype, f, (long long)B * nc, stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* prefix_len, const int32_t* parents, int B, int H, int N,
+                     int d, int S_max, float scale, void* out, float* lse, hipStream_t stream) {
+  if (B < 0 || H < 1 || N < 1 || N > SV_MAX_TREE_NODES || S_max < N) return SV_ERR_INVALID_ARG;
+  if (d != 128) return SV_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f) || !(scale < __builtin_huge_valf())) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!q || !k_cache || !v_cache || !prefix_len || !out) return SV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return SV_ERR_INVALID_ARG;
+  if ((long long)B * H >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  sv::AttnArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.prefix_len = prefix_len;
+  a.parents = parents;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.S_max = S_max;
+  a.scale_log2 = (float)((double)scale * sv::kLog2e);
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  if (sv::launch_attn(a, stream) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids, int n_rows,
+                             int n_slots, uint32_t* out_words, hipStream_t stream) {
+  if (n_rows < 0 || n_slots < 0) return SV_ERR_INVALID_ARG;
+  if ((long long)n_rows * n_slots == 0) return SV_OK;
+  if (!out_words || !aligned16(out_words)) return SV_ERR_INVALID_ARG;
+  if ((long long)n_rows * n_slots >= (1LL << 31) * 256LL) return SV_ERR_INVALID_ARG;
+  if (sv::launch_philox_words(seed, step, row_ids, n_rows, n_slots, out_words, stream) !=
+      hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_profile_next(hipEvent_t begin, hipEvent_t end) {
+  g_prof_begin = begin;
+  g_prof_end = end;
+  return SV_OK;
+}
+
+}  // extern "C"

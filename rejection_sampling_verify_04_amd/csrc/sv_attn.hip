@@ -1,0 +1,238 @@
+// Tree- or causal-masked verify attention on MFMA (gfx950).
+//
+// One workgroup per (batch row, head); wave w owns query rows 16w..16w+15.
+// Keys stream in tiles of 64 from the cache into LDS (K row-major, V
+// transposed), with the next tile's global loads in flight while the
+// current tile is multiplied.  Per tile and wave:
+//
+//   S^T[64 keys x 16 queries] = K_tile . Q^T    4 key blocks x 4 d-steps of
+//                                               v_mfma_f32_16x16x32_bf16
+//   online softmax per query column (log2 domain), mask from a 64-bit
+//   ancestor set per query for the keys in [L, L+N)
+//   O^T[128 d x 16 queries] += V^T . P^T        8 d blocks x 2 key-steps
+//
+// Keeping keys (and d) on the M side of both products puts every query in
+// one lane column of the accumulator, so the running max, the rescale of O
+// and the row sum need no cross-lane traffic except one 4-way combine at the
+// end.  The key order inside a key-step is permuted identically on both
+// operands of the P.V product so that P can be fed from the S accumulator
+// registers directly.
+//
+// The pass is HBM-bound (64 flop per byte of K/V against a bf16 ridge near
+// 312), so the matrix cores are used because the product is dense, not to
+// reach their peak.  Mask semantics: kwkr.cn/news/620872 §2.1 (causal verify),
+// cf-1.com/news/5632551 §5.4 and the lonae tree-attention paragraphs (tree mask).
+#include "sv_common.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kKT = 64;               // keys per tile
+constexpr int kKsStride = kD + 8;     // bf16 per K row in LDS (16 B pad)
+constexpr int kVtStride = kKT + 8;    // bf16 per V^T row in LDS (16 B pad)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVtStride];
+  __shared__ unsigned long long s_anc[kMaxNodes];
+  __shared__ int s_L, s_ok;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H;
+  const int N = a.N;
+  const long long headKV = (long long)bh * a.S_max * kD;
+  const long long headQ = (long long)bh * N * kD;
+
+  if (tid == 0) {
+    const int L = a.prefix_len[b];
+    s_L = L;
+    s_ok = L >= 0 && (long long)L + N <= (long long)a.S_max;
+  }
+  if (tid < N) {
+    unsigned long long m = 0ull;
+    if (a.parents) {
+      const int* par = a.parents + (long long)b * N;
+      int j = tid;
+      for (int steps = 0; steps < kMaxNodes && j >= 0; ++steps) {
+        m |= 1ull << j;
+        if (j == 0) break;
+        const int p = par[j];
+        if (p < 0 || p >= j) break;  // malformed parent: stop the walk
+        j = p;
+      }
+    } else {
+      m = ~0ull >> (63 - tid);       // chain: every earlier new token
+    }
+    s_anc[tid] = m;
+  }
+  __syncthreads();
+  const int L = s_L;
+  if (!s_ok) {
+    for (int i = tid; i < N * kD; i += kThreads) a.out[headQ + i] = 0;
+    if (a.lse && tid < N) a.lse[(long long)bh * N + tid] = __builtin_nanf("");
+    return;
+  }
+
+  const int g = lane >> 4, col = lane & 15;
+  const int qi = w * 16 + col;
+  const bool qvalid = qi < N;
+  bf16x8_t qop[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (qvalid) u = *(const uint4*)(a.q + headQ + (long long)qi * kD + ks * 32 + 8 * g);
+    qop[ks] = as_bf16x8(u);
+  }
+  const unsigned long long anc = qvalid ? s_anc[qi] : 0ull;
+
+  f32x4_t o[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_huge_valf();
+  float l_run = 0.0f;  // this lane's share of the row sum
+
+  const int total = L + N;
+  const int n_tiles = (total + kKT - 1) / kKT;
+  uint4 kr[4], vr[4];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ci = j * kThreads + tid;
+      const int key = ci >> 4, d0 = (ci & 15) * 8;
+      const int gk = t * kKT + key;
+      if (gk < total) {
+        kr[j] = *(const uint4*)(a.k + headKV + (long long)gk * kD + d0);
+        vr[j] = *(const uint4*)(a.v + headKV + (long long)gk * kD + d0);
+      } else {
+        kr[j] = make_uint4(0, 0, 0, 0);
+        vr[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_tile(0);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ci = j * kThreads + tid;
+      const int key = ci >> 4, d0 = (ci & 15) * 8;
+      *(uint4*)&Ks[key * kKsStride + d0] = kr[j];
+      const uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        Vt[(d0 + 2 * h) * kVtStride + key] = (uint16_t)(vw[h] & 0xffffu);
+        Vt[(d0 + 2 * h + 1) * kVtStride + key] = (uint16_t)(vw[h] >> 16);
+      }
+    }
+    __syncthreads();
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    f32x4_t s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 ku = *(const uint4*)&Ks[(kb * 16 + col) * kKsStride + ks * 32 + 8 * g];
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ku), qop[ks], s[kb], 0, 0, 0);
+      }
+    }
+
+    const int tile0 = t * kKT;
+    const bool need_mask = tile0 + kKT > L;
+    float tmax = -__builtin_huge_valf();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[kb][i] * a.scale_log2;
+        if (need_mask) {
+          const int kk = tile0 + kb * 16 + 4 * g + i;
+          bool ok = kk < L;
+          if (!ok && kk < total) ok = (anc >> (kk - L)) & 1ull;
+          x = ok ? x : -__builtin_huge_valf();
+        }
+        s[kb][i] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -__builtin_huge_valf() ? 0.0f : m_new;
+    const float alpha = exp2_hw(m_run - m_use);
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2_hw(s[kb][i] - m_use);
+        s[kb][i] = p;
+        psum += p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      // logical keys 8g..8g+7 of this key-step = physical keys
+      // 32*ks2 + 4g + {0..3} and 32*ks2 + 16 + 4g + {0..3}
+      const uint4 pu = make_uint4(pack_bf16x2(s[2 * ks2][0], s[2 * ks2][1]),
+                                  pack_bf16x2(s[2 * ks2][2], s[2 * ks2][3]),
+                                  pack_bf16x2(s[2 * ks2 + 1][0], s[2 * ks2 + 1][1]),
+                                  pack_bf16x2(s[2 * ks2 + 1][2], s[2 * ks2 + 1][3]));
+      const bf16x8_t pop = as_bf16x8(pu);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const uint16_t* vrow = &Vt[(mb * 16 + col) * kVtStride + ks2 * 32 + 4 * g];
+        const uint2 lo = *(const uint2*)vrow;
+        const uint2 hi = *(const uint2*)(vrow + 16);
+        const uint4 vu = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vu), pop, o[mb], 0, 0, 0);
+      }
+    }
+  }
+
+  float l = l_run + __shfl_xor(l_run, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (qvalid) {
+    const float inv = 1.0f / l;
+    uint16_t* orow = a.out + headQ + (long long)qi * kD;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const uint2 pk = make_uint2(pack_bf16x2(o[mb][0] * inv, o[mb][1] * inv),
+                                  pack_bf16x2(o[mb][2] * inv, o[mb][3] * inv));
+      *(uint2*)(orow + mb * 16 + 4 * g) = pk;
+    }
+    if (a.lse && g == 0)
+      a.lse[(long long)bh * N + qi] = (m_run + __log2f(l)) * 0.69314718055994531f;
+  }
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+  attn_kernel<<<dim3((unsigned)((long long)a.B * a.H)), dim3(kThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,101 @@
+"""The C-ABI library: builds, loads, exports every declared symbol, validates on the host.
+
+No call here reaches a kernel launch, so the file runs without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import rejection_sampling_verify_04_amd as sv
+    if not os.path.exists(sv.LIB_PATH):
+        from rejection_sampling_verify_04_amd import build
+        build.build()
+    return sv.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ["spec_verify_linear", "spec_verify_tree", "spec_verify_attn",
+                 "spec_verify_version", "spec_verify_status_string",
+                 "spec_verify_linear_workspace_size", "spec_verify_tree_workspace_size"]:
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    import rejection_sampling_verify_04_amd as sv
+    assert sv.version() >= 1
+    assert sv.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert sv.status_string(code) not in ("ok", "unknown status")
+    assert sv.status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    n = lib.spec_verify_linear_workspace_size(32, 160, 32000, 1)
+    assert n > 0 and n % 256 == 0
+    # partials (352 rows x 4 chunks x 16 B) + masses + counters
+    assert n >= 352 * 4 * 16 + 32 * 4 * 8 + 32 * 4
+    assert lib.spec_verify_linear_workspace_size(-1, 0, 10, 1) == 0
+    assert lib.spec_verify_tree_workspace_size(64, 64, 32000, 1) >= 64 * 64 * 4 * 16
+
+
+def _linear(lib, **kw):
+    args = dict(target=ctypes.c_void_p(16), draft=ctypes.c_void_p(16), dtype=1, B=2, V=100,
+                total=4, off=ctypes.c_void_p(16), tok=ctypes.c_void_p(16),
+                tt=ctypes.c_void_p(16), td=ctypes.c_void_p(16), na=ctypes.c_void_p(16),
+                out=ctypes.c_void_p(16), ws=ctypes.c_void_p(256), wsb=1 << 20)
+    args.update(kw)
+    return lib.spec_verify_linear(args["target"], args["draft"], args["dtype"], args["B"],
+                                  args["V"], args["total"], args["off"], args["tok"], args["tt"],
+                                  args["td"], 0, 0, None, args["na"], args["out"], None, None,
+                                  None, args["ws"], args["wsb"], None)
+
+
+def test_linear_host_validation(lib):
+    assert _linear(lib, dtype=7) == -1
+    assert _linear(lib, B=-1) == -1
+    assert _linear(lib, V=0) == -1
+    assert _linear(lib, total=2 * 64 + 1) == -1          # some gamma_b > 64
+    assert _linear(lib, B=0, total=0) == 0                # empty batch: no-op
+    assert _linear(lib, target=None) == -1
+    assert _linear(lib, na=None) == -1
+    assert _linear(lib, ws=None) == -3
+    assert _linear(lib, ws=ctypes.c_void_p(128)) == -3    # misaligned workspace
+    assert _linear(lib, wsb=16) == -3                     # too small
+    assert _linear(lib, V=64 * 8192 + 1) == -2            # vocabulary beyond the chunk table
+
+
+def test_tree_and_attn_host_validation(lib):
+    p = ctypes.c_void_p(256)
+    common = (p, None, 1, 4, 8, 100, p, p, None)
+    tail = (p, None, 0, 0, None, p, p, p, None, None, p, 1 << 20, None)
+    assert lib.spec_verify_tree(*common, 1, *tail) == -2        # SAMPLED_WOR not built
+    assert lib.spec_verify_tree(*common, 5, *tail) == -1
+    assert lib.spec_verify_tree(p, None, 1, 4, 65, 100, p, p, None, 0, *tail) == -1
+    assert lib.spec_verify_attn(p, p, p, p, None, 2, 4, 8, 64, 100, 0.1, p, None, None) == -2
+    assert lib.spec_verify_attn(p, p, p, p, None, 2, 4, 65, 128, 100, 0.1, p, None, None) == -1
+    assert lib.spec_verify_attn(p, p, p, p, None, 2, 4, 8, 128, 4, 0.1, p, None, None) == -1
+    assert lib.spec_verify_attn(p, p, p, p, None, 0, 4, 8, 128, 100, 0.1, p, None, None) == 0
+    assert lib.spec_verify_philox_words(0, 0, None, 0, 5, None, None) == 0
+    assert lib.spec_verify_philox_words(0, 0, None, 3, 5, None, None) == -1
+    assert lib.spec_verify_philox_words(0, 0, None, 3, 5, ctypes.c_void_p(8), None) == -1

@@ -1,0 +1,91 @@
+"""GPU parity of spec_verify_tree (TOPK) against the oracle."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import compare_tree, run_linear, run_tree, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_oracle(d):
+    return oracle.verify_tree_topk(d["target"], d["dtype"], d["parents"], d["tokens"],
+                                   d.get("n_nodes"), d["temp_target"], seed=d["seed"],
+                                   step=d["step"])
+
+
+def check(d, label):
+    say("[tree] %s: B=%d N=%d V=%d" % (label, d["B"], d["N"], d["V"]))
+    gpu = run_tree(d)
+    ref = run_oracle(d)
+    s = compare_tree(gpu, ref, d)
+    depth = np.bincount(np.maximum(gpu["num_accepted"], 0), minlength=5)
+    say("[tree] %s: ok %s depth histogram %s" % (label, s, depth.tolist()))
+    return gpu, ref
+
+
+def test_tree_v32k_full():
+    d = synth.tree_v32k()
+    say("[tree] nodes passing cumulative 0.1: %d; depth histogram %s" % (
+        d["nodes_passing_0p1"], d["depth_hist"].tolist()))
+    check(d, "tree v32k bf16")
+
+
+def test_peaked_trees_reach_depth():
+    d = synth.peaked_tree()
+    gpu, _ = check(d, "peaked V=64 fp32")
+    assert np.mean(gpu["num_accepted"] >= 2) > 0.5
+
+
+def test_peaked_trees_bf16_multichunk():
+    d = synth.tree_v32k(seed=21, B=16, N=40, V=20000, draft_sd=6.0, pert=0.5)
+    check(d, "peaked V=20000 bf16")
+
+
+def test_greedy_and_mixed_temperature_trees():
+    d = synth.peaked_tree(seed=22, B=24)
+    d["temp_target"] = np.where(np.arange(24) % 3 == 0, 0.0, d["temp_target"]).astype(np.float32)
+    check(d, "greedy trees")
+
+
+def test_partial_trees_and_error_rows():
+    d = synth.peaked_tree(seed=23, B=12, N=21)
+    d["n_nodes"] = d["n_nodes"].copy()
+    d["n_nodes"][:4] = [1, 5, 9, 20]
+    d["parents"] = d["parents"].copy()
+    d["tokens"] = d["tokens"].copy()
+    d["parents"][5, 3] = 7          # parent after child: bad shape
+    d["tokens"][6, 2] = d["V"]      # token out of range
+    d["n_nodes"][7] = 0             # bad node count
+    d["temp_target"] = d["temp_target"].copy()
+    d["temp_target"][8] = np.nan    # bad temperature
+    gpu, ref = check(d, "partial trees and error rows")
+    assert list(gpu["num_accepted"][[5, 6, 7, 8]]) == [-1, -1, -1, -1]
+
+
+def test_chain_tree_equals_linear_greedy_draft():
+    rng = np.random.default_rng(31)
+    B, g, V = 16, 6, 3000
+    y = rng.normal(0, 3, size=(B, g, V)).astype(np.float32)
+    x = rng.normal(0, 3, size=(B, g + 1, V)).astype(np.float32)
+    dtok = np.argmax(synth.bf16_values(synth.bf16_bits(y)), axis=2)
+    for b in range(B):
+        for i in range(g):
+            x[b, i, dtok[b, i]] = x[b, i].max() + rng.uniform(0, 5)
+    xb, yb = synth.bf16_bits(x), synth.bf16_bits(y)
+    T = np.linspace(0.5, 1.5, B).astype(np.float32)
+    lin = dict(kind="linear", dtype=1, B=B, V=V, target=xb.reshape(B * (g + 1), V),
+               draft=yb.reshape(B * g, V), offsets=np.arange(B + 1, dtype=np.int32) * g,
+               tokens=dtok.reshape(-1).astype(np.int32), temp_target=T,
+               temp_draft=np.zeros(B, np.float32), seed=4, step=2)
+    tree = dict(kind="tree", dtype=1, B=B, N=g + 1, V=V, target=xb,
+                parents=np.tile(np.arange(-1, g, dtype=np.int32), (B, 1)),
+                tokens=np.concatenate([np.zeros((B, 1), np.int32), dtok.astype(np.int32)], 1),
+                n_nodes=None, temp_target=T, seed=4, step=2)
+    gl = run_linear(lin)
+    gt = run_tree(tree)
+    assert np.array_equal(gl["num_accepted"], gt["num_accepted"])
+    assert np.array_equal(gl["out_tokens"].reshape(B, g + 1), gt["out_tokens"])
+    say("[tree] chain == linear, depths %s" % gt["num_accepted"].tolist())
