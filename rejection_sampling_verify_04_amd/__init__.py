@@ -235,10 +235,15 @@ def verify_attn(q, k_cache, v_cache, prefix_len, parents=None, scale=None, want_
     return outputs
 
 
-def profile_next(begin_event, end_event):
-    """Have the next linear/tree call record two torch.cuda.Events around its vocabulary pass."""
-    begin_event.record()   # make sure both HIP events exist
-    end_event.record()
+def profile_next(begin_event, end_event, ensure_created=True):
+    """Have the next linear/tree call record two torch.cuda.Events around its vocabulary pass.
+
+    The events must exist as HIP events; with ensure_created they are recorded
+    once here first (do that outside any graph capture).
+    """
+    if ensure_created:
+        begin_event.record()
+        end_event.record()
     library().spec_verify_profile_next(ctypes.c_void_p(begin_event.cuda_event),
                                        ctypes.c_void_p(end_event.cuda_event))
 

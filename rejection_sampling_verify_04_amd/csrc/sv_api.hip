@@ -12,18 +12,18 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int n_chunks_for(int V) { return (V + sv::kChunk - 1) / sv::kChunk; }
 
-// Workspace: [partials | chunk masses | per-row counters], each aligned.
+// Workspace: [partials | chunk masses | per-row decision records], each aligned.
 struct Layout {
-  size_t part, mass, counter, total;
+  size_t part, mass, rec, total;
 };
 
-Layout layout(long long n_rows, int B, int V) {
+Layout layout(long long n_rows, int B, int V, bool linear) {
   const int nc = n_chunks_for(V);
   Layout l;
   l.part = 0;
   l.mass = align_up((size_t)n_rows * nc * sizeof(sv::Partial));
-  l.counter = l.mass + align_up((size_t)B * nc * sizeof(double));
-  l.total = l.counter + align_up((size_t)B * sizeof(int));
+  l.rec = l.mass + (linear ? align_up((size_t)B * nc * sizeof(double)) : 0);
+  l.total = l.rec + (linear ? align_up((size_t)B * sizeof(sv::LinRecord)) : 0);
   if (l.total == 0) l.total = kAlign;
   return l;
 }
@@ -33,12 +33,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // One-shot timing hook (spec_verify_profile_next).
 hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 
-hipError_t launch_stats_timed(int dtype, const sv::StatsArgs& s, long long n_items,
-                              hipStream_t stream) {
+hipError_t launch_stats_timed(int dtype, const sv::StatsArgs& s, hipStream_t stream) {
   hipEvent_t b = g_prof_begin, e = g_prof_end;
   g_prof_begin = g_prof_end = nullptr;
   if (b && e && hipEventRecord(b, stream) != hipSuccess) return hipErrorUnknown;
-  const hipError_t err = sv::launch_stats(dtype, s, n_items, stream);
+  const hipError_t err = sv::launch_stats(dtype, s, stream);
   if (err != hipSuccess) return err;
   if (b && e && hipEventRecord(e, stream) != hipSuccess) return hipErrorUnknown;
   return hipSuccess;
@@ -69,7 +68,7 @@ const char* spec_verify_status_string(int status) {
 size_t spec_verify_linear_workspace_size(int B, int total_draft, int V, int dtype) {
   (void)dtype;
   if (B < 0 || total_draft < 0 || V < 1) return 0;
-  return layout(2LL * total_draft + B, B, V).total;
+  return layout(2LL * total_draft + B, B, V, true).total;
 }
 
 int spec_verify_linear(const void* target_logits, const void* draft_logits, int dtype, int B,
@@ -91,8 +90,9 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   const long long n_t = (long long)total_draft + B;
   const long long n_rows = n_t + total_draft;
   const int nc = n_chunks_for(V);
-  if (n_rows * nc >= (1LL << 31) || (long long)B * nc >= (1LL << 31)) return SV_ERR_INVALID_ARG;
-  const Layout l = layout(n_rows, B, V);
+  if (sv::stats_items(n_rows, nc) >= (1LL << 31) || (long long)B * nc >= (1LL << 31))
+    return SV_ERR_INVALID_ARG;
+  const Layout l = layout(n_rows, B, V, true);
   const int wst = check_workspace(workspace, workspace_bytes, l.total);
   if (wst != SV_OK) return wst;
 
@@ -116,10 +116,8 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   s.temp_a = temp_target;
   s.temp_b = temp_draft;
   s.part = (sv::Partial*)(ws + l.part);
-  s.zero = (int*)(ws + l.counter);
-  s.n_zero = B;
   s.vec_ok = vec_ok;
-  if (launch_stats_timed(dtype, s, n_rows * nc, stream) != hipSuccess) return SV_ERR_HIP;
+  if (launch_stats_timed(dtype, s, stream) != hipSuccess) return SV_ERR_HIP;
 
   sv::LinearArgs f{};
   f.target = target_logits;
@@ -138,22 +136,21 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   f.row_ids = row_ids;
   f.part = s.part;
   f.mass = (double*)(ws + l.mass);
-  f.counter = (int*)(ws + l.counter);
+  f.rec = (sv::LinRecord*)(ws + l.rec);
   f.num_accepted = num_accepted;
   f.out_tokens = out_tokens;
   f.p_at = p_at_draft;
   f.q_at = q_at_draft;
   f.row_status = row_status;
   f.vec_ok = vec_ok;
-  if (sv::launch_linear_finish(dtype, f, (long long)B * nc, stream) != hipSuccess)
-    return SV_ERR_HIP;
+  if (sv::launch_linear_finish(dtype, f, stream) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 
 size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype) {
   (void)dtype;
   if (B < 0 || N < 1 || V < 1) return 0;
-  return layout((long long)B * N, B, V).total;
+  return layout((long long)B * N, B, V, false).total;
 }
 
 int spec_verify_tree(const void* target_logits, const void* draft_logits, int dtype, int B,
@@ -176,8 +173,8 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
     return SV_ERR_INVALID_ARG;
   const long long n_rows = (long long)B * N;
   const int nc = n_chunks_for(V);
-  if (n_rows * nc >= (1LL << 31)) return SV_ERR_INVALID_ARG;
-  const Layout l = layout(n_rows, B, V);
+  if (sv::stats_items(n_rows, nc) >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  const Layout l = layout(n_rows, B, V, false);
   const int wst = check_workspace(workspace, workspace_bytes, l.total);
   if (wst != SV_OK) return wst;
   const int es = dtype == SV_BF16 ? 2 : 4;
@@ -199,10 +196,8 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
   s.temp_a = temp_target;
   s.temp_b = temp_target;
   s.part = (sv::Partial*)(ws + l.part);
-  s.zero = (int*)(ws + l.counter);
-  s.n_zero = B;
   s.vec_ok = vec_ok;
-  if (launch_stats_timed(dtype, s, n_rows * nc, stream) != hipSuccess) return SV_ERR_HIP;
+  if (launch_stats_timed(dtype, s, stream) != hipSuccess) return SV_ERR_HIP;
 
   sv::TreeArgs f{};
   f.target = target_logits;
@@ -218,16 +213,13 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
   f.step = step;
   f.row_ids = row_ids;
   f.part = s.part;
-  f.mass = (double*)(ws + l.mass);
-  f.counter = (int*)(ws + l.counter);
   f.num_accepted = num_accepted;
   f.path_nodes = path_nodes;
   f.out_tokens = out_tokens;
   f.p_at = p_at_node;
   f.row_status = row_status;
   f.vec_ok = vec_ok;
-  if (sv::launch_tree_finish(dtype, f, (long long)B * nc, stream) != hipSuccess)
-    return SV_ERR_HIP;
+  if (sv::launch_tree_finish(dtype, f, stream) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 

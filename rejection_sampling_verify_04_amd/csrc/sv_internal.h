@@ -22,9 +22,14 @@ struct StatsArgs {
   const float* temp_a;   // temperature of rows_a rows (per batch row)
   const float* temp_b;   // temperature of rows_b rows
   Partial* part;         // [n_rows][n_chunks]
-  int* zero;             // counters of the finish pass, cleared here
-  long long n_zero;
   int vec_ok;            // 16-byte vector loads are valid for every row
+};
+
+// Decision of one linear batch row, handed from the mass pass to the select pass.
+struct LinRecord {
+  int kind, flags, n_acc, token;
+  int o0, g, q_greedy, q_amax;
+  float p_c, p_inv_s, q_c, q_inv_s;
 };
 
 struct LinearArgs {
@@ -40,7 +45,7 @@ struct LinearArgs {
   const uint32_t* row_ids;
   const Partial* part;
   double* mass;          // [B][n_chunks]
-  int* counter;          // [B]
+  LinRecord* rec;        // [B]
   int* num_accepted;
   int* out_tokens;
   float* p_at;
@@ -59,8 +64,6 @@ struct TreeArgs {
   uint64_t seed, step;
   const uint32_t* row_ids;
   const Partial* part;
-  double* mass;
-  int* counter;
   int* num_accepted;
   int* path_nodes;
   int* out_tokens;
@@ -81,10 +84,10 @@ struct AttnArgs {
   float* lse;
 };
 
-hipError_t launch_stats(int dtype, const StatsArgs& a, long long n_items, hipStream_t st);
-hipError_t launch_linear_finish(int dtype, const LinearArgs& a, long long n_items,
-                                hipStream_t st);
-hipError_t launch_tree_finish(int dtype, const TreeArgs& a, long long n_items, hipStream_t st);
+long long stats_items(long long n_rows, int n_chunks);
+hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st);
+hipError_t launch_linear_finish(int dtype, const LinearArgs& a, hipStream_t st);
+hipError_t launch_tree_finish(int dtype, const TreeArgs& a, hipStream_t st);
 hipError_t launch_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids,
                                int n_rows, int n_slots, uint32_t* out, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);

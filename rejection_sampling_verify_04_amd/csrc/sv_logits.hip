@@ -1,30 +1,38 @@
 // Vocabulary-wide verify kernels (linear and tree), gfx950.
 //
-// Two launches per call:
+// Linear verify, three launches per call:
 //
-//   stats_kernel   one work item per (logit row, 8192-element chunk): a
-//                  single coalesced pass over the chunk (16-byte loads) that
-//                  reduces it to a Partial -- an offset and a sum of
-//                  exponentials for a sampled row, the max and its first
-//                  index for a greedy row.  This pass reads every logit of
-//                  the call exactly once and is the HBM-bound part.
+//   stats_kernel        one work item per (logit row, pair of 8192-element
+//                       chunks): coalesced 16-byte loads of both chunks are
+//                       issued together, then each chunk is reduced to a
+//                       Partial -- an offset and a sum of exponentials for a
+//                       sampled row, the max and its first index for a
+//                       greedy row.  This pass reads every logit of the call
+//                       exactly once and is the HBM-bound part.
 //
-//   *_finish       one work item per (batch row, chunk).  Every item merges
-//                  the row's partials (tiny), redoes the row's acceptance
-//                  decisions (identical arithmetic, so identical results in
-//                  every item), then computes the mass of the stop
-//                  distribution over its chunk: max(0, p - q) after a
-//                  rejection, p for a bonus token, p with the rejected
-//                  siblings removed in a tree.  The last item of the row
-//                  to finish (a per-row counter) picks the chunk holding
-//                  u * R, recomputes that chunk's terms with the same code,
-//                  and finds the first index whose cumulative mass exceeds
-//                  u * R, in vocabulary order.
+//   linear_mass_kernel  one work item per (batch row, chunk).  Every item
+//                       merges the row's partials, redoes the row's
+//                       acceptance decisions (identical arithmetic, so
+//                       identical results in every item) and computes the
+//                       mass of the stop distribution over its chunk:
+//                       max(0, p - q) after a rejection, p for the bonus
+//                       token.  Item 0 also stores the row's decision.
 //
-// The mass pass and the select pass accumulate each thread's 32 contiguous
-// terms sequentially in float64 and combine threads with one block scan, so
-// the chunk totals used to choose the chunk and the cumulative sums used
-// inside it are computed identically.
+//   linear_select_kernel one work item per batch row: picks the chunk that
+//                       holds u * R, recomputes that chunk's weights with the
+//                       same code as the mass pass and returns the first index
+//                       whose cumulative mass exceeds u * R, in vocabulary order.
+//
+// Tree verify, two launches: the same stats_kernel, then tree_kernel (one
+// work item per tree): it walks the tree level by level with one lane per
+// sibling, takes the stop node's chunk masses from its partials (minus the
+// rejected siblings), and selects in one chunk.
+//
+// Work items never wait for one another: a kernel boundary is the only
+// synchronisation, because device-scope fences and atomics are costly here.
+// The mass and select passes accumulate each thread's 32 contiguous weights
+// sequentially in float64 and combine threads with the same block scan, so
+// chunk totals and in-chunk cumulative sums agree bit for bit.
 //
 // Sources: acceptance rule and first-reject stop (kwkr.cn/news/620872 §2.3,
 // §4.1, §4.3; cf-1.com/news/5632551 §2.2); residual and bonus draws
@@ -65,43 +73,26 @@ __device__ int find_batch_row(const int* __restrict__ off, int B, long long x, i
 // Pass 1: per-chunk statistics of every logit row.
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
-  __shared__ int s_best;
-  __shared__ float s_redf[kWaves];
-  __shared__ double s_red[kWaves];
-  __shared__ unsigned long long s_red64[kWaves];
+struct ChunkLoad {
+  static constexpr int ES = DT ? 2 : 4;          // bytes per element
+  static constexpr int EPV = 16 / ES;            // elements per 16-byte load
+  static constexpr int NV = kPerThread / EPV;    // loads per thread per chunk
+  uint4 raw[NV];
 
-  constexpr int ES = DT ? 2 : 4;          // bytes per element
-  constexpr int EPV = 16 / ES;            // elements per 16-byte load
-  constexpr int NV = kPerThread / EPV;    // loads per thread
-
-  const int tid = threadIdx.x;
-  const long long item = blockIdx.x;
-  {
-    const long long z = item * kThreads + tid;
-    if (z < a.n_zero) a.zero[z] = 0;      // per-row counters of the finish pass
-  }
-  const long long row = item / a.n_chunks;
-  const int chunk = (int)(item - row * a.n_chunks);
-  const int V = a.V;
-  const long long rowbytes = (long long)V * ES;
-  const char* rowp = row < a.n_a ? (const char*)a.rows_a + row * rowbytes
-                                 : (const char*)a.rows_b + (row - a.n_a) * rowbytes;
-  const int c0 = chunk * kChunk;
-
-  // Issue the chunk's loads before looking up the row's temperature.
-  float v[kPerThread];
-  if (a.vec_ok) {
-    uint4 raw[NV];
+  // Thread t's vector j covers elements c0 + (j * 256 + t) * EPV + [0, EPV).
+  __device__ __forceinline__ void issue(const char* rowp, int V, int c0) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int e0 = c0 + (j * kThreads + tid) * EPV;
+      const int e0 = c0 + (j * kThreads + threadIdx.x) * EPV;
       if (e0 < V) raw[j] = *(const uint4*)(rowp + (long long)e0 * ES);
       else raw[j] = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
     }
+  }
+
+  __device__ __forceinline__ void unpack(int V, int c0, float v[kPerThread]) const {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int e0 = c0 + (j * kThreads + tid) * EPV;
+      const int e0 = c0 + (j * kThreads + threadIdx.x) * EPV;
       if (DT == 1) {
         const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
 #pragma unroll
@@ -120,36 +111,36 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
         for (int k = 0; k < EPV; ++k) v[j * EPV + k] = -__builtin_huge_valf();
       }
     }
-  } else {
+  }
+};
+
+template <int DT>
+__device__ __forceinline__ void load_scalar(const char* rowp, int V, int c0, float v[kPerThread]) {
+  constexpr int EPV = ChunkLoad<DT>::EPV;
+  constexpr int NV = ChunkLoad<DT>::NV;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+  for (int j = 0; j < NV; ++j) {
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        const int e = c0 + (j * kThreads + tid) * EPV + k;
-        v[j * EPV + k] = e < V ? load_logit<DT>(rowp, e) : -__builtin_huge_valf();
-      }
+    for (int k = 0; k < EPV; ++k) {
+      const int e = c0 + (j * kThreads + threadIdx.x) * EPV + k;
+      v[j * EPV + k] = e < V ? load_logit<DT>(rowp, e) : -__builtin_huge_valf();
     }
   }
+}
 
-  float T;
-  if (a.tree) {
-    const int b = (int)(row / a.N);
-    const int node = (int)(row - (long long)b * a.N);
-    const int nn = a.n_nodes ? a.n_nodes[b] : a.N;
-    if (node >= nn) return;               // unused node row: never read
-    T = a.temp_a[b];
-  } else if (row < a.n_a) {
-    T = a.temp_a[find_batch_row(a.offsets, a.B, row, 1, &s_best)];
-  } else {
-    T = a.temp_b[find_batch_row(a.offsets, a.B, row - a.n_a, 0, &s_best)];
-  }
+struct StatsShared {
+  float redf[kWaves];
+  double red[kWaves];
+  unsigned long long red64[kWaves];
+};
 
-  Partial* out = a.part + row * a.n_chunks + chunk;
-  if (!temp_ok(T)) {                      // the finish pass reports the row
-    if (tid == 0) *out = Partial{0.0f, 0, 0.0};
-    return;
-  }
-
+// Reduce one chunk held as this thread's 32 values (index order as loaded).
+template <int DT>
+__device__ __forceinline__ Partial chunk_partial(float v[kPerThread], int c0, float T,
+                                                 StatsShared* sh) {
+  constexpr int EPV = ChunkLoad<DT>::EPV;
+  constexpr int NV = ChunkLoad<DT>::NV;
+  const int tid = threadIdx.x;
   if (T == 0.0f) {
     // First maximum: the thread's elements are in increasing index order.
     float bv = -__builtin_huge_valf();
@@ -166,14 +157,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
     const unsigned long long key =
         ((unsigned long long)float_order_key(bv) << 32) | (0xffffffffu - (uint32_t)bi);
-    const unsigned long long best = block_max_u64(key, s_red64);
-    if (tid == 0) {
-      *out = Partial{float_from_order_key((uint32_t)(best >> 32)),
-                     (int)(0xffffffffu - (uint32_t)best), 0.0};
-    }
-    return;
+    const unsigned long long best = block_max_u64(key, sh->red64);
+    return Partial{float_from_order_key((uint32_t)(best >> 32)),
+                   (int)(0xffffffffu - (uint32_t)best), 0.0};
   }
-
   // Sampled row: thread-local offset from the thread's own maximum, then a
   // pairwise sum of 2^(x k - c); threads are merged exactly in float64.
   const float k2 = log2e_over_t(T);
@@ -190,10 +177,69 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     for (int e = 0; e < w; ++e) v[e] += v[e + w];
   }
   const float s = v[0];
-  const float C = block_max(any ? ct : -__builtin_huge_valf(), s_redf);
+  const float C = block_max(any ? ct : -__builtin_huge_valf(), sh->redf);
   const double contrib = (any && s > 0.0f) ? (double)s * exp2((double)ct - (double)C) : 0.0;
-  const double S = block_sum(contrib, s_red);
-  if (tid == 0) *out = Partial{C, 0, S};
+  const double S = block_sum(contrib, sh->red);
+  return Partial{C, 0, S};
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
+  __shared__ int s_best;
+  __shared__ StatsShared sh;
+
+  const int tid = threadIdx.x;
+  const long long item = blockIdx.x;
+  const int n_tiles = (a.n_chunks + 1) >> 1;
+  const long long row = item / n_tiles;
+  const int tile = (int)(item - row * n_tiles);
+  const int ca = 2 * tile, cb = ca + 1;
+  const bool has_b = cb < a.n_chunks;
+  const int V = a.V;
+  const long long rowbytes = (long long)V * ChunkLoad<DT>::ES;
+  const char* rowp = row < a.n_a ? (const char*)a.rows_a + row * rowbytes
+                                 : (const char*)a.rows_b + (row - a.n_a) * rowbytes;
+
+  // Issue both chunks' loads before looking up the row's temperature.
+  ChunkLoad<DT> la, lb;
+  if (a.vec_ok) {
+    la.issue(rowp, V, ca * kChunk);
+    if (has_b) lb.issue(rowp, V, cb * kChunk);
+  }
+
+  float T;
+  if (a.tree) {
+    const int b = (int)(row / a.N);
+    const int node = (int)(row - (long long)b * a.N);
+    const int nn = a.n_nodes ? a.n_nodes[b] : a.N;
+    if (node >= nn) return;               // unused node row: never read
+    T = a.temp_a[b];
+  } else if (row < a.n_a) {
+    T = a.temp_a[find_batch_row(a.offsets, a.B, row, 1, &s_best)];
+  } else {
+    T = a.temp_b[find_batch_row(a.offsets, a.B, row - a.n_a, 0, &s_best)];
+  }
+
+  Partial* out = a.part + row * a.n_chunks;
+  if (!temp_ok(T)) {                      // the finish pass reports the row
+    if (tid == 0) {
+      out[ca] = Partial{0.0f, 0, 0.0};
+      if (has_b) out[cb] = Partial{0.0f, 0, 0.0};
+    }
+    return;
+  }
+
+  float v[kPerThread];
+  if (a.vec_ok) la.unpack(V, ca * kChunk, v);
+  else load_scalar<DT>(rowp, V, ca * kChunk, v);
+  const Partial pa = chunk_partial<DT>(v, ca * kChunk, T, &sh);
+  if (tid == 0) out[ca] = pa;
+  if (has_b) {
+    if (a.vec_ok) lb.unpack(V, cb * kChunk, v);
+    else load_scalar<DT>(rowp, V, cb * kChunk, v);
+    const Partial pb = chunk_partial<DT>(v, cb * kChunk, T, &sh);
+    if (tid == 0) out[cb] = pb;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -244,13 +290,12 @@ __device__ __forceinline__ double row_prob(const RowStats& r, bool greedy, float
   return exp2((double)x * (double)k2 - (double)r.c) / r.s;
 }
 
-// The stop distribution's unnormalised weights for one row and chunk.
+// The stop distribution's unnormalised weights for one row.
 struct StopDist {
   const void* prow;       // target row at the stop position / node
   const void* qrow;       // draft row (residual only)
   int residual;           // 1: max(0, p - q); 0: p
-  int p_greedy, q_greedy;
-  int p_amax, q_amax;
+  int q_greedy, q_amax;
   float p_k, p_c, p_inv_s;
   float q_k, q_c, q_inv_s;
 };
@@ -299,8 +344,7 @@ __device__ __forceinline__ void stop_weights(const StopDist& d, int V, int chunk
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const int idx = e0 + e;
-    float p = d.p_greedy ? (idx == d.p_amax ? 1.0f : 0.0f)
-                         : exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
+    float p = exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
     if (d.residual) {
       const float q = d.q_greedy ? (idx == d.q_amax ? 1.0f : 0.0f)
                                  : exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
@@ -325,12 +369,11 @@ __device__ double chunk_mass(const StopDist& d, int V, int chunk, int vec_ok, ui
 }
 
 // First index of chunk `chunk` whose cumulative mass (starting at `base`)
-// exceeds `target`; -1 when rounding left it uncrossed.  Also returns the last
-// index with positive weight in *last_pos (or -1).
+// exceeds `target`; if rounding leaves it uncrossed, the last index with
+// positive weight; if the chunk has none, its first index.
 template <int DT>
 __device__ int chunk_select(const StopDist& d, int V, int chunk, int vec_ok, uint32_t mask,
-                            double base, double target, double* s_scan, int* s_min,
-                            int* s_lastpos, int* last_pos) {
+                            double base, double target, double* s_scan, int* s_misc) {
   float w[kPerThread];
   stop_weights<DT>(d, V, chunk, vec_ok, mask, w);
   double acc = 0.0;
@@ -347,19 +390,22 @@ __device__ int chunk_select(const StopDist& d, int V, int chunk, int vec_ok, uin
     if (found == 0x7fffffff && run > target && w[e] > 0.0f) found = e0 + e;
     if (w[e] > 0.0f) lastp = e0 + e;
   }
-  if (threadIdx.x == 0) { *s_min = 0x7fffffff; *s_lastpos = -1; }
+  if (threadIdx.x == 0) {
+    s_misc[0] = 0x7fffffff;
+    s_misc[1] = -1;
+  }
   __syncthreads();
-  if (found != 0x7fffffff) atomicMin(s_min, found);
-  if (lastp >= 0) atomicMax(s_lastpos, lastp);
+  if (found != 0x7fffffff) atomicMin(&s_misc[0], found);
+  if (lastp >= 0) atomicMax(&s_misc[1], lastp);
   __syncthreads();
-  const int k = *s_min;
-  *last_pos = *s_lastpos;
+  const int k = s_misc[0], last = s_misc[1];
   __syncthreads();
-  return k == 0x7fffffff ? -1 : k;
+  if (k != 0x7fffffff) return k;
+  return last >= 0 ? last : chunk * kChunk;
 }
 
-// Thread 0 of the last arriver finds the chunk holding u * R (R = the sum
-// of the row's chunk masses, in chunk order) and the mass before it.
+// Thread 0 finds the chunk holding u * R (R = the sum of the chunk masses,
+// in chunk order) and the mass before it.
 __device__ void choose_chunk(const double* s_mass, int n_chunks, double u, int* s_jc,
                              double* s_base, double* s_t) {
   if (threadIdx.x == 0) {
@@ -396,25 +442,24 @@ __device__ void choose_chunk(const double* s_mass, int n_chunks, double u, int* 
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2, linear verify.
+// Linear verify, pass 2: decisions and stop-distribution chunk masses.
+
+constexpr int kKindReject = 0, kKindBonus = 1, kKindGreedy = 2, kKindError = 3,
+              kKindBadShape = 4;
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void linear_finish_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kThreads) void linear_mass_kernel(LinearArgs a) {
   __shared__ RowStats s_rows[2 * kMaxGamma + 1];
   __shared__ double s_p[kMaxGamma], s_q[kMaxGamma];
-  __shared__ int s_tok[kMaxGamma];
-  __shared__ int s_flags, s_nacc, s_last;
+  __shared__ int s_flags, s_nacc;
   __shared__ double s_scan[kWaves];
-  __shared__ double s_mass[kMaxChunks];
-  __shared__ int s_misc[2];
-  __shared__ int s_jc;
-  __shared__ double s_base, s_t;
 
   const int tid = threadIdx.x;
   const int n_chunks = a.n_chunks;
   const int b = blockIdx.x / n_chunks;
   const int c = blockIdx.x - b * n_chunks;
   const int V = a.V;
+  LinRecord* rec = a.rec + b;
 
   const int o0 = a.off[b], o1 = a.off[b + 1];
   const int g = o1 - o0;
@@ -422,19 +467,18 @@ __global__ __launch_bounds__(kThreads) void linear_finish_kernel(LinearArgs a) {
   int err = 0;
   if (o0 < 0 || o1 < o0 || o1 > a.total_draft || g > kMaxGamma) err = kRowBadShape;
   else if (!temp_ok(Tt) || !temp_ok(Td)) err = kRowBadTemp;
-  const long long tr0 = (long long)o0 + b;  // first target row of b
   if (err) {
-    if (c == 0) {
-      if (err != kRowBadShape) {
-        for (int i = tid; i <= g; i += kThreads) a.out_tokens[tr0 + i] = -1;
-      }
-      if (tid == 0) {
-        a.num_accepted[b] = -1;
-        if (a.row_status) a.row_status[b] = err;
-      }
+    if (c == 0 && tid == 0) {
+      LinRecord r{};
+      r.kind = err == kRowBadShape ? kKindBadShape : kKindError;
+      r.flags = err;
+      r.o0 = o0;
+      r.g = g;
+      *rec = r;
     }
     return;
   }
+  const long long tr0 = (long long)o0 + b;  // first target row of b
   const bool gt = Tt == 0.0f, gd = Td == 0.0f;
   const float kt = gt ? 0.0f : log2e_over_t(Tt);
   const float kd = gd ? 0.0f : log2e_over_t(Td);
@@ -462,7 +506,6 @@ __global__ __launch_bounds__(kThreads) void linear_finish_kernel(LinearArgs a) {
         atomicOr(&s_flags, kRowBadToken);
         tok = 0;
       }
-      s_tok[i] = tok;
       const float x = load_logit<DT>(a.target, (tr0 + i) * (long long)V + tok);
       const float y = load_logit<DT>(a.draft, ((long long)o0 + i) * V + tok);
       const double p = row_prob(s_rows[i], gt, kt, x, tok);
@@ -488,55 +531,116 @@ __global__ __launch_bounds__(kThreads) void linear_finish_kernel(LinearArgs a) {
   const int n_acc = s_nacc;
 
   if (flags & kRowErrorMask) {
-    if (c == 0) {
-      for (int i = tid; i <= g; i += kThreads) a.out_tokens[tr0 + i] = -1;
-      if (tid == 0) {
-        a.num_accepted[b] = -1;
-        if (a.row_status) a.row_status[b] = flags & kRowErrorMask;
-      }
+    if (c == 0 && tid == 0) {
+      LinRecord r{};
+      r.kind = kKindError;
+      r.flags = flags & kRowErrorMask;
+      r.o0 = o0;
+      r.g = g;
+      *rec = r;
+    }
+    return;
+  }
+  if (c == 0) {
+    if (a.p_at) for (int i = tid; i < g; i += kThreads) a.p_at[o0 + i] = (float)s_p[i];
+    if (a.q_at) for (int i = tid; i < g; i += kThreads) a.q_at[o0 + i] = (float)s_q[i];
+  }
+  if (gt) {
+    // greedy target: the draw is the argmax of target row n_acc (no randoms)
+    if (c == 0 && tid == 0) {
+      LinRecord r{};
+      r.kind = kKindGreedy;
+      r.flags = flags;
+      r.n_acc = n_acc;
+      r.token = s_rows[n_acc].amax;
+      r.o0 = o0;
+      r.g = g;
+      *rec = r;
     }
     return;
   }
 
-  int token = -1;
-  int warn = flags;
-  if (gt) {
-    // greedy target: the draw is the argmax of target row n_acc (no randoms)
-    if (c != 0) return;
-    token = s_rows[n_acc].amax;
-  } else {
-    StopDist d;
-    const int pos = n_acc;
-    d.prow = (const char*)a.target + (tr0 + pos) * (long long)V * (DT ? 2 : 4);
-    d.residual = pos < g;
-    d.qrow = d.residual ? (const char*)a.draft + ((long long)o0 + pos) * V * (DT ? 2 : 4)
-                        : d.prow;
-    d.p_greedy = 0;
-    d.p_amax = 0;
-    d.p_k = kt;
-    d.p_c = s_rows[pos].c;
-    d.p_inv_s = (float)(1.0 / s_rows[pos].s);
-    d.q_greedy = gd;
-    if (d.residual) {
-      const RowStats& qs = s_rows[g + 1 + pos];
-      d.q_amax = qs.amax;
-      d.q_k = kd;
-      d.q_c = qs.c;
-      d.q_inv_s = gd ? 0.0f : (float)(1.0 / qs.s);
-    } else {
-      d.q_amax = 0;
-      d.q_k = d.q_c = d.q_inv_s = 0.0f;
+  const int pos = n_acc;
+  StopDist d;
+  d.prow = (const char*)a.target + (tr0 + pos) * (long long)V * (DT ? 2 : 4);
+  d.residual = pos < g;
+  d.qrow = d.residual ? (const char*)a.draft + ((long long)o0 + pos) * V * (DT ? 2 : 4) : d.prow;
+  d.p_k = kt;
+  d.p_c = s_rows[pos].c;
+  d.p_inv_s = (float)(1.0 / s_rows[pos].s);
+  d.q_greedy = d.residual ? gd : 0;
+  d.q_amax = d.residual ? s_rows[g + 1 + pos].amax : 0;
+  d.q_k = d.residual ? kd : 0.0f;
+  d.q_c = d.residual ? s_rows[g + 1 + pos].c : 0.0f;
+  d.q_inv_s = (d.residual && !gd) ? (float)(1.0 / s_rows[g + 1 + pos].s) : 0.0f;
+
+  const double m = chunk_mass<DT>(d, V, c, a.vec_ok, 0u, s_scan);
+  if (tid == 0) a.mass[(long long)b * n_chunks + c] = m;
+  if (c == 0 && tid == 0) {
+    LinRecord r{};
+    r.kind = d.residual ? kKindReject : kKindBonus;
+    r.flags = flags;
+    r.n_acc = n_acc;
+    r.o0 = o0;
+    r.g = g;
+    r.q_greedy = d.q_greedy;
+    r.q_amax = d.q_amax;
+    r.p_c = d.p_c;
+    r.p_inv_s = d.p_inv_s;
+    r.q_c = d.q_c;
+    r.q_inv_s = d.q_inv_s;
+    *rec = r;
+  }
+}
+
+// Linear verify, pass 3: the draw and the outputs.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void linear_select_kernel(LinearArgs a) {
+  __shared__ LinRecord s_rec;
+  __shared__ double s_mass[kMaxChunks];
+  __shared__ double s_scan[kWaves];
+  __shared__ int s_misc[2];
+  __shared__ int s_jc;
+  __shared__ double s_base, s_t;
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int n_chunks = a.n_chunks;
+  const int V = a.V;
+  if (tid == 0) s_rec = a.rec[b];
+  if (tid < n_chunks) s_mass[tid] = a.mass[(long long)b * n_chunks + tid];
+  const float Tt = a.temp_t[b], Td = a.temp_d[b];
+  __syncthreads();
+  const LinRecord r = s_rec;
+  const int o0 = r.o0, g = r.g;
+  const long long tr0 = (long long)o0 + b;
+
+  if (r.kind == kKindBadShape || r.kind == kKindError) {
+    if (r.kind == kKindError)
+      for (int i = tid; i <= g; i += kThreads) a.out_tokens[tr0 + i] = -1;
+    if (tid == 0) {
+      a.num_accepted[b] = -1;
+      if (a.row_status) a.row_status[b] = r.flags;
     }
-    const double m = chunk_mass<DT>(d, V, c, a.vec_ok, 0u, s_scan);
-    if (tid == 0) a.mass[(long long)b * n_chunks + c] = m;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.counter[b], 1) == n_chunks - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (tid < n_chunks) s_mass[tid] = a.mass[(long long)b * n_chunks + tid];
-    __syncthreads();
+    return;
+  }
+  const int n_acc = r.n_acc;
+  int token = r.token;
+  int warn = r.flags;
+  if (r.kind != kKindGreedy) {
+    StopDist d;
+    d.prow = (const char*)a.target + (tr0 + n_acc) * (long long)V * (DT ? 2 : 4);
+    d.residual = r.kind == kKindReject;
+    d.qrow = d.residual ? (const char*)a.draft + ((long long)o0 + n_acc) * V * (DT ? 2 : 4)
+                        : d.prow;
+    d.p_k = log2e_over_t(Tt);
+    d.p_c = r.p_c;
+    d.p_inv_s = r.p_inv_s;
+    d.q_greedy = r.q_greedy;
+    d.q_amax = r.q_amax;
+    d.q_k = (d.residual && Td > 0.0f) ? log2e_over_t(Td) : 0.0f;
+    d.q_c = r.q_c;
+    d.q_inv_s = r.q_inv_s;
     double R = 0.0;
     for (int j = 0; j < n_chunks; ++j) R += s_mass[j];
     if (!(R > 0.0)) {
@@ -550,18 +654,12 @@ __global__ __launch_bounds__(kThreads) void linear_finish_kernel(LinearArgs a) {
       __syncthreads();
     }
     const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
-    const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)pos).y);
+    const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)n_acc).y);
     choose_chunk(s_mass, n_chunks, u, &s_jc, &s_base, &s_t);
-    int last_pos;
-    const int k = chunk_select<DT>(d, V, s_jc, a.vec_ok, 0u, s_base, s_t, s_scan, s_misc,
-                                   s_misc + 1, &last_pos);
-    token = k >= 0 ? k : (last_pos >= 0 ? last_pos : s_jc * kChunk);
+    token = chunk_select<DT>(d, V, s_jc, a.vec_ok, 0u, s_base, s_t, s_scan, s_misc);
   }
-
   for (int i = tid; i <= g; i += kThreads)
-    a.out_tokens[tr0 + i] = i < n_acc ? s_tok[i] : (i == n_acc ? token : -1);
-  if (a.p_at) for (int i = tid; i < g; i += kThreads) a.p_at[o0 + i] = (float)s_p[i];
-  if (a.q_at) for (int i = tid; i < g; i += kThreads) a.q_at[o0 + i] = (float)s_q[i];
+    a.out_tokens[tr0 + i] = i < n_acc ? a.tokens[o0 + i] : (i == n_acc ? token : -1);
   if (tid == 0) {
     a.num_accepted[b] = n_acc;
     if (a.row_status) a.row_status[b] = warn & ~kRowErrorMask;
@@ -569,15 +667,18 @@ __global__ __launch_bounds__(kThreads) void linear_finish_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2, tree verify (TOPK).
+// Tree verify (TOPK): one work item per tree.
+
+constexpr int kTreePartCache = 1024;   // partials kept in LDS when nn * n_chunks fits
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void tree_finish_kernel(TreeArgs a) {
+__global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
   __shared__ RowStats s_rows[kMaxNodes];
-  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes], s_rem[kMaxNodes];
+  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes];
   __shared__ double s_pn[kMaxNodes], s_u[kMaxNodes];
-  __shared__ int s_flags, s_stop, s_depth, s_nrem, s_last;
-  __shared__ double s_remmass;
+  __shared__ int s_flags, s_stop, s_depth;
+  __shared__ unsigned long long s_removed;   // node bits of the rejected siblings
+  __shared__ Partial s_part[kTreePartCache];
   __shared__ double s_scan[kWaves];
   __shared__ double s_mass[kMaxChunks];
   __shared__ int s_misc[2];
@@ -586,8 +687,7 @@ __global__ __launch_bounds__(kThreads) void tree_finish_kernel(TreeArgs a) {
 
   const int tid = threadIdx.x;
   const int n_chunks = a.n_chunks;
-  const int b = blockIdx.x / n_chunks;
-  const int c = blockIdx.x - b * n_chunks;
+  const int b = blockIdx.x;
   const int V = a.V, N = a.N;
   const int nn = a.n_nodes ? a.n_nodes[b] : N;
   const float T = a.temp[b];
@@ -598,35 +698,41 @@ __global__ __launch_bounds__(kThreads) void tree_finish_kernel(TreeArgs a) {
   int err0 = 0;
   if (nn < 1 || nn > N) err0 = kRowBadShape;
   else if (!temp_ok(T)) err0 = kRowBadTemp;
-  if (!err0 && tid > 0 && tid < nn) {
-    const int par = a.parents[rb + tid];
-    const int tok = a.tokens[rb + tid];
-    if (par < 0 || par >= tid) atomicOr(&s_flags, kRowBadShape);
-    if (tok < 0 || tok >= V) atomicOr(&s_flags, kRowBadToken);
+  if (!err0 && tid < nn) {
+    int par = -1, tok = 0;
+    if (tid > 0) {
+      par = a.parents[rb + tid];
+      tok = a.tokens[rb + tid];
+      if (par < 0 || par >= tid) atomicOr(&s_flags, kRowBadShape);
+      if (tok < 0 || tok >= V) atomicOr(&s_flags, kRowBadToken);
+    }
     s_par[tid] = par;
     s_tok[tid] = tok;
   }
   const bool greedy = T == 0.0f;
-  const float k2 = greedy ? 0.0f : (err0 ? 0.0f : log2e_over_t(T));
+  const float k2 = (greedy || err0) ? 0.0f : log2e_over_t(T);
+  const bool cache = !err0 && nn * n_chunks <= kTreePartCache;
+  if (cache) {
+    for (int i = tid; i < nn * n_chunks; i += kThreads) s_part[i] = a.part[rb * n_chunks + i];
+  }
+  __syncthreads();
   if (!err0 && tid < nn) {
     RowStats rs;
-    if (!merge_row(a.part + (rb + tid) * n_chunks, n_chunks, greedy, &rs))
-      atomicOr(&s_flags, kRowNonFinite);
+    const Partial* pp = cache ? s_part + tid * n_chunks : a.part + (rb + tid) * n_chunks;
+    if (!merge_row(pp, n_chunks, greedy, &rs)) atomicOr(&s_flags, kRowNonFinite);
     s_rows[tid] = rs;
   }
   __syncthreads();
   const int err = err0 | (s_flags & kRowErrorMask);
   if (err) {
-    if (c == 0) {
-      for (int i = tid; i < N; i += kThreads) {
-        a.out_tokens[rb + i] = -1;
-        if (i < N - 1) a.path_nodes[(long long)b * (N - 1) + i] = -1;
-        if (a.p_at) a.p_at[rb + i] = 0.0f;
-      }
-      if (tid == 0) {
-        a.num_accepted[b] = -1;
-        if (a.row_status) a.row_status[b] = err;
-      }
+    for (int i = tid; i < N; i += kThreads) {
+      a.out_tokens[rb + i] = -1;
+      if (i < N - 1) a.path_nodes[(long long)b * (N - 1) + i] = -1;
+      if (a.p_at) a.p_at[rb + i] = 0.0f;
+    }
+    if (tid == 0) {
+      a.num_accepted[b] = -1;
+      if (a.row_status) a.row_status[b] = err;
     }
     return;
   }
@@ -640,91 +746,118 @@ __global__ __launch_bounds__(kThreads) void tree_finish_kernel(TreeArgs a) {
   }
   __syncthreads();
 
-  if (tid == 0) {
-    int node = 0, depth = 0, nrem = 0;
-    double removed = 0.0;
+  // Walk: one lane per node; at each level the current node's children are
+  // tested in index order through a prefix sum of the removed mass.
+  if (tid < 64) {
+    const int i = tid;
+    int node = 0, depth = 0;
+    unsigned long long removed = 0ull;
     while (true) {
-      int accepted = -1;
-      nrem = 0;
-      removed = 0.0;
-      for (int ch = node + 1; ch < nn; ++ch) {
-        if (s_par[ch] != node) continue;
-        const int tok = s_tok[ch];
-        bool dup = false;
-        for (int r = 0; r < nrem; ++r) dup |= s_rem[r] == tok;
-        const double denom = 1.0 - removed;
-        const double ratio = (dup || !(denom > 0.0)) ? 0.0 : s_pn[ch] / denom;
-        if (s_u[ch] < ratio) { accepted = ch; break; }
-        if (!dup) { s_rem[nrem++] = tok; removed += s_pn[ch]; }
+      const bool child = i > node && i < nn && s_par[i] == node;
+      const unsigned long long kids = __ballot(child);
+      if (!kids) break;   // leaf: bonus draw from p
+      // a sibling repeating an earlier sibling's token has nothing left to accept
+      bool dup = false;
+      if (child) {
+        unsigned long long before = kids & ((1ull << i) - 1ull);
+        while (before) {
+          const int j = __ffsll((long long)before) - 1;
+          before &= before - 1ull;
+          dup |= s_tok[j] == s_tok[i];
+        }
       }
-      if (accepted < 0) break;
-      s_path[depth++] = accepted;
-      node = accepted;
+      const double mass = (child && !dup) ? s_pn[i] : 0.0;
+      double incl = mass;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o, 64);
+        if (i >= o) incl += y;
+      }
+      double excl = __shfl_up(incl, 1, 64);
+      if (i == 0) excl = 0.0;
+      const double denom = 1.0 - excl;
+      const double ratio = (child && !dup && denom > 0.0) ? s_pn[i] / denom : 0.0;
+      const unsigned long long acc = __ballot(child && s_u[i] < ratio);
+      if (acc) {
+        const int first = __ffsll((long long)acc) - 1;
+        if (i == 0) s_path[depth] = first;
+        ++depth;
+        node = first;
+        continue;
+      }
+      removed = __ballot(child && !dup);
+      break;
     }
-    s_stop = node;
-    s_depth = depth;
-    s_nrem = nrem;
-    s_remmass = removed;
+    if (i == 0) {
+      s_stop = node;
+      s_depth = depth;
+      s_removed = removed;
+    }
   }
   __syncthreads();
-  const int stop = s_stop, depth = s_depth, nrem = s_nrem;
+  const int stop = s_stop, depth = s_depth;
+  const unsigned long long removed = s_removed;
 
   int token;
   int warn = 0;
   if (greedy) {
-    if (c != 0) return;
     token = s_rows[stop].amax;
   } else {
+    const RowStats st = s_rows[stop];
+    // chunk masses of p at the stop node from its partials, minus the
+    // rejected siblings' probabilities
+    if (tid < n_chunks) {
+      const Partial q = cache ? s_part[stop * n_chunks + tid] : a.part[(rb + stop) * n_chunks + tid];
+      double m = q.s > 0.0 ? q.s * exp2((double)q.c - (double)st.c) / st.s : 0.0;
+      unsigned long long rm = removed;
+      const int lo = tid * kChunk, hi = lo + kChunk;
+      while (rm) {
+        const int j = __ffsll((long long)rm) - 1;
+        rm &= rm - 1ull;
+        if (s_tok[j] >= lo && s_tok[j] < hi) m -= s_pn[j];
+      }
+      s_mass[tid] = m > 0.0 ? m : 0.0;
+    }
+    __syncthreads();
+    double R = 0.0;
+    for (int j = 0; j < n_chunks; ++j) R += s_mass[j];
+    bool masked = removed != 0ull;
+    if (!(R > 0.0)) {
+      // every sibling's token took the whole mass (rounding only): draw from p
+      warn |= kRowWarnRZero;
+      masked = false;
+      if (tid < n_chunks) {
+        const Partial q = cache ? s_part[stop * n_chunks + tid] : a.part[(rb + stop) * n_chunks + tid];
+        s_mass[tid] = q.s > 0.0 ? q.s * exp2((double)q.c - (double)st.c) / st.s : 0.0;
+      }
+      __syncthreads();
+    }
     StopDist d;
     d.prow = (const char*)a.target + (rb + stop) * (long long)V * (DT ? 2 : 4);
     d.qrow = d.prow;
     d.residual = 0;
-    d.p_greedy = 0;
-    d.p_amax = 0;
     d.p_k = k2;
-    d.p_c = s_rows[stop].c;
-    d.p_inv_s = (float)(1.0 / s_rows[stop].s);
+    d.p_c = st.c;
+    d.p_inv_s = (float)(1.0 / st.s);
     d.q_greedy = 0;
     d.q_amax = 0;
     d.q_k = d.q_c = d.q_inv_s = 0.0f;
-    // bits of this thread's 32 elements that belong to rejected siblings
-    auto mask_for = [&](int chunk) -> uint32_t {
-      const int e0 = chunk * kChunk + tid * kPerThread;
-      uint32_t mk = 0u;
-      for (int r = 0; r < nrem; ++r) {
-        const int off = s_rem[r] - e0;
-        if (off >= 0 && off < kPerThread) mk |= 1u << off;
-      }
-      return mk;
-    };
-    const double m = chunk_mass<DT>(d, V, c, a.vec_ok, mask_for(c), s_scan);
-    if (tid == 0) a.mass[(long long)b * n_chunks + c] = m;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.counter[b], 1) == n_chunks - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (tid < n_chunks) s_mass[tid] = a.mass[(long long)b * n_chunks + tid];
-    __syncthreads();
-    double R = 0.0;
-    for (int j = 0; j < n_chunks; ++j) R += s_mass[j];
-    bool masked = nrem > 0;
-    if (!(R > 0.0)) {
-      warn |= kRowWarnRZero;
-      masked = false;
-      for (int j = 0; j < n_chunks; ++j) {
-        const double mj = chunk_mass<DT>(d, V, j, a.vec_ok, 0u, s_scan);
-        if (tid == 0) s_mass[j] = mj;
-      }
-      __syncthreads();
-    }
     const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)stop).y);
     choose_chunk(s_mass, n_chunks, u, &s_jc, &s_base, &s_t);
-    int last_pos;
-    const int k = chunk_select<DT>(d, V, s_jc, a.vec_ok, masked ? mask_for(s_jc) : 0u, s_base,
-                                   s_t, s_scan, s_misc, s_misc + 1, &last_pos);
-    token = k >= 0 ? k : (last_pos >= 0 ? last_pos : s_jc * kChunk);
+    const int jc = s_jc;
+    // bits of this thread's 32 elements that belong to rejected siblings
+    uint32_t mk = 0u;
+    if (masked) {
+      const int e0 = jc * kChunk + tid * kPerThread;
+      unsigned long long rm = removed;
+      while (rm) {
+        const int j = __ffsll((long long)rm) - 1;
+        rm &= rm - 1ull;
+        const int off = s_tok[j] - e0;
+        if (off >= 0 && off < kPerThread) mk |= 1u << off;
+      }
+    }
+    token = chunk_select<DT>(d, V, jc, a.vec_ok, mk, s_base, s_t, s_scan, s_misc);
   }
 
   for (int i = tid; i < N; i += kThreads) {
@@ -756,22 +889,29 @@ __global__ __launch_bounds__(kThreads) void philox_words_kernel(uint64_t seed, u
 // ---------------------------------------------------------------------------
 // Host launchers.
 
-hipError_t launch_stats(int dtype, const StatsArgs& a, long long n_items, hipStream_t st) {
-  if (dtype == 1) stats_kernel<1><<<dim3((unsigned)n_items), dim3(kThreads), 0, st>>>(a);
-  else stats_kernel<0><<<dim3((unsigned)n_items), dim3(kThreads), 0, st>>>(a);
+long long stats_items(long long n_rows, int n_chunks) { return n_rows * ((n_chunks + 1) / 2); }
+
+hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st) {
+  const long long n = stats_items(a.n_rows, a.n_chunks);
+  if (dtype == 1) stats_kernel<1><<<dim3((unsigned)n), dim3(kThreads), 0, st>>>(a);
+  else stats_kernel<0><<<dim3((unsigned)n), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_linear_finish(int dtype, const LinearArgs& a, long long n_items,
-                                hipStream_t st) {
-  if (dtype == 1) linear_finish_kernel<1><<<dim3((unsigned)n_items), dim3(kThreads), 0, st>>>(a);
-  else linear_finish_kernel<0><<<dim3((unsigned)n_items), dim3(kThreads), 0, st>>>(a);
+hipError_t launch_linear_finish(int dtype, const LinearArgs& a, hipStream_t st) {
+  const unsigned n2 = (unsigned)((long long)a.B * a.n_chunks);
+  if (dtype == 1) linear_mass_kernel<1><<<dim3(n2), dim3(kThreads), 0, st>>>(a);
+  else linear_mass_kernel<0><<<dim3(n2), dim3(kThreads), 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dtype == 1) linear_select_kernel<1><<<dim3((unsigned)a.B), dim3(kThreads), 0, st>>>(a);
+  else linear_select_kernel<0><<<dim3((unsigned)a.B), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_tree_finish(int dtype, const TreeArgs& a, long long n_items, hipStream_t st) {
-  if (dtype == 1) tree_finish_kernel<1><<<dim3((unsigned)n_items), dim3(kThreads), 0, st>>>(a);
-  else tree_finish_kernel<0><<<dim3((unsigned)n_items), dim3(kThreads), 0, st>>>(a);
+hipError_t launch_tree_finish(int dtype, const TreeArgs& a, hipStream_t st) {
+  if (dtype == 1) tree_kernel<1><<<dim3((unsigned)a.B), dim3(kThreads), 0, st>>>(a);
+  else tree_kernel<0><<<dim3((unsigned)a.B), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
