@@ -7,11 +7,13 @@ linear verify B=32, gamma=5, V=32000 bf16 (160 draft positions per step).
 Other workloads (--workload) measure the remaining configurations.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by
-torch.cuda.synchronize().  The dominant kernel's duration comes from HIP
-events recorded on the call's own stream around that kernel, in every
-timed step (one-shot hook of the library, or events around the call when
-the call is one kernel).  Inputs rotate over enough copies to exceed the
-256 MB Infinity Cache, so the logits come from HBM.
+torch.cuda.synchronize(); the K steps are captured as one HIP graph and
+replayed (one untimed replay first), so host launch overhead does not pace
+the GPU.  The dominant kernel's duration comes from the same K steps run
+right after, each with a pair of HIP events attached to that kernel's
+dispatch on the call's own stream (the library's one-shot timing hook).
+Inputs rotate over enough copies to exceed the 256 MB Infinity Cache, so
+the logits come from HBM.
 
 Prints one JSON line.
 """
@@ -171,10 +173,8 @@ def main():
 
         def step(i, ev=None):
             if ev is not None:
-                ev[0].record(stream)
+                sv.profile_next(ev[0], ev[1])
             sv.verify_attn(qd, kd, vd, pld, par, outputs=outs)
-            if ev is not None:
-                ev[1].record(stream)
         config = dict(workload=wl, B=B, H=H, N=N, head_dim=dd, prefix_len=L,
                       mask="tree (64-node best-first top-4 trees)", input_dtype="bf16")
         unit = "verified query tokens/s"
@@ -207,7 +207,7 @@ def main():
             def step(i, ev=None):
                 s = sets[i % nc]
                 if ev is not None:
-                    sv.profile_next(ev[0], ev[1], ensure_created=False)
+                    sv.profile_next(ev[0], ev[1])
                 sv.verify_linear(s["t"], s["d"], off, tok, tt, td, seed=0, step=i, workspace=ws,
                                  outputs=outs)
             config = dict(workload=wl, B=Bn, gamma=("ragged 2/4/8" if wl == "bimodal_v152k"
@@ -234,7 +234,7 @@ def main():
 
             def step(i, ev=None):
                 if ev is not None:
-                    sv.profile_next(ev[0], ev[1], ensure_created=False)
+                    sv.profile_next(ev[0], ev[1])
                 sv.verify_tree(sets[i % nc], par, tok, tt, n_nodes=nn, seed=0, step=i,
                                workspace=ws, outputs=outs)
             config = dict(workload=wl, B=Bn, nodes=N, V=d["V"], mode="TOPK", input_dtype="bf16",
@@ -247,20 +247,14 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a_, b_ in evs:          # create the HIP events before any capture
-        a_.record()
-        b_.record()
-    torch.cuda.synchronize()
     use_graph = not args.no_graph and wl != "attn_tree"
     if use_graph:
         # The K timed steps are captured once and replayed as one graph, so
-        # the host does not pace the GPU; the per-step events are captured too.
+        # the host does not pace the GPU.
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(args.steps):
-                step(args.warmup + i, evs[i])
+                step(args.warmup + i)
         graph.replay()          # untimed: uploads the graph
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -270,9 +264,16 @@ def main():
     else:
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(args.warmup + i, evs[i])
+            step(args.warmup + i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+    # Dominant kernel's duration: the same K steps again, each with a pair of
+    # HIP events attached to that kernel's dispatch on the call's stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     avg_kern_s = float(np.mean(kern_ms)) / 1e3
     ms_per_step = wall * 1e3 / args.steps

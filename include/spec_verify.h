@@ -212,11 +212,13 @@ int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_i
                              int n_rows, int n_slots, uint32_t* out_words, hipStream_t stream);
 
 /*
- * Diagnostic timing hook (for benchmarks and profilers): the next
- * spec_verify_linear or spec_verify_tree call records `begin` on its stream
- * right before its vocabulary pass and `end` right after it, then forgets
- * both.  Either may be NULL to clear the hook.  Process-wide and not
- * thread-safe; it changes no output and skips no work.
+ * Diagnostic timing hook (for benchmarks): the next spec_verify_linear,
+ * spec_verify_tree or spec_verify_attn call attaches `begin` and `end` to the
+ * dispatch of its dominant kernel (the vocabulary pass, or the attention
+ * kernel), so the events bracket that kernel alone, as a profiler sees it;
+ * then the hook forgets both.  Either may be NULL to clear the hook.  Not
+ * for use under stream capture.  Process-wide and not thread-safe; it
+ * changes no output and skips no work.
  */
 int spec_verify_profile_next(hipEvent_t begin, hipEvent_t end);
 

@@ -21,7 +21,7 @@ Layout layout(long long n_rows, int B, int V, bool linear) {
   const int nc = n_chunks_for(V);
   Layout l;
   l.part = 0;
-  l.mass = align_up((size_t)n_rows * nc * sizeof(sv::Partial));
+  l.mass = align_up((size_t)n_rows * nc * sv::kPartsPerChunk * sizeof(sv::Partial));
   l.rec = l.mass + (linear ? align_up((size_t)B * nc * sizeof(double)) : 0);
   l.total = l.rec + (linear ? align_up((size_t)B * sizeof(sv::LinRecord)) : 0);
   if (l.total == 0) l.total = kAlign;
@@ -36,11 +36,7 @@ hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
 hipError_t launch_stats_timed(int dtype, const sv::StatsArgs& s, hipStream_t stream) {
   hipEvent_t b = g_prof_begin, e = g_prof_end;
   g_prof_begin = g_prof_end = nullptr;
-  if (b && e && hipEventRecord(b, stream) != hipSuccess) return hipErrorUnknown;
-  const hipError_t err = sv::launch_stats(dtype, s, stream);
-  if (err != hipSuccess) return err;
-  if (b && e && hipEventRecord(e, stream) != hipSuccess) return hipErrorUnknown;
-  return hipSuccess;
+  return sv::launch_stats(dtype, s, stream, b, e);
 }
 
 int check_workspace(void* ws, size_t bytes, size_t need) {
@@ -247,7 +243,9 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
   a.scale_log2 = (float)((double)scale * sv::kLog2e);
   a.out = (uint16_t*)out;
   a.lse = lse;
-  if (sv::launch_attn(a, stream) != hipSuccess) return SV_ERR_HIP;
+  hipEvent_t b = g_prof_begin, e = g_prof_end;
+  g_prof_begin = g_prof_end = nullptr;
+  if (sv::launch_attn(a, stream, b, e) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 

@@ -22,6 +22,8 @@
 // 312), so the matrix cores are used because the product is dense, not to
 // reach their peak.  Mask semantics: kwkr.cn/news/620872 §2.1 (causal verify),
 // cf-1.com/news/5632551 §5.4 and the lonae tree-attention paragraphs (tree mask).
+#include <hip/hip_ext.h>
+
 #include "sv_common.h"
 #include "sv_internal.h"
 
@@ -230,8 +232,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
-  attn_kernel<<<dim3((unsigned)((long long)a.B * a.H)), dim3(kThreads), 0, st>>>(a);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const dim3 grid((unsigned)((long long)a.B * a.H)), block(kThreads);
+  if (ev_start && ev_stop)
+    hipExtLaunchKernelGGL(attn_kernel, grid, block, 0, st, ev_start, ev_stop, 0, a);
+  else
+    attn_kernel<<<grid, block, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -6,10 +6,15 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;          // 4 waves of 64
+constexpr int kThreads = 256;          // vocabulary pass: 4 waves of 64
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = 8192;           // vocabulary elements per work item
-constexpr int kPerThread = kChunk / kThreads;  // 32 contiguous elements per thread
+constexpr int kChunk = 8192;           // vocabulary elements per chunk
+constexpr int kWaveSpan = kChunk / kWaves;     // 2048 elements reduced by one wave
+constexpr int kPerLane = kWaveSpan / 64;       // 32 elements per lane in the vocabulary pass
+constexpr int kPartsPerChunk = kWaves;         // one partial per wave
+constexpr int kFinThreads = 1024;      // finish passes: 16 waves of 64
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kPerThread = kChunk / kFinThreads;  // 8 contiguous elements per thread
 constexpr int kMaxChunks = 64;         // => V <= 524288
 constexpr int kMaxGamma = 64;
 constexpr int kMaxNodes = 64;
@@ -90,7 +95,7 @@ __device__ __forceinline__ double word_to_uniform(uint32_t w) {
   return (double)(w >> 8) * (1.0 / 16777216.0);
 }
 
-// ---- block-wide reductions over 256 threads ---------------------------------
+// ---- wave- and block-wide reductions ----------------------------------------
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -113,56 +118,25 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
-// All threads must call these; `scratch` is __shared__ with kWaves slots.
-__device__ __forceinline__ double block_sum(double v, double* scratch) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  v = wave_sum(v);
-  __syncthreads();
-  if (lane == 0) scratch[w] = v;
-  __syncthreads();
-  double t = scratch[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) t += scratch[i];
-  return t;
-}
-
-__device__ __forceinline__ float block_max(float v, float* scratch) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  v = wave_max(v);
-  __syncthreads();
-  if (lane == 0) scratch[w] = v;
-  __syncthreads();
-  float t = scratch[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) t = fmaxf(t, scratch[i]);
-  return t;
-}
-
-__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v,
-                                                            unsigned long long* scratch) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  v = wave_max_u64(v);
-  __syncthreads();
-  if (lane == 0) scratch[w] = v;
-  __syncthreads();
-  unsigned long long t = scratch[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) t = scratch[i] > t ? scratch[i] : t;
-  return t;
-}
-
-// Exclusive prefix sum over the block in thread order plus the block total.
-// The total is formed the same way on every call, so two passes over the
-// same per-thread values agree bit for bit.
-__device__ __forceinline__ double block_exclusive_scan(double v, double* scratch,
-                                                       double* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double incl = v;
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order.
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    double y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
+    const double y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
   }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NW waves in thread order, plus the
+// block total.  The total is formed the same way on every call, so two
+// passes over the same per-thread values agree bit for bit.  All threads
+// must call it; `scratch` is __shared__ with NW slots.
+template <int NW>
+__device__ __forceinline__ double block_exclusive_scan(double v, double* scratch, double* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const double incl = wave_inclusive_scan(v);
   double excl_lane = __shfl_up(incl, 1, 64);
   if (lane == 0) excl_lane = 0.0;
   __syncthreads();
@@ -172,7 +146,7 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* scratch
   for (int i = 0; i < w; ++i) base += scratch[i];
   double t = scratch[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) t += scratch[i];
+  for (int i = 1; i < NW; ++i) t += scratch[i];
   *total = t;
   return base + excl_lane;
 }

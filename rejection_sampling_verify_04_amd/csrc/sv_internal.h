@@ -85,11 +85,12 @@ struct AttnArgs {
 };
 
 long long stats_items(long long n_rows, int n_chunks);
-hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st);
+hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_t ev_start,
+                        hipEvent_t ev_stop);
 hipError_t launch_linear_finish(int dtype, const LinearArgs& a, hipStream_t st);
 hipError_t launch_tree_finish(int dtype, const TreeArgs& a, hipStream_t st);
 hipError_t launch_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids,
                                int n_rows, int n_slots, uint32_t* out, hipStream_t st);
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace sv
