@@ -6,18 +6,22 @@
 
 namespace sv {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;          // vocabulary pass: 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 8192;           // vocabulary elements per chunk
-constexpr int kWaveSpan = kChunk / kWaves;     // 2048 elements reduced by one wave
-constexpr int kPerLane = kWaveSpan / 64;       // 32 elements per lane in the vocabulary pass
-constexpr int kPartsPerChunk = kWaves;         // one partial per wave
+constexpr int kSubSpan = 2048;         // elements per sub-segment of the vocabulary pass
+constexpr int kSubs = kChunk / kSubSpan;       // sub-segments per chunk
+constexpr int kPerLane = kSubSpan / 64;        // 32 elements per lane and sub-segment
+constexpr int kPartsPerChunk = 1;              // one Partial per (row, chunk)
 constexpr int kFinThreads = 1024;      // finish passes: 16 waves of 64
 constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kPerThread = kChunk / kFinThreads;  // 8 contiguous elements per thread
 constexpr int kMaxChunks = 64;         // => V <= 524288
 constexpr int kMaxGamma = 64;
 constexpr int kMaxNodes = 64;
+constexpr int kMaxDevices = 64;      // per-device caches of launch shapes
 
 // Row status bits (mirrors the public header).
 constexpr int kRowBadToken = 1;
@@ -31,7 +35,7 @@ constexpr int kRowWarnRZero = 512;
 constexpr double kLog2e = 1.4426950408889634074;
 
 // One chunk's reduction of one logit row.  For a sampled row (T > 0):
-// c = an offset in log2 units and s = sum_v exp2(x_v * k - c) with
+// c = an integer offset in log2 units and s = sum_v exp2(x_v * k - c) with
 // k = log2(e) / T; the pair stands for sum_v exp2(x_v * k) = s * 2^c.
 // For a greedy row (T = 0): c = the maximum logit and amax its first index.
 struct Partial {
@@ -96,38 +100,102 @@ __device__ __forceinline__ double word_to_uniform(uint32_t w) {
 }
 
 // ---- wave- and block-wide reductions ----------------------------------------
+//
+// Within each row of 16 lanes the wave combines values with DPP lane moves
+// (a butterfly for reductions, shifts for prefix sums); the four row results
+// are then combined through readlane.  All 64 lanes must be active.
 
+// DPP move of a 32-bit value; lanes whose source is outside the row read 0.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return (hi << 32) | lo;
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i of 8 <- 7 - i
+constexpr int kDppMirror = 0x140;     // lane i of 16 <- 15 - i
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppWaveShr1 = 0x138;   // lane i <- lane i - 1 across the wave
+
+// Sum over the wave; every lane gets the same result.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    unsigned long long w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
+  uint64_t w = dpp_u64<kDppXor1>(v);
+  v = w > v ? w : v;
+  w = dpp_u64<kDppXor2>(v);
+  v = w > v ? w : v;
+  w = dpp_u64<kDppHalfMirror>(v);
+  v = w > v ? w : v;
+  w = dpp_u64<kDppMirror>(v);
+  v = w > v ? w : v;
+  uint64_t r = readlane_u64(v, 0);
+  w = readlane_u64(v, 16);
+  r = w > r ? w : r;
+  w = readlane_u64(v, 32);
+  r = w > r ? w : r;
+  w = readlane_u64(v, 48);
+  return w > r ? w : r;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order.
 __device__ __forceinline__ double wave_inclusive_scan(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  return v;
+  v += dpp_f64<kDppShr1>(v);
+  v += dpp_f64<kDppShr2>(v);
+  v += dpp_f64<kDppShr4>(v);
+  v += dpp_f64<kDppShr8>(v);
+  const int row = (threadIdx.x & 63) >> 4;
+  const double t0 = readlane_f64(v, 15), t1 = readlane_f64(v, 31), t2 = readlane_f64(v, 47);
+  const double add = row == 0 ? 0.0 : (row == 1 ? t0 : (row == 2 ? t0 + t1 : (t0 + t1) + t2));
+  return v + add;
 }
+
+// The inclusive value of the previous lane (0 for lane 0).
+__device__ __forceinline__ double wave_shift_up1(double v) { return dpp_f64<kDppWaveShr1>(v); }
 
 // Exclusive prefix sum over a block of NW waves in thread order, plus the
 // block total.  The total is formed the same way on every call, so two
@@ -137,8 +205,7 @@ template <int NW>
 __device__ __forceinline__ double block_exclusive_scan(double v, double* scratch, double* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const double incl = wave_inclusive_scan(v);
-  double excl_lane = __shfl_up(incl, 1, 64);
-  if (lane == 0) excl_lane = 0.0;
+  const double excl_lane = wave_shift_up1(incl);
   __syncthreads();
   if (lane == 63) scratch[w] = incl;
   __syncthreads();

@@ -43,6 +43,9 @@
 // (kwkr §5.3; lonae tree-attention paragraphs).
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "sv_common.h"
 #include "sv_internal.h"
 
@@ -74,7 +77,19 @@ __device__ int find_batch_row(const int* __restrict__ off, int B, long long x, i
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: per-wave statistics of every logit row.
+// Pass 1: statistics of every logit chunk.
+//
+// One wave reduces one chunk (8192 elements) of one row at a time, as four
+// sub-segments of 2048 elements; each of the wave's load instructions reads
+// 1 KB of consecutive bytes.  Each lane keeps a running offset and sum over
+// its 128 elements of the chunk, and the lanes are combined once per chunk.
+// The grid is sized to stay resident: wave g of G takes chunks g, g + G,
+// g + 2G, ... of the concatenated rows, so at any moment the grid sweeps one
+// contiguous window of the logits, and each wave's sub-segment loads run
+// RING sub-segments ahead of the one it reduces, across chunk boundaries.
+//
+// Offsets of sampled rows are integers (ceil of the scaled maximum), so every
+// rescale of a sum is an exact power of two.
 
 // One wave's 2048-element segment: lane l's vector j covers elements
 // seg0 + (j * 64 + l) * EPV + [0, EPV), so each load instruction of the wave
@@ -86,21 +101,27 @@ struct SegLoad {
   static constexpr int NV = kPerLane / EPV;      // loads per lane per segment
   uint4 raw[NV];
 
+  // Vectors past V read as -inf.  Rows are read once, so the loads carry the
+  // non-temporal hint.  With vectors valid (V a multiple of EPV) a vector is
+  // either wholly inside the row or wholly past it.
   __device__ __forceinline__ void issue(const char* rowp, int V, int seg0) {
     const int lane = threadIdx.x & 63;
+    constexpr uint32_t kNegInf = DT ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int e0 = seg0 + (j * 64 + lane) * EPV;
-      if (e0 < V) raw[j] = *(const uint4*)(rowp + (long long)e0 * ES);
-      else raw[j] = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+      if (e0 < V) {
+        const u32x4_t w = __builtin_nontemporal_load((const u32x4_t*)(rowp + (long long)e0 * ES));
+        raw[j] = make_uint4(w.x, w.y, w.z, w.w);
+      } else {
+        raw[j] = make_uint4(kNegInf, kNegInf, kNegInf, kNegInf);
+      }
     }
   }
 
-  __device__ __forceinline__ void unpack(int V, int seg0, float v[kPerLane]) const {
-    const int lane = threadIdx.x & 63;
+  __device__ __forceinline__ void unpack(float v[kPerLane]) const {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int e0 = seg0 + (j * 64 + lane) * EPV;
       if (DT == 1) {
         const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
 #pragma unroll
@@ -113,10 +134,6 @@ struct SegLoad {
         v[j * 4 + 1] = __uint_as_float(raw[j].y);
         v[j * 4 + 2] = __uint_as_float(raw[j].z);
         v[j * 4 + 3] = __uint_as_float(raw[j].w);
-      }
-      if (e0 >= V) {
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) v[j * EPV + k] = -__builtin_huge_valf();
       }
     }
   }
@@ -138,104 +155,243 @@ __device__ __forceinline__ void seg_load_scalar(const char* rowp, int V, int seg
   }
 }
 
-// Reduce one wave's segment (this lane's 32 values, index order as loaded).
+constexpr int kStatsCache = 1024;  // batch rows whose offsets/temperatures go to LDS
+
+// Largest j in [0, B) whose key off[j] + add * j is <= x, found by one wave
+// with 64 probes per round (B <= 64: one round; B <= 4096: two).
+__device__ __forceinline__ int wave_find_batch_row(const int* off, int B, long long x, int add) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, len = B;
+  while (len > 1) {
+    const int step = (len + 63) >> 6;
+    bool pred = false;
+    if (lane * step < len) {
+      const int j = lo + lane * step;
+      pred = (long long)off[j] + (long long)add * j <= x;
+    }
+    const unsigned long long m = __ballot(pred);
+    const int best = m ? 63 - __builtin_clzll(m) : 0;
+    lo += best * step;
+    len = min(step, len - best * step);
+  }
+  return lo;
+}
+
+// s * 2^d for an integer-valued d <= 0 (exact; -inf and huge |d| give 0).
+__device__ __forceinline__ double scale_pow2(double s, float d) {
+  return __builtin_ldexp(s, (int)fmaxf(d, -4096.0f));
+}
+
+// A lane's running statistics over its elements of one chunk.
+struct LaneStats {
+  float c;     // sampled: integer log2 offset; greedy: largest value so far
+  int idx;     // greedy: first index of that value
+  double s;    // sampled: sum of 2^(x k - c)
+};
+
+// Fold one sub-segment (this lane's 32 values, in increasing index order:
+// element e of vector j sits at seg0 + (j * 64 + lane) * EPV + e).
 template <int DT>
-__device__ __forceinline__ Partial seg_partial(float v[kPerLane], int seg0, float T) {
+__device__ __forceinline__ void lane_fold(float v[kPerLane], int seg0, bool greedy, float k2,
+                                          LaneStats& st) {
   constexpr int EPV = SegLoad<DT>::EPV;
   constexpr int NV = SegLoad<DT>::NV;
   const int lane = threadIdx.x & 63;
-  if (T == 0.0f) {
-    // First maximum: the lane's elements are in increasing index order.
-    float bv = -__builtin_huge_valf();
-    int bi = seg0 + lane * EPV;
+  if (greedy) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        const float x = v[j * EPV + k];
-        const bool gt = x > bv;
-        bv = gt ? x : bv;
-        bi = gt ? seg0 + (j * 64 + lane) * EPV + k : bi;
+      for (int e = 0; e < EPV; ++e) {
+        const float x = v[j * EPV + e];
+        const bool gt = x > st.c;
+        st.c = gt ? x : st.c;
+        st.idx = gt ? seg0 + (j * 64 + lane) * EPV + e : st.idx;
       }
     }
-    const unsigned long long key =
-        ((unsigned long long)float_order_key(bv) << 32) | (0xffffffffu - (uint32_t)bi);
-    const unsigned long long best = wave_max_u64(key);
-    return Partial{float_from_order_key((uint32_t)(best >> 32)),
-                   (int)(0xffffffffu - (uint32_t)best), 0.0};
+    return;
   }
-  // Sampled row: one offset for the wave, c = fl(max * k), then a pairwise
-  // sum of 2^(x k - c) per lane and a float64 sum over the lanes.
-  const float k2 = log2e_over_t(T);
   float m = -__builtin_huge_valf();
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e) m = fmaxf(m, v[e]);
-  m = wave_max(m);
-  if (!(m > -__builtin_huge_valf())) return Partial{-__builtin_huge_valf(), 0, 0.0};
-  const float c = m * k2;
+  const float mk = ceilf(m * k2);
+  if (mk > st.c) {
+    st.s = scale_pow2(st.s, st.c - mk);
+    st.c = mk;
+  }
+  const float cu = st.c > -__builtin_huge_valf() ? st.c : 0.0f;  // all -inf so far: terms are 0
 #pragma unroll
-  for (int e = 0; e < kPerLane; ++e) v[e] = exp2_hw(fmaf(v[e], k2, -c));
+  for (int e = 0; e < kPerLane; ++e) v[e] = exp2_hw(fmaf(v[e], k2, -cu));
 #pragma unroll
   for (int w = kPerLane / 2; w >= 1; w >>= 1) {
 #pragma unroll
     for (int e = 0; e < w; ++e) v[e] += v[e + w];
   }
-  const double S = wave_sum((double)v[0]);
-  return Partial{c, 0, S};
+  st.s += (double)v[0];
 }
 
-template <int DT, int CPW>
+// Combine the wave's lanes into the chunk's Partial.
+__device__ __forceinline__ Partial wave_combine(const LaneStats& st, bool greedy) {
+  if (greedy) {
+    const unsigned long long key =
+        ((unsigned long long)float_order_key(st.c) << 32) | (0xffffffffu - (uint32_t)st.idx);
+    const unsigned long long best = wave_max_u64(key);
+    return Partial{float_from_order_key((uint32_t)(best >> 32)),
+                   (int)(0xffffffffu - (uint32_t)best), 0.0};
+  }
+  const float C = wave_max(st.c);
+  if (!(C > -__builtin_huge_valf())) return Partial{-__builtin_huge_valf(), 0, 0.0};
+  const double t = st.s != 0.0 ? scale_pow2(st.s, st.c - C) : 0.0;
+  return Partial{C, 0, wave_sum(t)};
+}
+
+template <int DT>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
-  __shared__ int s_best;
+  constexpr int RING = 2;               // sub-segments in flight per wave
+  __shared__ int s_i[kStatsCache + 1];
+  __shared__ float s_f0[kStatsCache], s_f1[kStatsCache];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long long item = blockIdx.x;
-  const int n_tiles = (a.n_chunks + CPW - 1) / CPW;
-  const long long row = item / n_tiles;
-  const int tile = (int)(item - row * n_tiles);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int V = a.V;
+  const uint32_t nc = (uint32_t)a.n_chunks;
+  const uint32_t total = (uint32_t)a.n_rows * nc;   // < 2^31 (checked by the host)
+  const uint32_t G = gridDim.x * kWaves;
+  const uint32_t Gq = G / nc, Gr = G - Gq * nc;
   const long long rowbytes = (long long)V * SegLoad<DT>::ES;
-  const char* rowp = row < a.n_a ? (const char*)a.rows_a + row * rowbytes
-                                 : (const char*)a.rows_b + (row - a.n_a) * rowbytes;
+  auto row_ptr = [&](uint32_t r) -> const char* {
+    return r < a.n_a ? (const char*)a.rows_a + (long long)r * rowbytes
+                     : (const char*)a.rows_b + ((long long)r - a.n_a) * rowbytes;
+  };
 
-  // Issue this wave's loads for every chunk of the tile before looking up
-  // the row's temperature.
-  SegLoad<DT> ld[CPW];
-  if (a.vec_ok) {
+  uint32_t u = blockIdx.x * kWaves + wave;
+  uint32_t row = u / nc, ch = u - row * nc;
+  SegLoad<DT> ring[RING];
+  // The first chunk's loads go out before anything else; an unused tree
+  // row is still allocated, so reading it is harmless.
+  if (a.vec_ok && u < total) {
 #pragma unroll
-    for (int k = 0; k < CPW; ++k) {
-      const int ch = tile * CPW + k;
-      if (ch < a.n_chunks) ld[k].issue(rowp, V, ch * kChunk + wave * kWaveSpan);
-    }
+    for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
   }
 
-  float T;
-  if (a.tree) {
-    const int b = (int)(row / a.N);
-    const int node = (int)(row - (long long)b * a.N);
-    const int nn = a.n_nodes ? a.n_nodes[b] : a.N;
-    if (node >= nn) return;               // unused node row: never read
-    T = a.temp_a[b];
-  } else if (row < a.n_a) {
-    T = a.temp_a[find_batch_row(a.offsets, a.B, row, 1, &s_best)];
-  } else {
-    T = a.temp_b[find_batch_row(a.offsets, a.B, row - a.n_a, 0, &s_best)];
+  const bool cache = a.B <= kStatsCache;
+  if (cache) {
+    for (int i = threadIdx.x; i <= a.B; i += kThreads) {
+      if (a.tree) {
+        if (i < a.B) {
+          s_i[i] = a.n_nodes ? a.n_nodes[i] : a.N;
+          s_f0[i] = a.temp_a[i];
+        }
+      } else {
+        s_i[i] = a.offsets[i];
+        if (i < a.B) {
+          s_f0[i] = a.temp_a[i];
+          s_f1[i] = a.temp_b[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (u >= total) return;
+
+  // Whether a row's partials are needed (tree rows past n_nodes are not).
+  auto row_used = [&](uint32_t r) -> bool {
+    if (!a.tree) return true;
+    const uint32_t b = r / (uint32_t)a.N;
+    const int node = (int)(r - b * (uint32_t)a.N);
+    const int nn = cache ? s_i[b] : (a.n_nodes ? a.n_nodes[b] : a.N);
+    return node < nn;
+  };
+  auto row_temp = [&](uint32_t r) -> float {
+    if (a.tree) {
+      const uint32_t b = r / (uint32_t)a.N;
+      return cache ? s_f0[b] : a.temp_a[b];
+    }
+    if (r < a.n_a) {
+      if (cache) return s_f0[wave_find_batch_row(s_i, a.B, r, 1)];
+      return a.temp_a[wave_find_batch_row(a.offsets, a.B, r, 1)];
+    }
+    const long long x = (long long)r - a.n_a;
+    if (cache) return s_f1[wave_find_batch_row(s_i, a.B, x, 0)];
+    return a.temp_b[wave_find_batch_row(a.offsets, a.B, x, 0)];
+  };
+  auto advance = [&](uint32_t& r, uint32_t& c) {
+    c += Gr;
+    r += Gq;
+    if (c >= nc) {
+      c -= nc;
+      ++r;
+    }
+  };
+  auto chunk_begin = [&](uint32_t c, float T, bool& greedy, float& k2) {
+    greedy = T == 0.0f;
+    k2 = greedy ? 0.0f : log2e_over_t(T);
+    return LaneStats{-__builtin_huge_valf(), (int)c * kChunk + lane * SegLoad<DT>::EPV, 0.0};
+  };
+  auto chunk_end = [&](uint32_t r, uint32_t c, bool ok, bool greedy, const LaneStats& st) {
+    // a bad temperature is reported by the finish pass
+    const Partial p = ok ? wave_combine(st, greedy) : Partial{0.0f, 0, 0.0};
+    if (lane == 0) a.part[(long long)r * nc + c] = p;
+  };
+
+  if (!a.vec_ok) {                        // unaligned rows: plain loads, no prefetch
+    for (; u < total; u += G, advance(row, ch)) {
+      if (!row_used(row)) continue;
+      const float T = row_temp(row);
+      const bool ok = temp_ok(T);
+      bool greedy;
+      float k2;
+      LaneStats st = chunk_begin(ch, T, greedy, k2);
+      if (ok) {
+        for (int k = 0; k < kSubs; ++k) {
+          float v[kPerLane];
+          const int seg0 = (int)ch * kChunk + k * kSubSpan;
+          seg_load_scalar<DT>(row_ptr(row), V, seg0, v);
+          lane_fold<DT>(v, seg0, greedy, k2, st);
+        }
+      }
+      chunk_end(row, ch, ok, greedy, st);
+    }
+    return;
   }
 
-  Partial* out = a.part + row * (long long)a.n_chunks * kPartsPerChunk;
+  bool used = row_used(row);
+  float T = used ? row_temp(row) : 0.0f;
+  for (;;) {
+    uint32_t row1 = row, ch1 = ch;
+    advance(row1, ch1);
+    const bool has1 = u + G < total;
+    const bool used1 = has1 && row_used(row1);
+    const float T1 = used1 ? row_temp(row1) : 0.0f;
+    const char* p0 = row_ptr(row);
+    const char* p1 = row_ptr(row1);
+    const bool ok = used && temp_ok(T);
+    bool greedy;
+    float k2;
+    LaneStats st = chunk_begin(ch, T, greedy, k2);
 #pragma unroll
-  for (int k = 0; k < CPW; ++k) {
-    const int ch = tile * CPW + k;
-    if (ch >= a.n_chunks) break;
-    const int seg0 = ch * kChunk + wave * kWaveSpan;
-    Partial p{0.0f, 0, 0.0};
-    if (temp_ok(T)) {                     // a bad temperature is reported by the finish pass
-      float v[kPerLane];
-      if (a.vec_ok) ld[k].unpack(V, seg0, v);
-      else seg_load_scalar<DT>(rowp, V, seg0, v);
-      p = seg_partial<DT>(v, seg0, T);
+    for (int k = 0; k < kSubs; ++k) {
+      SegLoad<DT>& cur = ring[k % RING];
+      const int seg0 = (int)ch * kChunk + k * kSubSpan;
+      if (ok) {
+        float v[kPerLane];
+        cur.unpack(v);
+        lane_fold<DT>(v, seg0, greedy, k2, st);
+      }
+      // refill this slot with the sub-segment RING ahead
+      const int kn = k + RING;
+      if (kn < kSubs) {
+        if (used) cur.issue(p0, V, (int)ch * kChunk + kn * kSubSpan);
+      } else if (used1) {
+        cur.issue(p1, V, (int)ch1 * kChunk + (kn - kSubs) * kSubSpan);
+      }
     }
-    if (lane == 0) out[ch * kPartsPerChunk + wave] = p;
+    if (used) chunk_end(row, ch, ok, greedy, st);
+    if (!has1) break;
+    u += G;
+    row = row1;
+    ch = ch1;
+    used = used1;
+    T = T1;
   }
 }
 
@@ -248,49 +404,42 @@ struct RowStats {
   double s;    // sum of 2^(x k - c) (sampled)
 };
 
-// Merge one row's partials with one wave (lanes over partials, in index
-// order); returns false when the row has no finite maximum.
-__device__ bool merge_row_wave(const Partial* __restrict__ p, int n_parts, bool greedy,
-                               RowStats* out) {
+static_assert(kMaxChunks * kPartsPerChunk <= 64, "one partial per lane");
+
+// This lane's partial of a row (lane j holds partial j), or an empty one.
+__device__ __forceinline__ Partial lane_partial(const Partial* __restrict__ p, int n_parts) {
   const int lane = threadIdx.x & 63;
-  Partial q[kMaxChunks * kPartsPerChunk / 64];
-#pragma unroll
-  for (int k = 0; k < kMaxChunks * kPartsPerChunk / 64; ++k) {
-    const int j = lane + 64 * k;
-    q[k] = j < n_parts ? p[j] : Partial{-__builtin_huge_valf(), 0x7fffffff, 0.0};
-  }
+  return lane < n_parts ? p[lane] : Partial{-__builtin_huge_valf(), 0x7fffffff, 0.0};
+}
+
+// Merge one row's partials, loaded one per lane, with one wave; returns false
+// when the row has no finite maximum.
+__device__ bool merge_parts_wave(const Partial& q, int n_parts, bool greedy, RowStats* out) {
+  const int lane = threadIdx.x & 63;
   if (greedy) {
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int k = 0; k < kMaxChunks * kPartsPerChunk / 64; ++k) {
-      const int j = lane + 64 * k;
-      if (j < n_parts) {
-        const unsigned long long key = ((unsigned long long)float_order_key(q[k].c) << 32) |
-                                       (0xffffffffu - (uint32_t)q[k].amax);
-        best = key > best ? key : best;
-      }
-    }
-    best = wave_max_u64(best);
+    const unsigned long long key =
+        lane < n_parts ? ((unsigned long long)float_order_key(q.c) << 32) |
+                             (0xffffffffu - (uint32_t)q.amax)
+                       : 0ull;
+    const unsigned long long best = wave_max_u64(key);
     const float m = float_from_order_key((uint32_t)(best >> 32));
     out->c = m;
     out->amax = (int)(0xffffffffu - (uint32_t)best);
     out->s = 0.0;
     return m > -__builtin_huge_valf() && m < __builtin_huge_valf();
   }
-  float C = -__builtin_huge_valf();
-#pragma unroll
-  for (int k = 0; k < kMaxChunks * kPartsPerChunk / 64; ++k) C = fmaxf(C, q[k].c);
-  C = wave_max(C);
-  double S = 0.0;
-#pragma unroll
-  for (int k = 0; k < kMaxChunks * kPartsPerChunk / 64; ++k)
-    if (q[k].s > 0.0) S += q[k].s * exp2((double)q[k].c - (double)C);
-  S = wave_sum(S);
+  const float C = wave_max(q.c);
+  const double S = wave_sum(q.s > 0.0 ? scale_pow2(q.s, q.c - C) : 0.0);
   out->c = C;
   out->amax = 0;
   out->s = S;
   const bool finite_c = C > -__builtin_huge_valf() && C < __builtin_huge_valf();
   return finite_c && S > 0.0 && S < __builtin_huge_val();
+}
+
+__device__ __forceinline__ bool merge_row_wave(const Partial* __restrict__ p, int n_parts,
+                                               bool greedy, RowStats* out) {
+  return merge_parts_wave(lane_partial(p, n_parts), n_parts, greedy, out);
 }
 
 // Probability of token `tok` under a merged row, in float64.
@@ -310,26 +459,54 @@ struct StopDist {
   float q_k, q_c, q_inv_s;
 };
 
-// This thread's 8 contiguous weights of chunk `chunk` (zero past V and for
-// the bits set in `mask`).  The mass and select passes both call this.
+// This thread's 8 contiguous elements of one chunk of the stop row(s), as
+// loaded (vector path).
 template <int DT>
-__device__ __forceinline__ void stop_weights(const StopDist& d, int V, int chunk, int vec_ok,
-                                             uint32_t mask, float w[kPerThread]) {
-  constexpr int ES = DT ? 2 : 4;
-  constexpr int EPV = 16 / ES;
+struct StopVec {
+  static constexpr int ES = DT ? 2 : 4;
+  static constexpr int EPV = 16 / ES;
+  static constexpr int NV = kPerThread / EPV;
+  uint4 p[NV], q[NV];
+};
+
+template <int DT>
+__device__ __forceinline__ bool stop_vec_path(int V, int chunk, int vec_ok) {
+  return vec_ok && chunk * kChunk + (int)threadIdx.x * kPerThread + kPerThread <= V;
+}
+
+// Issue this thread's loads of chunk `chunk` (vector path only; the scalar
+// path loads inside stop_weights_from).
+template <int DT>
+__device__ __forceinline__ void stop_load(const StopDist& d, int V, int chunk, int vec_ok,
+                                          StopVec<DT>& r) {
+  constexpr int ES = StopVec<DT>::ES;
+  if (!stop_vec_path<DT>(V, chunk, vec_ok)) return;
+  const int e0 = chunk * kChunk + threadIdx.x * kPerThread;
+  const bool need_q = d.residual && !d.q_greedy;
+  const uint4* pp = (const uint4*)((const char*)d.prow + (long long)e0 * ES);
+  const uint4* qp = (const uint4*)((const char*)d.qrow + (long long)e0 * ES);
+#pragma unroll
+  for (int j = 0; j < StopVec<DT>::NV; ++j) {
+    r.p[j] = pp[j];
+    r.q[j] = need_q ? qp[j] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// This thread's 8 contiguous weights of chunk `chunk` (zero past V and for
+// the bits set in `mask`).  Every pass derives weights through this code.
+template <int DT>
+__device__ __forceinline__ void stop_weights_from(const StopDist& d, int V, int chunk, int vec_ok,
+                                                  uint32_t mask, const StopVec<DT>& r,
+                                                  float w[kPerThread]) {
+  constexpr int EPV = StopVec<DT>::EPV;
   const int e0 = chunk * kChunk + threadIdx.x * kPerThread;
   float xp[kPerThread], xq[kPerThread];
   const bool need_q = d.residual && !d.q_greedy;
-  if (vec_ok && e0 + kPerThread <= V) {
-    const uint4* pp = (const uint4*)((const char*)d.prow + (long long)e0 * ES);
-    const uint4* qp = (const uint4*)((const char*)d.qrow + (long long)e0 * ES);
+  if (stop_vec_path<DT>(V, chunk, vec_ok)) {
 #pragma unroll
-    for (int j = 0; j < kPerThread / EPV; ++j) {
-      const uint4 r = pp[j];
-      uint4 s = make_uint4(0, 0, 0, 0);
-      if (need_q) s = qp[j];
-      const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-      const uint32_t sw[4] = {s.x, s.y, s.z, s.w};
+    for (int j = 0; j < StopVec<DT>::NV; ++j) {
+      const uint32_t rw[4] = {r.p[j].x, r.p[j].y, r.p[j].z, r.p[j].w};
+      const uint32_t sw[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         if (DT == 1) {
@@ -338,8 +515,8 @@ __device__ __forceinline__ void stop_weights(const StopDist& d, int V, int chunk
           xq[j * 8 + 2 * h] = bf16_lo(sw[h]);
           xq[j * 8 + 2 * h + 1] = bf16_hi(sw[h]);
         } else {
-          xp[j * 4 + h] = __uint_as_float(rw[h]);
-          xq[j * 4 + h] = __uint_as_float(sw[h]);
+          xp[j * EPV + h] = __uint_as_float(rw[h]);
+          xq[j * EPV + h] = __uint_as_float(sw[h]);
         }
       }
     }
@@ -366,6 +543,14 @@ __device__ __forceinline__ void stop_weights(const StopDist& d, int V, int chunk
 }
 
 template <int DT>
+__device__ __forceinline__ void stop_weights(const StopDist& d, int V, int chunk, int vec_ok,
+                                             uint32_t mask, float w[kPerThread]) {
+  StopVec<DT> r;
+  stop_load<DT>(d, V, chunk, vec_ok, r);
+  stop_weights_from<DT>(d, V, chunk, vec_ok, mask, r, w);
+}
+
+template <int DT>
 __device__ double chunk_mass(const StopDist& d, int V, int chunk, int vec_ok, uint32_t mask,
                              double* s_scan) {
   float w[kPerThread];
@@ -386,8 +571,8 @@ __device__ __forceinline__ void block_first_last(int found, int lastp, int* s_fo
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const unsigned long long fm = __ballot(found != 0x7fffffff);
   const unsigned long long lm = __ballot(lastp >= 0);
-  const int wf = fm ? __shfl(found, __ffsll((long long)fm) - 1, 64) : 0x7fffffff;
-  const int wl = lm ? __shfl(lastp, 63 - __clzll((long long)lm), 64) : -1;
+  const int wf = fm ? __builtin_amdgcn_readlane(found, __ffsll((long long)fm) - 1) : 0x7fffffff;
+  const int wl = lm ? __builtin_amdgcn_readlane(lastp, 63 - __clzll((long long)lm)) : -1;
   if (lane == 0) {
     s_found[wave] = wf;
     s_last[wave] = wl;
@@ -446,15 +631,14 @@ __device__ void choose_chunk(const double* s_mass, int n_chunks, double u, int* 
     const int lane = threadIdx.x;
     const double m = lane < n_chunks ? s_mass[lane] : 0.0;
     const double incl = wave_inclusive_scan(m);
-    const double R = __shfl(incl, 63, 64);
+    const double R = readlane_f64(incl, 63);
     const double t = u * R;
-    double excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0;
+    const double excl = wave_shift_up1(incl);
     const unsigned long long hit = __ballot(lane < n_chunks && m > 0.0 && incl > t);
     const unsigned long long pos = __ballot(lane < n_chunks && m > 0.0);
     // rounding left u * R uncrossed: the last chunk with mass
     const int jc = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-    const double base = __shfl(excl, jc, 64);
+    const double base = readlane_f64(excl, jc);
     if (lane == 0) {
       *s_jc = jc;
       *s_base = base;
@@ -474,6 +658,7 @@ struct LinShared {
   RowStats rows[2 * kMaxGamma + 1];
   double p[kMaxGamma], q[kMaxGamma];
   int tok[kMaxGamma];
+  int rowok[2 * kMaxGamma + 1];
   int flags, nacc;
 };
 
@@ -507,43 +692,44 @@ __device__ LinRecord linear_decide(const LinearArgs& a, int b, bool write_output
   const float kt = gt ? 0.0f : log2e_over_t(Tt);
   const float kd = gd ? 0.0f : log2e_over_t(Td);
 
-  if (tid == 0) sh.flags = 0;
+  // Wave 0 fetches the drafts and the two logits at each; meanwhile every
+  // wave merges logit rows (target rows 0..g, then draft rows 0..g-1).
   int tok = 0;
+  float x = 0.0f, y = 0.0f;
   if (tid < g) {
     tok = a.tokens[o0 + tid];
-    sh.tok[tid] = tok;
+    const int tk = (tok >= 0 && tok < V) ? tok : 0;
+    x = load_logit<DT>(a.target, (tr0 + tid) * (long long)V + tk);
+    y = load_logit<DT>(a.draft, ((long long)o0 + tid) * V + tk);
   }
-  __syncthreads();
-  const int nr = 2 * g + 1;  // target rows 0..g, then draft rows 0..g-1
+  const int nr = 2 * g + 1;
   for (int rr = wave; rr < nr; rr += kFinWaves) {
     const bool is_t = rr <= g;
     const long long row = is_t ? tr0 + rr : a.n_target_rows + o0 + (rr - g - 1);
     RowStats rs;
     const bool ok = merge_row_wave(a.part + row * n_parts, n_parts, is_t ? gt : gd, &rs);
     if (lane == 0) {
-      if (!ok) atomicOr(&sh.flags, kRowNonFinite);
       sh.rows[rr] = rs;
+      sh.rowok[rr] = ok;
     }
   }
   __syncthreads();
 
   if (tid < 64) {
     const int i = tid;
-    bool reject = false;
+    bool reject = false, badtok = false, qzero = false, bad_row = false;
+    for (int rr = i; rr < nr; rr += 64) bad_row |= !sh.rowok[rr];
     if (i < g) {
-      if (tok < 0 || tok >= V) {
-        atomicOr(&sh.flags, kRowBadToken);
-        tok = 0;
-      }
-      const float x = load_logit<DT>(a.target, (tr0 + i) * (long long)V + tok);
-      const float y = load_logit<DT>(a.draft, ((long long)o0 + i) * V + tok);
-      const double p = row_prob(sh.rows[i], gt, kt, x, tok);
-      const double q = row_prob(sh.rows[g + 1 + i], gd, kd, y, tok);
+      sh.tok[i] = tok;
+      badtok = tok < 0 || tok >= V;
+      const int tk = badtok ? 0 : tok;
+      const double p = row_prob(sh.rows[i], gt, kt, x, tk);
+      const double q = row_prob(sh.rows[g + 1 + i], gd, kd, y, tk);
       double rt;
       if (q > 0.0) {
         rt = p / q;
       } else {
-        atomicOr(&sh.flags, kRowWarnQZero);
+        qzero = true;
         rt = p > 0.0 ? __builtin_huge_val() : 0.0;
       }
       const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
@@ -553,7 +739,12 @@ __device__ LinRecord linear_decide(const LinearArgs& a, int b, bool write_output
       sh.q[i] = q;
     }
     const unsigned long long rej = __ballot(reject);
-    if (tid == 0) sh.nacc = rej ? (__ffsll((long long)rej) - 1) : g;
+    const int flags = (__ballot(bad_row) ? kRowNonFinite : 0) | (__ballot(badtok) ? kRowBadToken : 0) |
+                      (__ballot(qzero) ? kRowWarnQZero : 0);
+    if (tid == 0) {
+      sh.nacc = rej ? (__ffsll((long long)rej) - 1) : g;
+      sh.flags = flags;
+    }
   }
   __syncthreads();
   const int flags = sh.flags;
@@ -636,19 +827,49 @@ struct RowWeights {
   double excl[4];
 };
 
+// All chunks' loads go out before any weight is formed; one block scan then
+// serves the four chunks (the same wave scan and wave-total order as
+// block_exclusive_scan, per chunk).
 template <int DT>
 __device__ __forceinline__ void row_weights(const StopDist& d, int V, int n_chunks, int vec_ok,
                                             RowWeights& rw, double* s_scan, double* s_mass) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  StopVec<DT> sv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (c < n_chunks) stop_load<DT>(d, V, c, vec_ok, sv[c]);
+  double incl[4], excl_lane[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
+    double acc = 0.0;
     if (c < n_chunks) {
-      stop_weights<DT>(d, V, c, vec_ok, 0u, rw.w[c]);
-      double acc = 0.0;
+      stop_weights_from<DT>(d, V, c, vec_ok, 0u, sv[c], rw.w[c]);
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e) acc += (double)rw.w[c][e];
-      double total;
-      rw.excl[c] = block_exclusive_scan<kFinWaves>(acc, s_scan, &total);
-      if (threadIdx.x == 0) s_mass[c] = total;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) rw.w[c][e] = 0.0f;
+    }
+    incl[c] = wave_inclusive_scan(acc);
+    excl_lane[c] = wave_shift_up1(incl[c]);
+  }
+  __syncthreads();
+  if (lane == 63) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s_scan[c * kFinWaves + wave] = incl[c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const double* sc = s_scan + c * kFinWaves;
+    double base = 0.0;
+    for (int i = 0; i < wave; ++i) base += sc[i];
+    rw.excl[c] = base + excl_lane[c];
+    if (threadIdx.x == 0 && c < n_chunks) {
+      double t = sc[0];
+#pragma unroll
+      for (int i = 1; i < kFinWaves; ++i) t += sc[i];
+      s_mass[c] = t;
     }
   }
   __syncthreads();
@@ -657,7 +878,7 @@ __device__ __forceinline__ void row_weights(const StopDist& d, int V, int n_chun
 template <int DT>
 __global__ __launch_bounds__(kFinThreads) void linear_row_kernel(LinearArgs a) {
   __shared__ LinShared sh;
-  __shared__ double s_scan[kFinWaves];
+  __shared__ double s_scan[4 * kFinWaves];
   __shared__ double s_mass[kMaxChunks];
   __shared__ int s_found[kFinWaves], s_last[kFinWaves];
   __shared__ int s_jc;
@@ -775,9 +996,11 @@ __global__ __launch_bounds__(kFinThreads) void linear_select_kernel(LinearArgs a
 
 template <int DT>
 __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
+  constexpr int kNodesPerWave = kMaxNodes / kFinWaves;
   __shared__ RowStats s_rows[kMaxNodes];
-  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes];
-  __shared__ double s_pn[kMaxNodes], s_u[kMaxNodes];
+  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes], s_rowok[kMaxNodes];
+  __shared__ double s_pn[kMaxNodes];
+  __shared__ double s_cm[kMaxNodes * kMaxChunks];  // p's mass per (node, chunk)
   __shared__ int s_flags, s_stop, s_depth;
   __shared__ unsigned long long s_removed;   // node bits of the rejected siblings
   __shared__ double s_scan[kFinWaves];
@@ -794,37 +1017,63 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
   const int nn = a.n_nodes ? a.n_nodes[b] : N;
   const float T = a.temp[b];
   const long long rb = (long long)b * N;
+  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
 
-  if (tid == 0) s_flags = 0;
-  __syncthreads();
   int err0 = 0;
   if (nn < 1 || nn > N) err0 = kRowBadShape;
   else if (!temp_ok(T)) err0 = kRowBadTemp;
-  if (!err0 && tid < nn) {
-    int par = -1, tok = 0;
-    if (tid > 0) {
-      par = a.parents[rb + tid];
-      tok = a.tokens[rb + tid];
-      if (par < 0 || par >= tid) atomicOr(&s_flags, kRowBadShape);
-      if (tok < 0 || tok >= V) atomicOr(&s_flags, kRowBadToken);
-    }
-    s_par[tid] = par;
-    s_tok[tid] = tok;
-  }
   const bool greedy = T == 0.0f;
   const float k2 = (greedy || err0) ? 0.0f : log2e_over_t(T);
+
+  // Wave 0 (one lane per node) fetches the tree and the logit of each node's
+  // token under its parent; meanwhile every wave merges node rows, all of
+  // its rows' partials loaded before the first is reduced.
+  int par = -1, tok = 0;
+  float x = 0.0f;
+  bool badpar = false, badtok = false;
+  if (!err0 && tid > 0 && tid < nn) {
+    par = a.parents[rb + tid];
+    tok = a.tokens[rb + tid];
+    badpar = par < 0 || par >= tid;
+    badtok = tok < 0 || tok >= V;
+    x = load_logit<DT>(a.target, (rb + (badpar ? 0 : par)) * (long long)V + (badtok ? 0 : tok));
+  }
   if (!err0) {
-    for (int n = wave; n < nn; n += kFinWaves) {
-      RowStats rs;
-      const bool ok = merge_row_wave(a.part + (rb + n) * n_parts, n_parts, greedy, &rs);
-      if (lane == 0) {
-        if (!ok) atomicOr(&s_flags, kRowNonFinite);
-        s_rows[n] = rs;
+    Partial q[kNodesPerWave];
+#pragma unroll
+    for (int k = 0; k < kNodesPerWave; ++k) {
+      const int n = wave + k * kFinWaves;
+      q[k] = n < nn ? lane_partial(a.part + (rb + n) * n_parts, n_parts)
+                    : Partial{-__builtin_huge_valf(), 0x7fffffff, 0.0};
+    }
+#pragma unroll
+    for (int k = 0; k < kNodesPerWave; ++k) {
+      const int n = wave + k * kFinWaves;
+      if (n < nn) {
+        RowStats rs;
+        const bool ok = merge_parts_wave(q[k], n_parts, greedy, &rs);
+        if (lane == 0) {
+          s_rows[n] = rs;
+          s_rowok[n] = ok;
+        }
+        if (!greedy && lane < n_chunks)
+          s_cm[n * n_chunks + lane] = q[k].s > 0.0 ? scale_pow2(q[k].s, q[k].c - rs.c) / rs.s : 0.0;
       }
     }
   }
+  if (tid < kMaxNodes) {
+    s_par[tid] = par;
+    s_tok[tid] = tok;
+  }
   __syncthreads();
-  const int err = err0 | (s_flags & kRowErrorMask);
+  if (tid < 64) {
+    const int flags = (__ballot(badpar) ? kRowBadShape : 0) | (__ballot(badtok) ? kRowBadToken : 0) |
+                      (__ballot(tid < nn && !err0 && !s_rowok[tid < kMaxNodes ? tid : 0])
+                           ? kRowNonFinite : 0);
+    if (tid == 0) s_flags = err0 | flags;
+  }
+  __syncthreads();
+  const int err = s_flags & kRowErrorMask;
   if (err) {
     for (int i = tid; i < N; i += kFinThreads) {
       a.out_tokens[rb + i] = -1;
@@ -838,12 +1087,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
     return;
   }
 
-  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
+  double u_acc = 0.0;
   if (tid > 0 && tid < nn) {
-    const int par = s_par[tid], tok = s_tok[tid];
-    const float x = load_logit<DT>(a.target, (rb + par) * (long long)V + tok);
     s_pn[tid] = row_prob(s_rows[par], greedy, k2, x, tok);
-    s_u[tid] = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)tid).x);
+    u_acc = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)tid).x);
   }
   __syncthreads();
 
@@ -869,11 +1116,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
       }
       const double mass = (child && !dup) ? s_pn[i] : 0.0;
       const double incl = wave_inclusive_scan(mass);
-      double excl = __shfl_up(incl, 1, 64);
-      if (i == 0) excl = 0.0;
+      const double excl = wave_shift_up1(incl);
       const double denom = 1.0 - excl;
       const double ratio = (child && !dup && denom > 0.0) ? s_pn[i] / denom : 0.0;
-      const unsigned long long acc = __ballot(child && s_u[i] < ratio);
+      const unsigned long long acc = __ballot(child && u_acc < ratio);
       if (acc) {
         const int first = __ffsll((long long)acc) - 1;
         if (i == 0) s_path[depth] = first;
@@ -900,17 +1146,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
     token = s_rows[stop].amax;
   } else {
     const RowStats st = s_rows[stop];
-    const Partial* sp = a.part + (rb + stop) * n_parts;
-    // chunk masses of p at the stop node from its partials, minus the
-    // rejected siblings' probabilities
+    // chunk masses of p at the stop node, minus the rejected siblings'
+    // probabilities
     if (tid < n_chunks) {
-      double m = 0.0;
-#pragma unroll
-      for (int w = 0; w < kPartsPerChunk; ++w) {
-        const Partial q = sp[tid * kPartsPerChunk + w];
-        if (q.s > 0.0) m += q.s * exp2((double)q.c - (double)st.c);
-      }
-      m /= st.s;
+      double m = s_cm[stop * n_chunks + tid];
       unsigned long long rm = removed;
       const int lo = tid * kChunk, hi = lo + kChunk;
       double cut = 0.0;
@@ -931,15 +1170,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
       // every sibling's token took the whole mass (rounding only): draw from p
       warn |= kRowWarnRZero;
       masked = false;
-      if (tid < n_chunks) {
-        double m = 0.0;
-#pragma unroll
-        for (int w = 0; w < kPartsPerChunk; ++w) {
-          const Partial q = sp[tid * kPartsPerChunk + w];
-          if (q.s > 0.0) m += q.s * exp2((double)q.c - (double)st.c);
-        }
-        s_mass[tid] = m / st.s;
-      }
+      if (tid < n_chunks) s_mass[tid] = s_cm[stop * n_chunks + tid];
       __syncthreads();
     }
     StopDist d;
@@ -1001,38 +1232,50 @@ __global__ __launch_bounds__(kThreads) void philox_words_kernel(uint64_t seed, u
 
 // Chunks per stats work item: one while a single round of work items fills
 // the GPU (short critical path), two beyond (more loads in flight per item).
-int stats_chunks_per_item(long long n_rows, int n_chunks) {
-  return n_rows * n_chunks <= 2048 ? 1 : 2;
-}
-
 long long stats_items(long long n_rows, int n_chunks) {
-  const int cpw = stats_chunks_per_item(n_rows, n_chunks);
-  return n_rows * ((n_chunks + cpw - 1) / cpw);
+  return n_rows * n_chunks * kPartsPerChunk;
 }
 
-// With both events set, they are attached to the kernel's dispatch packet
-// (start and end of the kernel itself, as a profiler sees it).
+// Workgroups of the streaming pass that fit on the current device at once.
+static int stats_resident_blocks(int dtype) {
+  static std::atomic<int> cache[2][kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int c = cache[dtype][dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int n_cu = 0, occ = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 0;
+    const hipError_t e = dtype == 1
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, stats_kernel<1>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, stats_kernel<0>, kThreads, 0);
+    if (e != hipSuccess) occ = 0;
+    c = std::max(1, n_cu) * std::max(1, occ);
+    cache[dtype][dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+// Pass 1.  Launched with events, the events bracket the kernel's dispatch.
 hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_t ev_start,
                         hipEvent_t ev_stop) {
-  const long long n = stats_items(a.n_rows, a.n_chunks);
-  const int cpw = stats_chunks_per_item(a.n_rows, a.n_chunks);
-  const dim3 grid((unsigned)n), block(kThreads);
+  const long long segs = stats_items(a.n_rows, a.n_chunks);
+  if (segs <= 0) return hipSuccess;
+  const int dt = dtype == 1 ? 1 : 0;
+  const long long want = (segs + kWaves - 1) / kWaves;
+  const dim3 grid((unsigned)std::min<long long>(want, stats_resident_blocks(dt))), block(kThreads);
   const bool timed = ev_start && ev_stop;
-#define SV_LAUNCH_STATS(DT, CPW)                                                             \
-  do {                                                                                      \
-    if (timed)                                                                              \
-      hipExtLaunchKernelGGL(stats_kernel<DT, CPW>, grid, block, 0, st, ev_start, ev_stop, 0, a); \
-    else                                                                                    \
-      stats_kernel<DT, CPW><<<grid, block, 0, st>>>(a);                                     \
-  } while (0)
-  if (dtype == 1) {
-    if (cpw == 1) SV_LAUNCH_STATS(1, 1);
-    else SV_LAUNCH_STATS(1, 2);
+  if (dt == 1) {
+    if (timed)
+      hipExtLaunchKernelGGL(stats_kernel<1>, grid, block, 0, st, ev_start, ev_stop, 0, a);
+    else
+      stats_kernel<1><<<grid, block, 0, st>>>(a);
   } else {
-    if (cpw == 1) SV_LAUNCH_STATS(0, 1);
-    else SV_LAUNCH_STATS(0, 2);
+    if (timed)
+      hipExtLaunchKernelGGL(stats_kernel<0>, grid, block, 0, st, ev_start, ev_stop, 0, a);
+    else
+      stats_kernel<0><<<grid, block, 0, st>>>(a);
   }
-#undef SV_LAUNCH_STATS
   return hipGetLastError();
 }
 

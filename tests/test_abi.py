@@ -53,10 +53,10 @@ def test_version_and_status_strings(lib):
 def test_workspace_sizes(lib):
     n = lib.spec_verify_linear_workspace_size(32, 160, 32000, 1)
     assert n > 0 and n % 256 == 0
-    # partials (352 rows x 4 chunks x 16 B) + masses + counters
-    assert n >= 352 * 4 * 4 * 16 + 32 * 4 * 8
+    # partials (352 rows x 4 chunks x 16 B) + chunk masses (32 rows x 4 chunks x 8 B)
+    assert n >= 352 * 4 * 16 + 32 * 4 * 8
     assert lib.spec_verify_linear_workspace_size(-1, 0, 10, 1) == 0
-    assert lib.spec_verify_tree_workspace_size(64, 64, 32000, 1) >= 64 * 64 * 4 * 4 * 16
+    assert lib.spec_verify_tree_workspace_size(64, 64, 32000, 1) >= 64 * 64 * 4 * 16
 
 
 def _linear(lib, **kw):
