@@ -50,7 +50,24 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run device-to-device copies of this many MiB (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib, steps):
+    """Plain device copies of a known size, for scaling HBM byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(calibration="copy", bytes_read=n, bytes_written=n, copies=steps)),
+          flush=True)
 
 
 def copies_for(nbytes):
@@ -72,7 +89,7 @@ def cpu_baseline_linear(d, seconds):
     rows = 0
     t0 = time.perf_counter()
     b = 0
-    while time.perf_counter() - t0 < seconds and rows < 10 * B:
+    while time.perf_counter() - t0 < seconds:
         bb = b % B
         o0, o1 = int(off[bb]), int(off[bb + 1])
         t = o0 + bb
@@ -94,7 +111,7 @@ def cpu_baseline_tree(d, seconds):
     B = d["B"]
     t0 = time.perf_counter()
     rows = nodes = 0
-    while time.perf_counter() - t0 < seconds and rows < 10 * B:
+    while time.perf_counter() - t0 < seconds:
         b = rows % B
         oracle.verify_tree_topk(d["target"][b:b + 1], d["dtype"], d["parents"][b:b + 1],
                                 d["tokens"][b:b + 1], d["n_nodes"][b:b + 1],
@@ -126,13 +143,27 @@ def cpu_baseline_attn(q, k, v, L, parents, seconds):
                        "(BLAS matmul threads)" % (heads, dt))
 
 
-def load_traffic(path, workload):
+def load_traffic(path, workload, kernel_sig):
+    """HBM bytes per launch of the dominant kernel, from counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size); None when
+    absent or taken on a different build of the kernel."""
     try:
         with open(path) as f:
-            t = json.load(f)
-        return t.get(workload)
+            t = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
+    if not t or t.get("kernel_source_sha1") != kernel_sig:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def kernel_source_sig(wl):
+    """SHA-1 of the source file that holds the dominant kernel."""
+    import hashlib
+    name = "sv_attn.hip" if wl == "attn_tree" else "sv_logits.hip"
+    path = os.path.join(ROOT, "rejection_sampling_verify_04_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()
 
 
 def main():
@@ -141,6 +172,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib, args.steps)
+        return
     import torch
     import synth
     import rejection_sampling_verify_04_amd as sv
@@ -279,7 +313,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     achieved = alg_bytes / avg_kern_s / 1e9
-    traffic = load_traffic(args.traffic_json, wl)
+    traffic = load_traffic(args.traffic_json, wl, kernel_source_sig(wl))
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=traffic,

@@ -112,6 +112,10 @@ const char* spec_verify_status_string(int status);
  *   B, V           batch rows (>= 0; 0 is a no-op) and vocabulary size (>= 1).
  *   total_draft    draft_offsets[B] (host copy, sizes the launch).
  *   draft_offsets  [B + 1] int32, non-decreasing, draft_offsets[0] = 0.
+ *                  A row whose own offsets are out of range is flagged
+ *                  SV_ROW_BAD_SHAPE; when the offsets are not
+ *                  non-decreasing, the other rows' results are unspecified
+ *                  (the packed row -> batch row mapping is then ambiguous).
  *   draft_tokens   [total_draft] int32 draft token ids.
  *   temp_target, temp_draft  [B] float temperatures; 0 means greedy (a
  *                  one-hot at the first maximum, kwkr §4.3).

@@ -12,17 +12,19 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int n_chunks_for(int V) { return (V + sv::kChunk - 1) / sv::kChunk; }
 
-// Workspace: [partials | chunk masses | per-row decision records], each aligned.
+// Workspace: [partials | gathered logits | chunk wave totals | per-row
+// decision records], each aligned.  n_gath = logits gathered at draft tokens.
 struct Layout {
-  size_t part, mass, rec, total;
+  size_t part, gath, mass, rec, total;
 };
 
-Layout layout(long long n_rows, int B, int V, bool linear) {
+Layout layout(long long n_rows, int B, int V, long long n_gath, bool linear) {
   const int nc = n_chunks_for(V);
   Layout l;
   l.part = 0;
-  l.mass = align_up((size_t)n_rows * nc * sv::kPartsPerChunk * sizeof(sv::Partial));
-  l.rec = l.mass + (linear ? align_up((size_t)B * nc * sizeof(double)) : 0);
+  l.gath = align_up((size_t)n_rows * nc * sv::kPartsPerChunk * sizeof(sv::Partial));
+  l.mass = l.gath + align_up((size_t)n_gath * sizeof(float));
+  l.rec = l.mass + (linear ? align_up((size_t)B * nc * sv::kFinWaves * sizeof(double)) : 0);
   l.total = l.rec + (linear ? align_up((size_t)B * sizeof(sv::LinRecord)) : 0);
   if (l.total == 0) l.total = kAlign;
   return l;
@@ -64,7 +66,7 @@ const char* spec_verify_status_string(int status) {
 size_t spec_verify_linear_workspace_size(int B, int total_draft, int V, int dtype) {
   (void)dtype;
   if (B < 0 || total_draft < 0 || V < 1) return 0;
-  return layout(2LL * total_draft + B, B, V, true).total;
+  return layout(2LL * total_draft + B, B, V, 2LL * total_draft, true).total;
 }
 
 int spec_verify_linear(const void* target_logits, const void* draft_logits, int dtype, int B,
@@ -88,7 +90,7 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   const int nc = n_chunks_for(V);
   if (sv::stats_items(n_rows, nc) >= (1LL << 31) || (long long)B * nc >= (1LL << 31))
     return SV_ERR_INVALID_ARG;
-  const Layout l = layout(n_rows, B, V, true);
+  const Layout l = layout(n_rows, B, V, 2LL * total_draft, true);
   const int wst = check_workspace(workspace, workspace_bytes, l.total);
   if (wst != SV_OK) return wst;
 
@@ -113,6 +115,10 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   s.temp_b = temp_draft;
   s.part = (sv::Partial*)(ws + l.part);
   s.vec_ok = vec_ok;
+  s.tokens = draft_tokens;
+  s.parents = nullptr;
+  s.total_draft = total_draft;
+  s.gath = (float*)(ws + l.gath);
   if (launch_stats_timed(dtype, s, stream) != hipSuccess) return SV_ERR_HIP;
 
   sv::LinearArgs f{};
@@ -131,7 +137,8 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   f.step = step;
   f.row_ids = row_ids;
   f.part = s.part;
-  f.mass = (double*)(ws + l.mass);
+  f.gath = s.gath;
+  f.wsum = (double*)(ws + l.mass);
   f.rec = (sv::LinRecord*)(ws + l.rec);
   f.num_accepted = num_accepted;
   f.out_tokens = out_tokens;
@@ -146,7 +153,7 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
 size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype) {
   (void)dtype;
   if (B < 0 || N < 1 || V < 1) return 0;
-  return layout((long long)B * N, B, V, false).total;
+  return layout((long long)B * N, B, V, (long long)B * N, false).total;
 }
 
 int spec_verify_tree(const void* target_logits, const void* draft_logits, int dtype, int B,
@@ -170,7 +177,7 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
   const long long n_rows = (long long)B * N;
   const int nc = n_chunks_for(V);
   if (sv::stats_items(n_rows, nc) >= (1LL << 31)) return SV_ERR_INVALID_ARG;
-  const Layout l = layout(n_rows, B, V, false);
+  const Layout l = layout(n_rows, B, V, n_rows, false);
   const int wst = check_workspace(workspace, workspace_bytes, l.total);
   if (wst != SV_OK) return wst;
   const int es = dtype == SV_BF16 ? 2 : 4;
@@ -193,6 +200,10 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
   s.temp_b = temp_target;
   s.part = (sv::Partial*)(ws + l.part);
   s.vec_ok = vec_ok;
+  s.tokens = node_tokens;
+  s.parents = parents;
+  s.total_draft = 0;
+  s.gath = (float*)(ws + l.gath);
   if (launch_stats_timed(dtype, s, stream) != hipSuccess) return SV_ERR_HIP;
 
   sv::TreeArgs f{};
@@ -209,6 +220,7 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
   f.step = step;
   f.row_ids = row_ids;
   f.part = s.part;
+  f.gath = s.gath;
   f.num_accepted = num_accepted;
   f.path_nodes = path_nodes;
   f.out_tokens = out_tokens;

@@ -142,6 +142,7 @@ constexpr int kDppHalfMirror = 0x141; // lane i of 8 <- 7 - i
 constexpr int kDppMirror = 0x140;     // lane i of 16 <- 15 - i
 constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
 constexpr int kDppWaveShr1 = 0x138;   // lane i <- lane i - 1 across the wave
+constexpr int kDppWaveShl1 = 0x130;   // lane i <- lane i + 1 across the wave
 
 // Sum over the wave; every lane gets the same result.
 __device__ __forceinline__ double wave_sum(double v) {

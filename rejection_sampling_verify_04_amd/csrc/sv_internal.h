@@ -23,13 +23,21 @@ struct StatsArgs {
   const float* temp_b;   // temperature of rows_b rows
   Partial* part;         // [n_rows][n_chunks]
   int vec_ok;            // 16-byte vector loads are valid for every row
+  // Logits gathered at the draft tokens: linear, x_i[d_i] at [i] and y_i[d_i]
+  // at [total_draft + i]; tree, node n's token under its parent at [b N + n].
+  const int* tokens;
+  const int* parents;
+  int total_draft;
+  float* gath;
 };
 
 // Decision of one linear batch row, handed from the mass pass to the select pass.
 struct LinRecord {
   int kind, flags, n_acc, token;
   int o0, g, q_greedy, q_amax;
-  float p_c, p_inv_s, q_c, q_inv_s;
+  float u_smp;               // uniform of the stop draw
+  float p_k, p_c, p_inv_s;   // target: log2(e) / T, offset, 1 / sum
+  float q_k, q_c, q_inv_s;   // draft, at a rejection
 };
 
 struct LinearArgs {
@@ -44,7 +52,8 @@ struct LinearArgs {
   uint64_t seed, step;
   const uint32_t* row_ids;
   const Partial* part;
-  double* mass;          // [B][n_chunks]
+  const float* gath;     // logits at the draft tokens (target, then draft)
+  double* wsum;          // [B][n_chunks][16]: wave totals of each chunk's stop mass
   LinRecord* rec;        // [B]
   int* num_accepted;
   int* out_tokens;
@@ -64,6 +73,7 @@ struct TreeArgs {
   uint64_t seed, step;
   const uint32_t* row_ids;
   const Partial* part;
+  const float* gath;     // logit of each node's token under its parent
   int* num_accepted;
   int* path_nodes;
   int* out_tokens;

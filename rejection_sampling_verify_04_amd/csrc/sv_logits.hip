@@ -1,40 +1,30 @@
 // Vocabulary-wide verify kernels (linear and tree), gfx950.
 //
-// Linear verify, three launches per call:
+// Pass 1, stats_kernel: a resident grid in which each wave reduces whole
+// 8192-logit chunks of the logit rows (one HBM read of every logit, with
+// non-temporal 16-byte loads in flight ahead of the reduction) into one
+// Partial per (row, chunk): an integer log2 offset and a float64 sum of
+// exponentials for a sampled row, the maximum and its first index for a
+// greedy row.  Its first work items gather the logits at the draft tokens.
 //
-//   stats_kernel        one work item per (logit row, 1 or 2 chunks of 8192
-//                       elements); each wave reduces its own 2048 elements
-//                       with coalesced 16-byte loads into a Partial -- an
-//                       offset and a sum of exponentials for a sampled row,
-//                       the max and its first index for a greedy row.  This
-//                       pass reads every logit of the call exactly once and
-//                       is the HBM-bound part.
-//
-//   linear_mass_kernel  one 1024-thread work item per (batch row, chunk).
-//                       Every item merges the row's partials (one wave per
-//                       logit row), redoes the row's acceptance decisions
-//                       (identical arithmetic, so identical results in every
-//                       item) and computes the mass of the stop distribution
-//                       over its chunk: max(0, p - q) after a rejection, p
-//                       for the bonus token.  Item 0 stores the row's
-//                       decision and the accepted tokens.
-//
-//   linear_select_kernel one 1024-thread work item per batch row: picks the
-//                       chunk that holds u * R, recomputes that chunk's
-//                       weights with the same code as the mass pass and
-//                       returns the first index whose cumulative mass exceeds
-//                       u * R, in vocabulary order.
-//
-// Tree verify, two launches: the same stats_kernel, then tree_kernel (one
-// 1024-thread work item per tree): it walks the tree level by level with one
-// lane per sibling, takes the stop node's chunk masses from its partials
-// (minus the rejected siblings), and selects in one chunk.
+// Linear finish:
+//   V of one chunk    linear_row_kernel: one work item per batch row takes
+//                     the decision, forms the stop weights, scans and draws.
+//   V of 2..4 chunks  linear_decide_mass_kernel (one work item per (row,
+//                     chunk): decision, then the chunk's stop mass as 16 wave
+//                     totals), then linear_select_kernel.
+//   larger V          linear_decide_kernel (per row), linear_mass_kernel (a
+//                     resident, pipelined grid over (row, chunk)), then
+//                     linear_select_kernel (one wave per row: chunk from the
+//                     masses, wave from the wave totals, element from that
+//                     wave's 512 weights).
+// Tree finish, tree_kernel: one work item per tree walks it with one lane per
+// node and draws in one chunk of the stop row.
 //
 // Work items never wait for one another: a kernel boundary is the only
 // synchronisation, because device-scope fences and atomics are costly here.
-// The mass and select passes accumulate each thread's 8 contiguous weights
-// sequentially in float64 and combine threads with the same block scan, so
-// chunk totals and in-chunk cumulative sums agree bit for bit.
+// Every pass forms weights and their sums with the same code in the same
+// order, so chunk totals and in-chunk cumulative sums agree bit for bit.
 //
 // Sources: acceptance rule and first-reject stop (kwkr.cn/news/620872 §2.3,
 // §4.1, §4.3; cf-1.com/news/5632551 §2.2); residual and bonus draws
@@ -101,9 +91,9 @@ struct SegLoad {
   static constexpr int NV = kPerLane / EPV;      // loads per lane per segment
   uint4 raw[NV];
 
-  // Vectors past V read as -inf.  Rows are read once, so the loads carry the
-  // non-temporal hint.  With vectors valid (V a multiple of EPV) a vector is
-  // either wholly inside the row or wholly past it.
+  // Vectors past V read as -inf.  Rows are read once here, so the loads carry
+  // the non-temporal hint.  With vectors valid (V a multiple of EPV) a vector
+  // is either wholly inside the row or wholly past it.
   __device__ __forceinline__ void issue(const char* rowp, int V, int seg0) {
     const int lane = threadIdx.x & 63;
     constexpr uint32_t kNegInf = DT ? 0xff80ff80u : 0xff800000u;
@@ -111,7 +101,8 @@ struct SegLoad {
     for (int j = 0; j < NV; ++j) {
       const int e0 = seg0 + (j * 64 + lane) * EPV;
       if (e0 < V) {
-        const u32x4_t w = __builtin_nontemporal_load((const u32x4_t*)(rowp + (long long)e0 * ES));
+        const u32x4_t w =
+            __builtin_nontemporal_load((const u32x4_t*)(rowp + (long long)e0 * ES));
         raw[j] = make_uint4(w.x, w.y, w.z, w.w);
       } else {
         raw[j] = make_uint4(kNegInf, kNegInf, kNegInf, kNegInf);
@@ -177,9 +168,55 @@ __device__ __forceinline__ int wave_find_batch_row(const int* off, int B, long l
   return lo;
 }
 
+// Largest b in [0, B) with off[b] <= i, each lane for its own i (fixed
+// number of steps: ceil(log2(B))).
+__device__ __forceinline__ int lane_batch_row(const int* off, int B, long long i) {
+  int lo = 0;
+  for (int step = 1 << (31 - __builtin_clz(max(B, 1))); step > 0; step >>= 1)
+    if (lo + step < B && (long long)off[lo + step] <= i) lo += step;
+  return lo;
+}
+
 // s * 2^d for an integer-valued d <= 0 (exact; -inf and huge |d| give 0).
 __device__ __forceinline__ double scale_pow2(double s, float d) {
   return __builtin_ldexp(s, (int)fmaxf(d, -4096.0f));
+}
+
+// Work items of the stats launch that gather logits at draft tokens (one
+// item per thread): linear, total_draft items; tree, B * N.
+__host__ __device__ inline long long gather_items(const StatsArgs& a) {
+  return a.tree ? (long long)a.B * a.N : (long long)a.total_draft;
+}
+__host__ __device__ inline int gather_blocks(const StatsArgs& a) {
+  return (int)((gather_items(a) + kThreads - 1) / kThreads);
+}
+
+// gath[i] = logit of item i's token: linear, x_i[d_i] at [i] and y_i[d_i]
+// at [total_draft + i] (target row i + b for position i of batch row b,
+// draft row i); tree, node j's token under its parent row at [j].  Tokens
+// and parents outside their range read index 0 (the finish pass flags them).
+template <int DT>
+__device__ void gather_logits(const StatsArgs& a, int* s_off) {
+  const long long n = gather_items(a);
+  const long long it = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const int V = a.V;
+  const bool cache = !a.tree && a.B <= kStatsCache;
+  if (cache) {
+    for (int i = threadIdx.x; i <= a.B; i += kThreads) s_off[i] = a.offsets[i];
+    __syncthreads();
+  }
+  if (it >= n) return;
+  const int tok = a.tokens[it];
+  const int tc = (tok >= 0 && tok < V) ? tok : 0;
+  if (a.tree) {
+    const int par = a.parents[it];
+    const long long xr = it - it % a.N + ((par >= 0 && par < a.N) ? par : 0);
+    a.gath[it] = load_logit<DT>(a.rows_a, xr * V + tc);
+  } else {
+    const int b = cache ? lane_batch_row(s_off, a.B, it) : lane_batch_row(a.offsets, a.B, it);
+    a.gath[it] = load_logit<DT>(a.rows_a, (it + b) * V + tc);
+    a.gath[n + it] = load_logit<DT>(a.rows_b, it * V + tc);
+  }
 }
 
 // A lane's running statistics over its elements of one chunk.
@@ -244,18 +281,27 @@ __device__ __forceinline__ Partial wave_combine(const LaneStats& st, bool greedy
   return Partial{C, 0, wave_sum(t)};
 }
 
-template <int DT>
+// RING = sub-segments in flight per wave: 2 for streaming many chunks per
+// wave, 4 (a whole chunk) when every wave has about one chunk.
+template <int DT, int RING>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
-  constexpr int RING = 2;               // sub-segments in flight per wave
   __shared__ int s_i[kStatsCache + 1];
   __shared__ float s_f0[kStatsCache], s_f1[kStatsCache];
 
+  const int V = a.V;
+  // The first work items gather the logits at the draft tokens; being
+  // dispatched first, they finish while the rest stream the vocabulary.
+  const int n_gblk = gather_blocks(a);
+  if ((int)blockIdx.x < n_gblk) {
+    gather_logits<DT>(a, s_i);
+    return;
+  }
+  const int blk = blockIdx.x - n_gblk;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int V = a.V;
   const uint32_t nc = (uint32_t)a.n_chunks;
   const uint32_t total = (uint32_t)a.n_rows * nc;   // < 2^31 (checked by the host)
-  const uint32_t G = gridDim.x * kWaves;
+  const uint32_t G = (gridDim.x - n_gblk) * kWaves;
   const uint32_t Gq = G / nc, Gr = G - Gq * nc;
   const long long rowbytes = (long long)V * SegLoad<DT>::ES;
   auto row_ptr = [&](uint32_t r) -> const char* {
@@ -263,8 +309,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
                      : (const char*)a.rows_b + ((long long)r - a.n_a) * rowbytes;
   };
 
-  uint32_t u = blockIdx.x * kWaves + wave;
+  uint32_t u = blk * kWaves + wave;
   uint32_t row = u / nc, ch = u - row * nc;
+
   SegLoad<DT> ring[RING];
   // The first chunk's loads go out before anything else; an unused tree
   // row is still allocated, so reading it is harmless.
@@ -402,37 +449,50 @@ struct RowStats {
   float c;     // log2 offset (sampled) or max logit (greedy)
   int amax;    // first argmax (greedy)
   double s;    // sum of 2^(x k - c) (sampled)
+  double inv_s;  // 1 / s
 };
 
 static_assert(kMaxChunks * kPartsPerChunk <= 64, "one partial per lane");
 
 // This lane's partial of a row (lane j holds partial j), or an empty one.
+// Every lane loads (from a clamped index), so that no load sits behind a
+// branch: a load whose value crosses a branch join is waited for there.
+// Lanes >= n_parts read partial 0; the merge ignores them.
 __device__ __forceinline__ Partial lane_partial(const Partial* __restrict__ p, int n_parts) {
   const int lane = threadIdx.x & 63;
-  return lane < n_parts ? p[lane] : Partial{-__builtin_huge_valf(), 0x7fffffff, 0.0};
+  return p[lane < n_parts ? lane : 0];
 }
 
-// Merge one row's partials, loaded one per lane, with one wave; returns false
-// when the row has no finite maximum.
-__device__ bool merge_parts_wave(const Partial& q, int n_parts, bool greedy, RowStats* out) {
+// Merge one row's partials, loaded one per lane (lanes >= n_parts ignored),
+// with one wave; returns false when the row has no finite maximum.  Both the
+// greedy and the sampled merge are formed and one is selected, so that every
+// field of the loaded partial is used on one path and its load stays whole
+// and ahead of any branch.
+__device__ bool merge_parts_wave(const Partial& q_in, int n_parts, bool greedy, RowStats* out) {
   const int lane = threadIdx.x & 63;
+  const bool valid = lane < n_parts;
+  const float qc = valid ? q_in.c : -__builtin_huge_valf();
+  const double qs = valid ? q_in.s : 0.0;
+  // greedy: largest value, lowest index on ties
+  const unsigned long long key =
+      valid ? ((unsigned long long)float_order_key(q_in.c) << 32) | (0xffffffffu - (uint32_t)q_in.amax)
+            : 0ull;
+  const unsigned long long best = wave_max_u64(key);
+  const float gm = float_from_order_key((uint32_t)(best >> 32));
+  // sampled: common integer offset, exact rescale of each chunk sum
+  const float C = wave_max(qc);
+  const double S = wave_sum(qs > 0.0 ? scale_pow2(qs, qc - C) : 0.0);
   if (greedy) {
-    const unsigned long long key =
-        lane < n_parts ? ((unsigned long long)float_order_key(q.c) << 32) |
-                             (0xffffffffu - (uint32_t)q.amax)
-                       : 0ull;
-    const unsigned long long best = wave_max_u64(key);
-    const float m = float_from_order_key((uint32_t)(best >> 32));
-    out->c = m;
+    out->c = gm;
     out->amax = (int)(0xffffffffu - (uint32_t)best);
     out->s = 0.0;
-    return m > -__builtin_huge_valf() && m < __builtin_huge_valf();
+    out->inv_s = 0.0;
+    return gm > -__builtin_huge_valf() && gm < __builtin_huge_valf();
   }
-  const float C = wave_max(q.c);
-  const double S = wave_sum(q.s > 0.0 ? scale_pow2(q.s, q.c - C) : 0.0);
   out->c = C;
   out->amax = 0;
   out->s = S;
+  out->inv_s = 1.0 / S;
   const bool finite_c = C > -__builtin_huge_valf() && C < __builtin_huge_valf();
   return finite_c && S > 0.0 && S < __builtin_huge_val();
 }
@@ -442,11 +502,20 @@ __device__ __forceinline__ bool merge_row_wave(const Partial* __restrict__ p, in
   return merge_parts_wave(lane_partial(p, n_parts), n_parts, greedy, out);
 }
 
-// Probability of token `tok` under a merged row, in float64.
+// 2^e for a float64 e: the integer part exactly (ldexp), the fraction in
+// [-1/2, 1/2] through the hardware 2^x (about 1e-7 relative).
+__device__ __forceinline__ double exp2_split(double e) {
+  const double n = __builtin_rint(e);
+  const float f = (float)(e - n);
+  return __builtin_ldexp((double)exp2_hw(f), (int)fmax(fmin(n, 2000.0), -2000.0));
+}
+
+// Probability of token `tok` under a merged row (exponent formed exactly in
+// float64: x k is exact there and the offset is an integer).
 __device__ __forceinline__ double row_prob(const RowStats& r, bool greedy, float k2, float x,
                                            int tok) {
   if (greedy) return tok == r.amax ? 1.0 : 0.0;
-  return exp2((double)x * (double)k2 - (double)r.c) / r.s;
+  return exp2_split((double)x * (double)k2 - (double)r.c) * r.inv_s;
 }
 
 // The stop distribution's unnormalised weights for one row.
@@ -459,6 +528,21 @@ struct StopDist {
   float q_k, q_c, q_inv_s;
 };
 
+// A thread's total of its 8 weights: pairwise in float32, once to float64.
+// Every pass forms thread totals through this code.
+__device__ __forceinline__ double thread_total(const float w[kPerThread]) {
+  static_assert((kPerThread & (kPerThread - 1)) == 0, "pairwise tree");
+  float t[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) t[e] = w[e];
+#pragma unroll
+  for (int h = kPerThread / 2; h >= 1; h >>= 1) {
+#pragma unroll
+    for (int e = 0; e < h; ++e) t[e] = t[2 * e] + t[2 * e + 1];
+  }
+  return (double)t[0];
+}
+
 // This thread's 8 contiguous elements of one chunk of the stop row(s), as
 // loaded (vector path).
 template <int DT>
@@ -469,40 +553,39 @@ struct StopVec {
   uint4 p[NV], q[NV];
 };
 
+// Issue this thread's loads of chunk `chunk` (vector path: V a multiple of
+// the vector width, so each vector lies wholly inside or wholly past the
+// row).  Vectors past V, and the draft row when it is not needed, load from
+// a valid address whose values are never used; nothing sits behind a branch.
 template <int DT>
-__device__ __forceinline__ bool stop_vec_path(int V, int chunk, int vec_ok) {
-  return vec_ok && chunk * kChunk + (int)threadIdx.x * kPerThread + kPerThread <= V;
-}
-
-// Issue this thread's loads of chunk `chunk` (vector path only; the scalar
-// path loads inside stop_weights_from).
-template <int DT>
-__device__ __forceinline__ void stop_load(const StopDist& d, int V, int chunk, int vec_ok,
-                                          StopVec<DT>& r) {
-  constexpr int ES = StopVec<DT>::ES;
-  if (!stop_vec_path<DT>(V, chunk, vec_ok)) return;
-  const int e0 = chunk * kChunk + threadIdx.x * kPerThread;
+__device__ __forceinline__ void stop_load(const StopDist& d, int V, int chunk, StopVec<DT>& r,
+                                          int tix = threadIdx.x) {
+  constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV;
+  const int e0 = chunk * kChunk + tix * kPerThread;
   const bool need_q = d.residual && !d.q_greedy;
-  const uint4* pp = (const uint4*)((const char*)d.prow + (long long)e0 * ES);
-  const uint4* qp = (const uint4*)((const char*)d.qrow + (long long)e0 * ES);
+  const char* prow = (const char*)d.prow;
+  const char* qrow = need_q ? (const char*)d.qrow : prow;
 #pragma unroll
   for (int j = 0; j < StopVec<DT>::NV; ++j) {
-    r.p[j] = pp[j];
-    r.q[j] = need_q ? qp[j] : make_uint4(0, 0, 0, 0);
+    const int ej = e0 + j * EPV;
+    const long long off = ej < V ? (long long)ej * ES : 0;
+    r.p[j] = *(const uint4*)(prow + off);
+    r.q[j] = *(const uint4*)(qrow + off);
   }
 }
 
-// This thread's 8 contiguous weights of chunk `chunk` (zero past V and for
-// the bits set in `mask`).  Every pass derives weights through this code.
+// The 8 contiguous weights of thread `tix` (of 1024) in chunk `chunk` (zero
+// past V and for the bits set in `mask`).  Every pass derives weights
+// through this code.
 template <int DT>
 __device__ __forceinline__ void stop_weights_from(const StopDist& d, int V, int chunk, int vec_ok,
                                                   uint32_t mask, const StopVec<DT>& r,
-                                                  float w[kPerThread]) {
+                                                  float w[kPerThread], int tix = threadIdx.x) {
   constexpr int EPV = StopVec<DT>::EPV;
-  const int e0 = chunk * kChunk + threadIdx.x * kPerThread;
+  const int e0 = chunk * kChunk + tix * kPerThread;
   float xp[kPerThread], xq[kPerThread];
   const bool need_q = d.residual && !d.q_greedy;
-  if (stop_vec_path<DT>(V, chunk, vec_ok)) {
+  if (vec_ok) {
 #pragma unroll
     for (int j = 0; j < StopVec<DT>::NV; ++j) {
       const uint32_t rw[4] = {r.p[j].x, r.p[j].y, r.p[j].z, r.p[j].w};
@@ -528,6 +611,8 @@ __device__ __forceinline__ void stop_weights_from(const StopDist& d, int V, int 
       xq[e] = (need_q && idx < V) ? load_logit<DT>(d.qrow, idx) : 0.0f;
     }
   }
+  // per-element range and mask tests only where they can matter
+  const bool plain = mask == 0u && e0 + kPerThread <= V;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const int idx = e0 + e;
@@ -537,7 +622,7 @@ __device__ __forceinline__ void stop_weights_from(const StopDist& d, int V, int 
                                  : exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
       p = fmaxf(p - q, 0.0f);
     }
-    if (idx >= V || ((mask >> e) & 1u)) p = 0.0f;
+    if (!plain && (idx >= V || ((mask >> e) & 1u))) p = 0.0f;
     w[e] = p;
   }
 }
@@ -546,7 +631,7 @@ template <int DT>
 __device__ __forceinline__ void stop_weights(const StopDist& d, int V, int chunk, int vec_ok,
                                              uint32_t mask, float w[kPerThread]) {
   StopVec<DT> r;
-  stop_load<DT>(d, V, chunk, vec_ok, r);
+  if (vec_ok) stop_load<DT>(d, V, chunk, r);
   stop_weights_from<DT>(d, V, chunk, vec_ok, mask, r, w);
 }
 
@@ -555,9 +640,7 @@ __device__ double chunk_mass(const StopDist& d, int V, int chunk, int vec_ok, ui
                              double* s_scan) {
   float w[kPerThread];
   stop_weights<DT>(d, V, chunk, vec_ok, mask, w);
-  double acc = 0.0;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) acc += (double)w[e];
+  const double acc = thread_total(w);
   double total;
   block_exclusive_scan<kFinWaves>(acc, s_scan, &total);
   return total;
@@ -615,9 +698,7 @@ __device__ int chunk_select(const StopDist& d, int V, int chunk, int vec_ok, uin
                             int* s_last) {
   float w[kPerThread];
   stop_weights<DT>(d, V, chunk, vec_ok, mask, w);
-  double acc = 0.0;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) acc += (double)w[e];
+  const double acc = thread_total(w);
   double total;
   const double excl = block_exclusive_scan<kFinWaves>(acc, s_scan, &total);
   return find_in_chunk(w, chunk, base, excl, target, s_found, s_last);
@@ -654,12 +735,15 @@ __device__ void choose_chunk(const double* s_mass, int n_chunks, double u, int* 
 constexpr int kKindReject = 0, kKindBonus = 1, kKindGreedy = 2, kKindError = 3,
               kKindBadShape = 4;
 
+constexpr int kDecideRowsPerWave = 2;   // logit rows each wave merges up front (2 g + 1 <= 32)
+
 struct LinShared {
   RowStats rows[2 * kMaxGamma + 1];
   double p[kMaxGamma], q[kMaxGamma];
   int tok[kMaxGamma];
   int rowok[2 * kMaxGamma + 1];
   int flags, nacc;
+  float usmp;
 };
 
 // Merge row b's partials (one wave per logit row), test its drafts and fill a
@@ -692,22 +776,43 @@ __device__ LinRecord linear_decide(const LinearArgs& a, int b, bool write_output
   const float kt = gt ? 0.0f : log2e_over_t(Tt);
   const float kd = gd ? 0.0f : log2e_over_t(Td);
 
-  // Wave 0 fetches the drafts and the two logits at each; meanwhile every
-  // wave merges logit rows (target rows 0..g, then draft rows 0..g-1).
-  int tok = 0;
-  float x = 0.0f, y = 0.0f;
-  if (tid < g) {
-    tok = a.tokens[o0 + tid];
-    const int tk = (tok >= 0 && tok < V) ? tok : 0;
-    x = load_logit<DT>(a.target, (tr0 + tid) * (long long)V + tk);
-    y = load_logit<DT>(a.draft, ((long long)o0 + tid) * V + tk);
-  }
+  // Every wave loads the partials of its logit rows (target rows 0..g, then
+  // draft rows 0..g-1) first, then the draft token of its lane's position
+  // and the two logits at it; only wave 0's lanes < g keep the latter.  All
+  // addresses are clamped to valid ones, so every lane loads unconditionally.
   const int nr = 2 * g + 1;
-  for (int rr = wave; rr < nr; rr += kFinWaves) {
-    const bool is_t = rr <= g;
-    const long long row = is_t ? tr0 + rr : a.n_target_rows + o0 + (rr - g - 1);
+  auto row_of = [&](int rr) -> long long {
+    return rr <= g ? tr0 + rr : a.n_target_rows + o0 + (rr - g - 1);
+  };
+  // rows wave + 4 k (k < kDecideRowsPerWave), clamped into [0, nr): loaded
+  // and merged unconditionally
+  Partial q[kDecideRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kDecideRowsPerWave; ++k)
+    q[k] = lane_partial(a.part + row_of(min(wave + k * kFinWaves, nr - 1)) * n_parts, n_parts);
+  // lane l's Philox block of slot l, formed while the loads are in flight
+  // (wave 0 uses it: word 0 tests d_{l-1}, word 1 is the draw at stop l)
+  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
+  const uint4 wl = verify_words(a.seed, a.step, rid, (uint32_t)lane);
+  // the draft tokens and the logits at them (gathered by the vocabulary pass)
+  const int li = min(lane, g > 0 ? g - 1 : 0);
+  const int tok = *(g > 0 ? a.tokens + o0 + li : a.off);
+  const float x = g > 0 ? a.gath[o0 + li] : 0.0f;
+  const float y = g > 0 ? a.gath[a.total_draft + o0 + li] : 0.0f;
+#pragma unroll
+  for (int k = 0; k < kDecideRowsPerWave; ++k) {
+    const int rr = min(wave + k * kFinWaves, nr - 1);
     RowStats rs;
-    const bool ok = merge_row_wave(a.part + row * n_parts, n_parts, is_t ? gt : gd, &rs);
+    const bool ok = merge_parts_wave(q[k], n_parts, rr <= g ? gt : gd, &rs);
+    if (lane == 0 && wave + k * kFinWaves < nr) {
+      sh.rows[rr] = rs;
+      sh.rowok[rr] = ok;
+    }
+  }
+  // long draft runs (2g + 1 > 32 rows): the rest, one row per round
+  for (int rr = wave + kDecideRowsPerWave * kFinWaves; rr < nr; rr += kFinWaves) {
+    RowStats rs;
+    const bool ok = merge_row_wave(a.part + row_of(rr) * n_parts, n_parts, rr <= g ? gt : gd, &rs);
     if (lane == 0) {
       sh.rows[rr] = rs;
       sh.rowok[rr] = ok;
@@ -719,31 +824,33 @@ __device__ LinRecord linear_decide(const LinearArgs& a, int b, bool write_output
     const int i = tid;
     bool reject = false, badtok = false, qzero = false, bad_row = false;
     for (int rr = i; rr < nr; rr += 64) bad_row |= !sh.rowok[rr];
+    // slot 64 (g = 64 only) separately
+    uint32_t acc_word = dpp_u32<kDppWaveShl1>(wl.x);   // lane i <- lane i + 1
+    if (g == kMaxGamma && i == 63) acc_word = verify_words(a.seed, a.step, rid, 64u).x;
     if (i < g) {
       sh.tok[i] = tok;
       badtok = tok < 0 || tok >= V;
       const int tk = badtok ? 0 : tok;
       const double p = row_prob(sh.rows[i], gt, kt, x, tk);
       const double q = row_prob(sh.rows[g + 1 + i], gd, kd, y, tk);
-      double rt;
-      if (q > 0.0) {
-        rt = p / q;
-      } else {
-        qzero = true;
-        rt = p > 0.0 ? __builtin_huge_val() : 0.0;
-      }
-      const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
-      const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)(i + 1)).x);
-      reject = !(u < rt);
+      qzero = !(q > 0.0);
+      // u < min(1, p / q), written without the division (u < 1; q = 0
+      // accepts iff p > 0; p = 0 always rejects)
+      const double u = word_to_uniform(acc_word);
+      reject = !(u * q < p);
       sh.p[i] = p;
       sh.q[i] = q;
     }
     const unsigned long long rej = __ballot(reject);
     const int flags = (__ballot(bad_row) ? kRowNonFinite : 0) | (__ballot(badtok) ? kRowBadToken : 0) |
                       (__ballot(qzero) ? kRowWarnQZero : 0);
+    const int nacc = rej ? (__ffsll((long long)rej) - 1) : g;
+    const uint32_t smp_word = nacc < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)wl.y, nacc)
+                                        : verify_words(a.seed, a.step, rid, 64u).y;
     if (tid == 0) {
-      sh.nacc = rej ? (__ffsll((long long)rej) - 1) : g;
+      sh.nacc = nacc;
       sh.flags = flags;
+      sh.usmp = (float)word_to_uniform(smp_word);
     }
   }
   __syncthreads();
@@ -772,36 +879,38 @@ __device__ LinRecord linear_decide(const LinearArgs& a, int b, bool write_output
     r.token = sh.rows[n_acc].amax;
     return r;
   }
+  r.u_smp = sh.usmp;
   const bool residual = n_acc < g;
   r.kind = residual ? kKindReject : kKindBonus;
+  r.p_k = kt;
   r.p_c = sh.rows[n_acc].c;
-  r.p_inv_s = (float)(1.0 / sh.rows[n_acc].s);
+  r.p_inv_s = (float)sh.rows[n_acc].inv_s;
   if (residual) {
     const RowStats& qs = sh.rows[g + 1 + n_acc];
     r.q_greedy = gd;
     r.q_amax = qs.amax;
+    r.q_k = kd;
     r.q_c = qs.c;
-    r.q_inv_s = gd ? 0.0f : (float)(1.0 / qs.s);
+    r.q_inv_s = gd ? 0.0f : (float)qs.inv_s;
   }
   return r;
 }
 
 // The stop distribution a non-greedy record describes.
 template <int DT>
-__device__ __forceinline__ StopDist record_dist(const LinearArgs& a, int b, const LinRecord& r,
-                                                float Tt, float Td) {
+__device__ __forceinline__ StopDist record_dist(const LinearArgs& a, int b, const LinRecord& r) {
   StopDist d;
   const long long tr0 = (long long)r.o0 + b;
   const long long es = DT ? 2 : 4;
   d.prow = (const char*)a.target + (tr0 + r.n_acc) * (long long)a.V * es;
   d.residual = r.kind == kKindReject;
   d.qrow = d.residual ? (const char*)a.draft + ((long long)r.o0 + r.n_acc) * a.V * es : d.prow;
-  d.p_k = log2e_over_t(Tt);
+  d.p_k = r.p_k;
   d.p_c = r.p_c;
   d.p_inv_s = r.p_inv_s;
   d.q_greedy = d.residual ? r.q_greedy : 0;
   d.q_amax = r.q_amax;
-  d.q_k = (d.residual && Td > 0.0f) ? log2e_over_t(Td) : 0.0f;
+  d.q_k = d.residual ? r.q_k : 0.0f;
   d.q_c = r.q_c;
   d.q_inv_s = r.q_inv_s;
   return d;
@@ -819,103 +928,31 @@ __device__ __forceinline__ void write_row_status(const LinearArgs& a, int b, con
 }
 
 // ---------------------------------------------------------------------------
-// Linear verify, V <= 4 chunks: one work item per batch row does everything.
-
-// The weights and masses of up to 4 chunks, kept in registers.
-struct RowWeights {
-  float w[4][kPerThread];
-  double excl[4];
-};
-
-// All chunks' loads go out before any weight is formed; one block scan then
-// serves the four chunks (the same wave scan and wave-total order as
-// block_exclusive_scan, per chunk).
-template <int DT>
-__device__ __forceinline__ void row_weights(const StopDist& d, int V, int n_chunks, int vec_ok,
-                                            RowWeights& rw, double* s_scan, double* s_mass) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  StopVec<DT> sv[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    if (c < n_chunks) stop_load<DT>(d, V, c, vec_ok, sv[c]);
-  double incl[4], excl_lane[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    double acc = 0.0;
-    if (c < n_chunks) {
-      stop_weights_from<DT>(d, V, c, vec_ok, 0u, sv[c], rw.w[c]);
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e) acc += (double)rw.w[c][e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e) rw.w[c][e] = 0.0f;
-    }
-    incl[c] = wave_inclusive_scan(acc);
-    excl_lane[c] = wave_shift_up1(incl[c]);
-  }
-  __syncthreads();
-  if (lane == 63) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s_scan[c * kFinWaves + wave] = incl[c];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const double* sc = s_scan + c * kFinWaves;
-    double base = 0.0;
-    for (int i = 0; i < wave; ++i) base += sc[i];
-    rw.excl[c] = base + excl_lane[c];
-    if (threadIdx.x == 0 && c < n_chunks) {
-      double t = sc[0];
-#pragma unroll
-      for (int i = 1; i < kFinWaves; ++i) t += sc[i];
-      s_mass[c] = t;
-    }
-  }
-  __syncthreads();
-}
+// Linear verify, V of one chunk: one work item per batch row does everything.
 
 template <int DT>
 __global__ __launch_bounds__(kFinThreads) void linear_row_kernel(LinearArgs a) {
   __shared__ LinShared sh;
-  __shared__ double s_scan[4 * kFinWaves];
-  __shared__ double s_mass[kMaxChunks];
+  __shared__ double s_scan[kFinWaves];
   __shared__ int s_found[kFinWaves], s_last[kFinWaves];
-  __shared__ int s_jc;
-  __shared__ double s_base, s_t;
 
   const int b = blockIdx.x;
-  const int n_chunks = a.n_chunks;
   const LinRecord r = linear_decide<DT>(a, b, true, sh);
   int warn = 0;
   if (r.kind == kKindReject || r.kind == kKindBonus) {
-    const float Tt = a.temp_t[b], Td = a.temp_d[b];
-    StopDist d = record_dist<DT>(a, b, r, Tt, Td);
-    RowWeights rw;
-    row_weights<DT>(d, a.V, n_chunks, a.vec_ok, rw, s_scan, s_mass);
-    double R = 0.0;
-    for (int c = 0; c < n_chunks; ++c) R += s_mass[c];
-    if (!(R > 0.0) && d.residual) {
+    StopDist d = record_dist<DT>(a, b, r);
+    float w[kPerThread];
+    double R, excl;
+    for (int pass = 0; pass < 2; ++pass) {
+      stop_weights<DT>(d, a.V, 0, a.vec_ok, 0u, w);
+      const double acc = thread_total(w);
+      excl = block_exclusive_scan<kFinWaves>(acc, s_scan, &R);
+      if (R > 0.0 || !d.residual) break;
       // zero residual mass (rounding only): draw from p at this position
       warn |= kRowWarnRZero;
       d.residual = 0;
-      row_weights<DT>(d, a.V, n_chunks, a.vec_ok, rw, s_scan, s_mass);
     }
-    const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
-    const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)r.n_acc).y);
-    choose_chunk(s_mass, n_chunks, u, &s_jc, &s_base, &s_t);
-    const int jc = s_jc;
-    float wj[kPerThread];
-    double ej = 0.0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c == jc) {
-#pragma unroll
-        for (int e = 0; e < kPerThread; ++e) wj[e] = rw.w[c][e];
-        ej = rw.excl[c];
-      }
-    }
-    const int token = find_in_chunk(wj, jc, s_base, ej, s_t, s_found, s_last);
+    const int token = find_in_chunk(w, 0, 0.0, excl, (double)r.u_smp * R, s_found, s_last);
     if (threadIdx.x == 0) a.out_tokens[(long long)r.o0 + b + r.n_acc] = token;
   }
   if (threadIdx.x == 0) write_row_status(a, b, r, warn);
@@ -932,63 +969,232 @@ __global__ __launch_bounds__(kFinThreads) void linear_decide_kernel(LinearArgs a
   if (threadIdx.x == 0) a.rec[b] = r;
 }
 
-template <int DT>
+constexpr int kMassRecCache = 512;   // batch-row decisions staged in LDS by the mass pass
+
+// Mass of the stop distribution per (row, chunk), kept as the chunk's 16 wave
+// totals (the block scan's partial sums; the chunk mass is their sum in wave
+// order).  The grid stays resident; work item g takes units g, g + G, ...
+// (unit = row-major (row, chunk)), with the next unit's loads in flight
+// while the current one is reduced.
+// With CACHE the decisions are read from LDS only (B <= kMassRecCache), so
+// that waiting for one never waits for the data loads in flight.
+template <int DT, bool CACHE>
 __global__ __launch_bounds__(kFinThreads) void linear_mass_kernel(LinearArgs a) {
-  __shared__ LinRecord s_rec;
+  __shared__ LinRecord s_rec[CACHE ? kMassRecCache : 1];
+  __shared__ double s_scan[kFinWaves];
+  const int nc = a.n_chunks, V = a.V;
+  const long long total = (long long)a.B * nc;
+  if (CACHE) {
+    for (int i = threadIdx.x; i < a.B; i += kFinThreads) s_rec[i] = a.rec[i];
+    __syncthreads();
+  }
+  const long long G = gridDim.x;
+  long long u = blockIdx.x;
+  if (u >= total) return;
+  // The unit's stop distribution; a unit with nothing to draw loads row 0.
+  auto unit = [&](long long uu, int& bb, int& cc, bool& live) -> StopDist {
+    bb = (int)(uu / nc);
+    cc = (int)(uu - (long long)bb * nc);
+    const LinRecord r = CACHE ? s_rec[bb] : a.rec[bb];
+    live = r.kind == kKindReject || r.kind == kKindBonus;
+    StopDist d = record_dist<DT>(a, bb, r);
+    if (!live) {
+      d.prow = d.qrow = a.target;
+      d.residual = 0;
+    }
+    return d;
+  };
+  int b, c;
+  bool live;
+  auto reduce = [&](const StopDist& dd, int bb, int cc, const StopVec<DT>& cur, int vec) {
+    float w[kPerThread];
+    stop_weights_from<DT>(dd, V, cc, vec, 0u, cur, w);
+    const double acc = thread_total(w);
+    double m;
+    block_exclusive_scan<kFinWaves>(acc, s_scan, &m);
+    if (threadIdx.x < kFinWaves) a.wsum[((long long)bb * nc + cc) * kFinWaves + threadIdx.x] = s_scan[threadIdx.x];
+  };
+  if (!a.vec_ok) {                        // unaligned rows: plain loads, no prefetch
+    const StopVec<DT> none{};
+    for (; u < total; u += G) {
+      const StopDist dd = unit(u, b, c, live);
+      if (live) reduce(dd, b, c, none, 0);
+    }
+    return;
+  }
+  StopDist d = unit(u, b, c, live);
+  StopVec<DT> buf0, buf1;
+  stop_load<DT>(d, V, c, buf0);
+  // One step: issue the next unit's loads into `nxt`, reduce the current
+  // unit from `cur`; false when the current unit was this item's last.
+  auto step = [&](StopVec<DT>& cur, StopVec<DT>& nxt) -> bool {
+    const long long u1 = u + G;
+    const bool has1 = u1 < total;
+    int b1, c1;
+    bool live1;
+    const StopDist d1 = unit(has1 ? u1 : u, b1, c1, live1);
+    live1 = live1 && has1;
+    stop_load<DT>(d1, V, c1, nxt);
+    if (live) reduce(d, b, c, cur, 1);
+    u = u1;
+    b = b1;
+    c = c1;
+    live = live1;
+    d = d1;
+    return has1;
+  };
+  for (;;) {
+    if (!step(buf0, buf1)) break;
+    if (!step(buf1, buf0)) break;
+  }
+}
+
+// V of 2..4 chunks: every (row, chunk) work item takes the row's decision
+// itself (identical arithmetic, so identical results; the chunk-0 item
+// stores it and the accepted tokens) and then its chunk's wave totals, so
+// that the stop row is read, and its weights formed, by as many compute
+// units as it has chunks.
+template <int DT>
+__global__ __launch_bounds__(kFinThreads) void linear_decide_mass_kernel(LinearArgs a) {
+  __shared__ LinShared sh;
   __shared__ double s_scan[kFinWaves];
   const int n_chunks = a.n_chunks;
   const int b = blockIdx.x / n_chunks;
   const int c = blockIdx.x - b * n_chunks;
-  if (threadIdx.x == 0) s_rec = a.rec[b];
-  const float Tt = a.temp_t[b], Td = a.temp_d[b];
-  __syncthreads();
-  const LinRecord r = s_rec;
+  const LinRecord r = linear_decide<DT>(a, b, c == 0, sh);
+  if (c == 0 && threadIdx.x == 0) a.rec[b] = r;
   if (r.kind != kKindReject && r.kind != kKindBonus) return;
-  const StopDist d = record_dist<DT>(a, b, r, Tt, Td);
-  const double m = chunk_mass<DT>(d, a.V, c, a.vec_ok, 0u, s_scan);
-  if (threadIdx.x == 0) a.mass[(long long)b * n_chunks + c] = m;
+  const StopDist d = record_dist<DT>(a, b, r);
+  chunk_mass<DT>(d, a.V, c, a.vec_ok, 0u, s_scan);
+  if (threadIdx.x < kFinWaves)
+    a.wsum[((long long)b * n_chunks + c) * kFinWaves + threadIdx.x] = s_scan[threadIdx.x];
 }
 
+// This wave's 64 lanes form the weights of threads 64 w + lane (of 1024) of
+// chunk c and their exclusive prefix within the wave, as the block scan does.
 template <int DT>
-__global__ __launch_bounds__(kFinThreads) void linear_select_kernel(LinearArgs a) {
-  __shared__ LinRecord s_rec;
-  __shared__ double s_mass[kMaxChunks];
-  __shared__ double s_scan[kFinWaves];
-  __shared__ int s_found[kFinWaves], s_last[kFinWaves];
-  __shared__ int s_jc;
-  __shared__ double s_base, s_t;
+__device__ __forceinline__ double wave_chunk_part(const StopDist& d, int V, int c, int w,
+                                                  int vec_ok, float wt[kPerThread], double* acc_out) {
+  const int tix = w * 64 + (threadIdx.x & 63);
+  StopVec<DT> sv;
+  if (vec_ok) stop_load<DT>(d, V, c, sv, tix);
+  stop_weights_from<DT>(d, V, c, vec_ok, 0u, sv, wt, tix);
+  const double acc = thread_total(wt);
+  *acc_out = acc;
+  return wave_inclusive_scan(acc);
+}
 
-  const int tid = threadIdx.x;
+// Select, one wave per batch row: the chunk holding u * R from the chunk masses (each the wave-order sum of its
+// 16 wave totals), the wave of that chunk holding it from the running wave
+// totals, then the element from that wave's 512 weights -- the same sums,
+// in the same order, as a block-wide search over the chunk.  With zero
+// residual mass (rounding only) the draw falls back to p, whose wave totals
+// this wave then forms itself.
+template <int DT>
+__global__ __launch_bounds__(64) void linear_select_kernel(LinearArgs a) {
+  __shared__ double s_ws[kMaxChunks * kFinWaves];
+  const int lane = threadIdx.x;
   const int b = blockIdx.x;
-  const int n_chunks = a.n_chunks;
-  if (tid == 0) s_rec = a.rec[b];
-  if (tid < n_chunks) s_mass[tid] = a.mass[(long long)b * n_chunks + tid];
-  const float Tt = a.temp_t[b], Td = a.temp_d[b];
-  __syncthreads();
-  const LinRecord r = s_rec;
+  const int nc = a.n_chunks;
+  const int nws = nc * kFinWaves;
+  const double* wsb = a.wsum + (long long)b * nws;
+  constexpr int kPerLaneWs = kMaxChunks * kFinWaves / 64;
+  double wv[kPerLaneWs];
+#pragma unroll
+  for (int k = 0; k < kPerLaneWs; ++k) {
+    const int i = lane + 64 * k;
+    wv[k] = wsb[i < nws ? i : 0];
+  }
+  const LinRecord r = a.rec[b];
   int warn = 0;
   if (r.kind == kKindReject || r.kind == kKindBonus) {
-    StopDist d = record_dist<DT>(a, b, r, Tt, Td);
-    double R = 0.0;
-    for (int j = 0; j < n_chunks; ++j) R += s_mass[j];
-    if (!(R > 0.0)) {
-      // zero residual mass (rounding only): draw from p at this position
+    StopDist d = record_dist<DT>(a, b, r);
+#pragma unroll
+    for (int k = 0; k < kPerLaneWs; ++k)
+      if (lane + 64 * k < nws) s_ws[lane + 64 * k] = wv[k];
+    __syncthreads();
+    auto chunk_masses = [&]() -> double {
+      double m = 0.0;
+      if (lane < nc) {
+        const double* w = s_ws + lane * kFinWaves;
+        m = w[0];
+#pragma unroll
+        for (int i = 1; i < kFinWaves; ++i) m += w[i];
+      }
+      return m;
+    };
+    double m = chunk_masses();
+    double incl = wave_inclusive_scan(m);
+    double R = readlane_f64(incl, 63);
+    if (!(R > 0.0) && d.residual) {
+      // zero residual mass: form p's wave totals here, chunk by chunk
       warn |= kRowWarnRZero;
       d.residual = 0;
-      for (int j = 0; j < n_chunks; ++j) {
-        const double mj = chunk_mass<DT>(d, a.V, j, a.vec_ok, 0u, s_scan);
-        if (tid == 0) s_mass[j] = mj;
+      for (int c = 0; c < nc; ++c) {
+        for (int w = 0; w < kFinWaves; ++w) {
+          float wt[kPerThread];
+          double acc;
+          const double inc = wave_chunk_part<DT>(d, a.V, c, w, a.vec_ok, wt, &acc);
+          const double tot = readlane_f64(inc, 63);
+          if (lane == 0) s_ws[c * kFinWaves + w] = tot;
+        }
       }
       __syncthreads();
+      m = chunk_masses();
+      incl = wave_inclusive_scan(m);
+      R = readlane_f64(incl, 63);
     }
-    const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
-    const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)r.n_acc).y);
-    choose_chunk(s_mass, n_chunks, u, &s_jc, &s_base, &s_t);
-    const int token = chunk_select<DT>(d, a.V, s_jc, a.vec_ok, 0u, s_base, s_t, s_scan, s_found,
-                                       s_last);
-    if (tid == 0) a.out_tokens[(long long)r.o0 + b + r.n_acc] = token;
+    // chunk
+    const double t = (double)r.u_smp * R;
+    const double excl = wave_shift_up1(incl);
+    const unsigned long long hit = __ballot(lane < nc && m > 0.0 && incl > t);
+    const unsigned long long pos = __ballot(lane < nc && m > 0.0);
+    const int jc = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+    const double base = readlane_f64(excl, jc);
+    // wave of the chunk: running wave totals X_w, summed from 0 in wave order
+    const double* wj = s_ws + jc * kFinWaves;
+    int ws_hit = -1, ws_pos = -1;
+    double X = 0.0, Xw = 0.0;
+    for (int w = 0; w < kFinWaves; ++w) {
+      const double next = X + wj[w];
+      if (wj[w] > 0.0) {
+        if (ws_hit < 0 && base + next > t) {
+          ws_hit = w;
+          Xw = X;
+        }
+        ws_pos = w;
+      }
+      X = next;
+    }
+    int wsel = ws_hit;
+    if (wsel < 0) {
+      wsel = ws_pos >= 0 ? ws_pos : 0;
+      X = 0.0;
+      for (int w = 0; w < wsel; ++w) X += wj[w];
+      Xw = X;
+    }
+    // element, within wave wsel of chunk jc
+    float wt[kPerThread];
+    double acc;
+    const double inc = wave_chunk_part<DT>(d, a.V, jc, wsel, a.vec_ok, wt, &acc);
+    double run = base + (Xw + wave_shift_up1(inc));
+    const int e0 = jc * kChunk + (wsel * 64 + lane) * kPerThread;
+    int found = 0x7fffffff, lastp = -1;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      run += (double)wt[e];
+      if (found == 0x7fffffff && run > t && wt[e] > 0.0f) found = e0 + e;
+      if (wt[e] > 0.0f) lastp = e0 + e;
+    }
+    const unsigned long long fm = __ballot(found != 0x7fffffff);
+    const unsigned long long lm = __ballot(lastp >= 0);
+    int token;
+    if (fm) token = __builtin_amdgcn_readlane(found, __ffsll((long long)fm) - 1);
+    else if (lm) token = __builtin_amdgcn_readlane(lastp, 63 - __clzll((long long)lm));
+    else token = jc * kChunk;
+    if (lane == 0) a.out_tokens[(long long)r.o0 + b + r.n_acc] = token;
   }
-  if (tid == 0) write_row_status(a, b, r, warn);
+  if (lane == 0) write_row_status(a, b, r, warn);
 }
 
 // ---------------------------------------------------------------------------
@@ -1025,27 +1231,28 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
   const bool greedy = T == 0.0f;
   const float k2 = (greedy || err0) ? 0.0f : log2e_over_t(T);
 
-  // Wave 0 (one lane per node) fetches the tree and the logit of each node's
-  // token under its parent; meanwhile every wave merges node rows, all of
-  // its rows' partials loaded before the first is reduced.
-  int par = -1, tok = 0;
-  float x = 0.0f;
-  bool badpar = false, badtok = false;
-  if (!err0 && tid > 0 && tid < nn) {
-    par = a.parents[rb + tid];
-    tok = a.tokens[rb + tid];
-    badpar = par < 0 || par >= tid;
-    badtok = tok < 0 || tok >= V;
-    x = load_logit<DT>(a.target, (rb + (badpar ? 0 : par)) * (long long)V + (badtok ? 0 : tok));
+  // Every wave loads its node rows' partials (rows clamped into the tree)
+  // and one node per lane: its parent, its token and the logit of the token
+  // under the parent (gathered by the vocabulary pass).  Only wave 0's lanes
+  // 1..nn-1 keep the latter.  No load sits behind a branch.
+  Partial q[kNodesPerWave];
+#pragma unroll
+  for (int k = 0; k < kNodesPerWave; ++k) {
+    const int n = min(wave + k * kFinWaves, N - 1);
+    q[k] = lane_partial(a.part + (rb + n) * n_parts, n_parts);
+  }
+  const int li = lane < N ? lane : 0;
+  int par = a.parents[rb + li];
+  int tok = a.tokens[rb + li];
+  const float x = a.gath[rb + li];   // gathered by the vocabulary pass
+  const bool mine = !err0 && tid > 0 && tid < nn;
+  const bool badpar = mine && (par < 0 || par >= tid);
+  const bool badtok = mine && (tok < 0 || tok >= V);
+  if (!mine) {
+    par = -1;
+    tok = 0;
   }
   if (!err0) {
-    Partial q[kNodesPerWave];
-#pragma unroll
-    for (int k = 0; k < kNodesPerWave; ++k) {
-      const int n = wave + k * kFinWaves;
-      q[k] = n < nn ? lane_partial(a.part + (rb + n) * n_parts, n_parts)
-                    : Partial{-__builtin_huge_valf(), 0x7fffffff, 0.0};
-    }
 #pragma unroll
     for (int k = 0; k < kNodesPerWave; ++k) {
       const int n = wave + k * kFinWaves;
@@ -1057,7 +1264,8 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
           s_rowok[n] = ok;
         }
         if (!greedy && lane < n_chunks)
-          s_cm[n * n_chunks + lane] = q[k].s > 0.0 ? scale_pow2(q[k].s, q[k].c - rs.c) / rs.s : 0.0;
+          s_cm[n * n_chunks + lane] =
+              q[k].s > 0.0 ? scale_pow2(q[k].s, q[k].c - rs.c) / rs.s : 0.0;
       }
     }
   }
@@ -1179,7 +1387,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
     d.residual = 0;
     d.p_k = k2;
     d.p_c = st.c;
-    d.p_inv_s = (float)(1.0 / st.s);
+    d.p_inv_s = (float)st.inv_s;
     d.q_greedy = 0;
     d.q_amax = 0;
     d.q_k = d.q_c = d.q_inv_s = 0.0f;
@@ -1236,67 +1444,95 @@ long long stats_items(long long n_rows, int n_chunks) {
   return n_rows * n_chunks * kPartsPerChunk;
 }
 
-// Workgroups of the streaming pass that fit on the current device at once.
-static int stats_resident_blocks(int dtype) {
-  static std::atomic<int> cache[2][kMaxDevices];
+// Workgroups of a kernel that fit on the current device at once (cached per
+// kernel slot and device).
+template <typename K>
+static int resident_blocks(int slot, K kernel, int threads) {
+  static std::atomic<int> cache[8][kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  int c = cache[dtype][dev].load(std::memory_order_relaxed);
+  int c = cache[slot][dev].load(std::memory_order_relaxed);
   if (c == 0) {
     int n_cu = 0, occ = 0;
     if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       n_cu = 0;
-    const hipError_t e = dtype == 1
-        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, stats_kernel<1>, kThreads, 0)
-        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, stats_kernel<0>, kThreads, 0);
-    if (e != hipSuccess) occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess)
+      occ = 0;
     c = std::max(1, n_cu) * std::max(1, occ);
-    cache[dtype][dev].store(c, std::memory_order_relaxed);
+    cache[slot][dev].store(c, std::memory_order_relaxed);
   }
   return c;
+}
+
+static int stats_resident_blocks(int dt, int ring) {
+  if (dt == 1)
+    return ring == 4 ? resident_blocks(0, stats_kernel<1, 4>, kThreads)
+                     : resident_blocks(1, stats_kernel<1, 2>, kThreads);
+  return resident_blocks(2, stats_kernel<0, 2>, kThreads);
+}
+
+static int mass_resident_blocks(int dt) {
+  return dt == 1 ? resident_blocks(3, linear_mass_kernel<1, true>, kFinThreads)
+                 : resident_blocks(4, linear_mass_kernel<0, true>, kFinThreads);
 }
 
 // Pass 1.  Launched with events, the events bracket the kernel's dispatch.
 hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_t ev_start,
                         hipEvent_t ev_stop) {
-  const long long segs = stats_items(a.n_rows, a.n_chunks);
-  if (segs <= 0) return hipSuccess;
+  const long long units = stats_items(a.n_rows, a.n_chunks);
+  if (units <= 0) return hipSuccess;
   const int dt = dtype == 1 ? 1 : 0;
-  const long long want = (segs + kWaves - 1) / kWaves;
-  const dim3 grid((unsigned)std::min<long long>(want, stats_resident_blocks(dt))), block(kThreads);
   const bool timed = ev_start && ev_stop;
-  if (dt == 1) {
-    if (timed)
-      hipExtLaunchKernelGGL(stats_kernel<1>, grid, block, 0, st, ev_start, ev_stop, 0, a);
-    else
-      stats_kernel<1><<<grid, block, 0, st>>>(a);
-  } else {
-    if (timed)
-      hipExtLaunchKernelGGL(stats_kernel<0>, grid, block, 0, st, ev_start, ev_stop, 0, a);
-    else
-      stats_kernel<0><<<grid, block, 0, st>>>(a);
-  }
+  const dim3 block(kThreads);
+#define SV_LAUNCH(K)                                                          \
+  do {                                                                        \
+    if (timed) hipExtLaunchKernelGGL(K, grid, block, 0, st, ev_start, ev_stop, 0, a); \
+    else K<<<grid, block, 0, st>>>(a);                                        \
+  } while (0)
+  const long long want = (units + kWaves - 1) / kWaves;
+  // a whole chunk in flight per wave when one round of waves covers the call
+  const int ring = (dt == 1 && want <= stats_resident_blocks(1, 4)) ? 4 : 2;
+  const dim3 grid((unsigned)(std::min<long long>(want, stats_resident_blocks(dt, ring)) +
+                             gather_blocks(a)));
+  if (dt == 1 && ring == 4) SV_LAUNCH((stats_kernel<1, 4>));
+  else if (dt == 1) SV_LAUNCH((stats_kernel<1, 2>));
+  else SV_LAUNCH((stats_kernel<0, 2>));
+#undef SV_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t launch_linear_finish(int dtype, const LinearArgs& a, hipStream_t st) {
   const dim3 rows((unsigned)a.B), block(kFinThreads);
-  if (a.n_chunks <= 4) {
+  if (a.n_chunks == 1) {
     if (dtype == 1) linear_row_kernel<1><<<rows, block, 0, st>>>(a);
     else linear_row_kernel<0><<<rows, block, 0, st>>>(a);
     return hipGetLastError();
   }
-  const dim3 items((unsigned)((long long)a.B * a.n_chunks));
-  if (dtype == 1) linear_decide_kernel<1><<<rows, block, 0, st>>>(a);
-  else linear_decide_kernel<0><<<rows, block, 0, st>>>(a);
-  hipError_t e = hipGetLastError();
+  const long long units = (long long)a.B * a.n_chunks;
+  hipError_t e;
+  if (a.n_chunks <= 4) {
+    const dim3 items((unsigned)units);
+    if (dtype == 1) linear_decide_mass_kernel<1><<<items, block, 0, st>>>(a);
+    else linear_decide_mass_kernel<0><<<items, block, 0, st>>>(a);
+    e = hipGetLastError();
+  } else {
+    if (dtype == 1) linear_decide_kernel<1><<<rows, block, 0, st>>>(a);
+    else linear_decide_kernel<0><<<rows, block, 0, st>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid((unsigned)std::min<long long>(units, mass_resident_blocks(dtype == 1 ? 1 : 0)));
+    if (a.B <= kMassRecCache) {
+      if (dtype == 1) linear_mass_kernel<1, true><<<mgrid, block, 0, st>>>(a);
+      else linear_mass_kernel<0, true><<<mgrid, block, 0, st>>>(a);
+    } else {
+      if (dtype == 1) linear_mass_kernel<1, false><<<mgrid, block, 0, st>>>(a);
+      else linear_mass_kernel<0, false><<<mgrid, block, 0, st>>>(a);
+    }
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
-  if (dtype == 1) linear_mass_kernel<1><<<items, block, 0, st>>>(a);
-  else linear_mass_kernel<0><<<items, block, 0, st>>>(a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (dtype == 1) linear_select_kernel<1><<<rows, block, 0, st>>>(a);
-  else linear_select_kernel<0><<<rows, block, 0, st>>>(a);
+  if (dtype == 1) linear_select_kernel<1><<<rows, dim3(64), 0, st>>>(a);
+  else linear_select_kernel<0><<<rows, dim3(64), 0, st>>>(a);
   return hipGetLastError();
 }
 
