@@ -1,9 +1,10 @@
 // Tree- or causal-masked verify attention on MFMA (gfx950).
 //
 // One workgroup per (batch row, head); wave w owns query rows 16w..16w+15.
-// Keys stream in tiles of 64 from the cache into LDS (K row-major, V
-// transposed), with the next tile's global loads in flight while the
-// current tile is multiplied.  Per tile and wave:
+// Keys stream in tiles of 64 from the cache into LDS (K and V row-major),
+// with the next tile's global loads in flight while the current tile is
+// multiplied.  The V^T operand is formed on the way out of LDS by the
+// transposing read ds_read_b64_tr_b16.  Per tile and wave:
 //
 //   S^T[64 keys x 16 queries] = K_tile . Q^T    4 key blocks x 4 d-steps of
 //                                               v_mfma_f32_16x16x32_bf16
@@ -35,7 +36,22 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kKT = 64;               // keys per tile
 constexpr int kKsStride = kD + 8;     // bf16 per K row in LDS (16 B pad)
-constexpr int kVtStride = kKT + 8;    // bf16 per V^T row in LDS (16 B pad)
+// bf16 per V row in LDS: 72 dwords, so the four rows x 32 bytes that one
+// 16-lane transposing read touches fall on 32 distinct banks
+constexpr int kVsStride = kD + 16;
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16, per group of 16 lanes: lane j receives element (j & 3)
+// of the 4-element blocks addressed by lanes 4 e + (j >> 2), e = 0..3.  With
+// lane i addressing row key0 + (i >> 2), column d0 + 4 (i & 3), lane j thus
+// receives V[key0 + e][d0 + j] for e = 0..3: four consecutive keys of one
+// column, as the MFMA A operand wants them.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4i16_t __attribute__((address_space(3)))*)p);
+  return __builtin_bit_cast(uint2, r);
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -49,9 +65,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kKT * kVsStride];
   __shared__ unsigned long long s_anc[kMaxNodes];
   __shared__ int s_L, s_ok;
 
@@ -112,20 +128,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 
   const int total = L + N;
   const int n_tiles = (total + kKT - 1) / kKT;
+  // The next tile's loads are in flight while this tile is multiplied.  Keys
+  // past the end load the last key (finite, masked to weight 0), so that no
+  // load sits behind a branch: a load whose value crosses a branch join is
+  // waited for there, which would drain the prefetch.
   uint4 kr[4], vr[4];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ci = j * kThreads + tid;
       const int key = ci >> 4, d0 = (ci & 15) * 8;
-      const int gk = t * kKT + key;
-      if (gk < total) {
-        kr[j] = *(const uint4*)(a.k + headKV + (long long)gk * kD + d0);
-        vr[j] = *(const uint4*)(a.v + headKV + (long long)gk * kD + d0);
-      } else {
-        kr[j] = make_uint4(0, 0, 0, 0);
-        vr[j] = make_uint4(0, 0, 0, 0);
-      }
+      const int gk = min(t * kKT + key, total - 1);
+      kr[j] = *(const uint4*)(a.k + headKV + (long long)gk * kD + d0);
+      vr[j] = *(const uint4*)(a.v + headKV + (long long)gk * kD + d0);
     }
   };
   load_tile(0);
@@ -137,15 +152,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       const int ci = j * kThreads + tid;
       const int key = ci >> 4, d0 = (ci & 15) * 8;
       *(uint4*)&Ks[key * kKsStride + d0] = kr[j];
-      const uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        Vt[(d0 + 2 * h) * kVtStride + key] = (uint16_t)(vw[h] & 0xffffu);
-        Vt[(d0 + 2 * h + 1) * kVtStride + key] = (uint16_t)(vw[h] >> 16);
-      }
+      *(uint4*)&Vs[key * kVsStride + d0] = vr[j];
     }
     __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    load_tile(min(t + 1, n_tiles - 1));
 
     f32x4_t s[4];
 #pragma unroll
@@ -205,11 +215,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                                   pack_bf16x2(s[2 * ks2 + 1][0], s[2 * ks2 + 1][1]),
                                   pack_bf16x2(s[2 * ks2 + 1][2], s[2 * ks2 + 1][3]));
       const bf16x8_t pop = as_bf16x8(pu);
+      // V rows of the keys 32 ks2 + 4 g + {0..3} and 32 ks2 + 16 + 4 g + {0..3}
+      const uint16_t* vlo = &Vs[(ks2 * 32 + 4 * g + (col >> 2)) * kVsStride + 4 * (col & 3)];
+      const uint16_t* vhi = vlo + 16 * kVsStride;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const uint16_t* vrow = &Vt[(mb * 16 + col) * kVtStride + ks2 * 32 + 4 * g];
-        const uint2 lo = *(const uint2*)vrow;
-        const uint2 hi = *(const uint2*)(vrow + 16);
+        const uint2 lo = lds_read_tr16(vlo + mb * 16);
+        const uint2 hi = lds_read_tr16(vhi + mb * 16);
         const uint4 vu = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vu), pop, o[mb], 0, 0, 0);
       }
