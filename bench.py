@@ -158,12 +158,17 @@ def load_traffic(path, workload, kernel_sig):
 
 
 def kernel_source_sig(wl):
-    """SHA-1 of the source file that holds the dominant kernel."""
+    """SHA-1 over the sources that the dominant kernel is compiled from (its
+    own file and the headers that file includes)."""
     import hashlib
-    name = "sv_attn.hip" if wl == "attn_tree" else "sv_logits.hip"
-    path = os.path.join(ROOT, "rejection_sampling_verify_04_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha1(f.read()).hexdigest()
+    csrc = os.path.join(ROOT, "rejection_sampling_verify_04_amd", "csrc")
+    names = (["sv_attn.hip", "sv_common.h", "sv_internal.h"] if wl == "attn_tree"
+             else ["sv_stats.hip", "sv_common.h", "sv_internal.h"])
+    h = hashlib.sha1()
+    for name in names:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def main():

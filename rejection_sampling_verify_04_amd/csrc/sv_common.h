@@ -56,6 +56,11 @@ __device__ __forceinline__ bool temp_ok(float T) {
 // Raw hardware 2^x (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s * 2^d for an integer-valued d <= 0 (exact; -inf and huge |d| give 0).
+__device__ __forceinline__ double scale_pow2(double s, float d) {
+  return __builtin_ldexp(s, (int)fmaxf(d, -4096.0f));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

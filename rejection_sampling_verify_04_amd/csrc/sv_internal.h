@@ -4,6 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
+#include "sv_common.h"
+
 namespace sv {
 
 struct Partial;
@@ -93,6 +98,26 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
 };
+
+// Workgroups of a kernel that fit on the current device at once (cached per
+// kernel slot and device; slots are unique across the library).
+template <typename K>
+inline int resident_blocks(int slot, K kernel, int threads) {
+  static std::atomic<int> cache[8][kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int c = cache[slot][dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int n_cu = 0, occ = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess)
+      occ = 0;
+    c = std::max(1, n_cu) * std::max(1, occ);
+    cache[slot][dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
 
 long long stats_items(long long n_rows, int n_chunks);
 hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_t ev_start,

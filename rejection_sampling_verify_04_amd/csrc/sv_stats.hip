@@ -1,0 +1,457 @@
+// Pass 1 of the vocabulary-wide verify (linear and tree), gfx950.
+//
+// stats_kernel: a resident grid in which each wave reduces whole 8192-logit
+// chunks of the logit rows (one HBM read of every logit, with non-temporal
+// 16-byte loads in flight ahead of the reduction) into one Partial per (row,
+// chunk): an integer log2 offset and a float64 sum of exponentials for a
+// sampled row, the maximum and its first index for a greedy row.  Its first
+// work items gather the logits at the draft tokens.
+//
+// Sources: the softmax statistics that the acceptance ratio and the draws
+// need (kwkr.cn/news/620872 §2.3, §4.1; blog.lonae.com/posts/
+// 2026-draft-model-kv-jDwzYp, formal-definition paragraph).
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+
+#include "sv_common.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------
+// Pass 1: statistics of every logit chunk.
+//
+// One wave reduces one chunk (8192 elements) of one row at a time, as four
+// sub-segments of 2048 elements; each of the wave's load instructions reads
+// 1 KB of consecutive bytes.  Each lane keeps a running offset and sum over
+// its 128 elements of the chunk, and the lanes are combined once per chunk.
+// The grid is sized to stay resident: wave g of G takes chunks g, g + G,
+// g + 2G, ... of the concatenated rows, so at any moment the grid sweeps one
+// contiguous window of the logits, and each wave's sub-segment loads run
+// RING sub-segments ahead of the one it reduces, across chunk boundaries.
+//
+// Offsets of sampled rows are integers (ceil of the scaled maximum), so every
+// rescale of a sum is an exact power of two.
+
+// One wave's 2048-element segment: lane l's vector j covers elements
+// seg0 + (j * 64 + l) * EPV + [0, EPV), so each load instruction of the wave
+// reads 1 KB of consecutive bytes.
+template <int DT>
+struct SegLoad {
+  static constexpr int ES = DT ? 2 : 4;          // bytes per element
+  static constexpr int EPV = 16 / ES;            // elements per 16-byte load
+  static constexpr int NV = kPerLane / EPV;      // loads per lane per segment
+  uint4 raw[NV];
+
+  // Vectors past V read as -inf.  Rows are read once here, so the loads carry
+  // the non-temporal hint.  With vectors valid (V a multiple of EPV) a vector
+  // is either wholly inside the row or wholly past it.
+  __device__ __forceinline__ void issue(const char* rowp, int V, int seg0) {
+    const int lane = threadIdx.x & 63;
+    constexpr uint32_t kNegInf = DT ? 0xff80ff80u : 0xff800000u;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e0 = seg0 + (j * 64 + lane) * EPV;
+      if (e0 < V) {
+        const u32x4_t w =
+            __builtin_nontemporal_load((const u32x4_t*)(rowp + (long long)e0 * ES));
+        raw[j] = make_uint4(w.x, w.y, w.z, w.w);
+      } else {
+        raw[j] = make_uint4(kNegInf, kNegInf, kNegInf, kNegInf);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void unpack(float v[kPerLane]) const {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (DT == 1) {
+        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[j * 8 + 2 * h] = bf16_lo(w[h]);
+          v[j * 8 + 2 * h + 1] = bf16_hi(w[h]);
+        }
+      } else {
+        v[j * 4 + 0] = __uint_as_float(raw[j].x);
+        v[j * 4 + 1] = __uint_as_float(raw[j].y);
+        v[j * 4 + 2] = __uint_as_float(raw[j].z);
+        v[j * 4 + 3] = __uint_as_float(raw[j].w);
+      }
+    }
+  }
+};
+
+template <int DT>
+__device__ __forceinline__ void seg_load_scalar(const char* rowp, int V, int seg0,
+                                                float v[kPerLane]) {
+  constexpr int EPV = SegLoad<DT>::EPV;
+  constexpr int NV = SegLoad<DT>::NV;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) {
+      const int e = seg0 + (j * 64 + lane) * EPV + k;
+      v[j * EPV + k] = e < V ? load_logit<DT>(rowp, e) : -__builtin_huge_valf();
+    }
+  }
+}
+
+constexpr int kStatsCache = 1024;  // batch rows whose offsets/temperatures go to LDS
+
+// Largest j in [0, B) whose key off[j] + add * j is <= x, found by one wave
+// with 64 probes per round (B <= 64: one round; B <= 4096: two).
+__device__ __forceinline__ int wave_find_batch_row(const int* off, int B, long long x, int add) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, len = B;
+  while (len > 1) {
+    const int step = (len + 63) >> 6;
+    bool pred = false;
+    if (lane * step < len) {
+      const int j = lo + lane * step;
+      pred = (long long)off[j] + (long long)add * j <= x;
+    }
+    const unsigned long long m = __ballot(pred);
+    const int best = m ? 63 - __builtin_clzll(m) : 0;
+    lo += best * step;
+    len = min(step, len - best * step);
+  }
+  return lo;
+}
+
+// Largest b in [0, B) with off[b] <= i, each lane for its own i (fixed
+// number of steps: ceil(log2(B))).
+__device__ __forceinline__ int lane_batch_row(const int* off, int B, long long i) {
+  int lo = 0;
+  for (int step = 1 << (31 - __builtin_clz(max(B, 1))); step > 0; step >>= 1)
+    if (lo + step < B && (long long)off[lo + step] <= i) lo += step;
+  return lo;
+}
+
+// Work items of the stats launch that gather logits at draft tokens (one
+// item per thread): linear, total_draft items; tree, B * N.
+__host__ __device__ inline long long gather_items(const StatsArgs& a) {
+  return a.tree ? (long long)a.B * a.N : (long long)a.total_draft;
+}
+__host__ __device__ inline int gather_blocks(const StatsArgs& a) {
+  return (int)((gather_items(a) + kThreads - 1) / kThreads);
+}
+
+// gath[i] = logit of item i's token: linear, x_i[d_i] at [i] and y_i[d_i]
+// at [total_draft + i] (target row i + b for position i of batch row b,
+// draft row i); tree, node j's token under its parent row at [j].  Tokens
+// and parents outside their range read index 0 (the finish pass flags them).
+template <int DT>
+__device__ void gather_logits(const StatsArgs& a, int* s_off) {
+  const long long n = gather_items(a);
+  const long long it = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const int V = a.V;
+  const bool cache = !a.tree && a.B <= kStatsCache;
+  if (cache) {
+    for (int i = threadIdx.x; i <= a.B; i += kThreads) s_off[i] = a.offsets[i];
+    __syncthreads();
+  }
+  if (it >= n) return;
+  const int tok = a.tokens[it];
+  const int tc = (tok >= 0 && tok < V) ? tok : 0;
+  if (a.tree) {
+    const int par = a.parents[it];
+    const long long xr = it - it % a.N + ((par >= 0 && par < a.N) ? par : 0);
+    a.gath[it] = load_logit<DT>(a.rows_a, xr * V + tc);
+  } else {
+    const int b = cache ? lane_batch_row(s_off, a.B, it) : lane_batch_row(a.offsets, a.B, it);
+    a.gath[it] = load_logit<DT>(a.rows_a, (it + b) * V + tc);
+    a.gath[n + it] = load_logit<DT>(a.rows_b, it * V + tc);
+  }
+}
+
+// A lane's running statistics over its elements of one chunk.
+struct LaneStats {
+  float c;     // sampled: integer log2 offset; greedy: largest value so far
+  int idx;     // greedy: first index of that value
+  double s;    // sampled: sum of 2^(x k - c)
+};
+
+// Fold one sub-segment (this lane's 32 values, in increasing index order:
+// element e of vector j sits at seg0 + (j * 64 + lane) * EPV + e).
+template <int DT>
+__device__ __forceinline__ void lane_fold(float v[kPerLane], int seg0, bool greedy, float k2,
+                                          LaneStats& st) {
+  constexpr int EPV = SegLoad<DT>::EPV;
+  constexpr int NV = SegLoad<DT>::NV;
+  const int lane = threadIdx.x & 63;
+  if (greedy) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float x = v[j * EPV + e];
+        const bool gt = x > st.c;
+        st.c = gt ? x : st.c;
+        st.idx = gt ? seg0 + (j * 64 + lane) * EPV + e : st.idx;
+      }
+    }
+    return;
+  }
+  float m = -__builtin_huge_valf();
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) m = fmaxf(m, v[e]);
+  const float mk = ceilf(m * k2);
+  if (mk > st.c) {
+    st.s = scale_pow2(st.s, st.c - mk);
+    st.c = mk;
+  }
+  const float cu = st.c > -__builtin_huge_valf() ? st.c : 0.0f;  // all -inf so far: terms are 0
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) v[e] = exp2_hw(fmaf(v[e], k2, -cu));
+#pragma unroll
+  for (int w = kPerLane / 2; w >= 1; w >>= 1) {
+#pragma unroll
+    for (int e = 0; e < w; ++e) v[e] += v[e + w];
+  }
+  st.s += (double)v[0];
+}
+
+// Combine the wave's lanes into the chunk's Partial.
+__device__ __forceinline__ Partial wave_combine(const LaneStats& st, bool greedy) {
+  if (greedy) {
+    const unsigned long long key =
+        ((unsigned long long)float_order_key(st.c) << 32) | (0xffffffffu - (uint32_t)st.idx);
+    const unsigned long long best = wave_max_u64(key);
+    return Partial{float_from_order_key((uint32_t)(best >> 32)),
+                   (int)(0xffffffffu - (uint32_t)best), 0.0};
+  }
+  const float C = wave_max(st.c);
+  if (!(C > -__builtin_huge_valf())) return Partial{-__builtin_huge_valf(), 0, 0.0};
+  const double t = st.s != 0.0 ? scale_pow2(st.s, st.c - C) : 0.0;
+  return Partial{C, 0, wave_sum(t)};
+}
+
+// RING = sub-segments in flight per wave: 2 for streaming many chunks per
+// wave, 4 (a whole chunk) when every wave has about one chunk.
+template <int DT, int RING>
+__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
+  __shared__ int s_i[kStatsCache + 1];
+  __shared__ float s_f0[kStatsCache], s_f1[kStatsCache];
+
+  const int V = a.V;
+  // The first work items gather the logits at the draft tokens; being
+  // dispatched first, they finish while the rest stream the vocabulary.
+  const int n_gblk = gather_blocks(a);
+  if ((int)blockIdx.x < n_gblk) {
+    gather_logits<DT>(a, s_i);
+    return;
+  }
+  const int blk = blockIdx.x - n_gblk;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t nc = (uint32_t)a.n_chunks;
+  const uint32_t total = (uint32_t)a.n_rows * nc;   // < 2^31 (checked by the host)
+  const uint32_t G = (gridDim.x - n_gblk) * kWaves;
+  const uint32_t Gq = G / nc, Gr = G - Gq * nc;
+  const long long rowbytes = (long long)V * SegLoad<DT>::ES;
+  auto row_ptr = [&](uint32_t r) -> const char* {
+    return r < a.n_a ? (const char*)a.rows_a + (long long)r * rowbytes
+                     : (const char*)a.rows_b + ((long long)r - a.n_a) * rowbytes;
+  };
+
+  uint32_t u = blk * kWaves + wave;
+  uint32_t row = u / nc, ch = u - row * nc;
+
+  SegLoad<DT> ring[RING];
+  // The first chunk's loads go out before anything else; an unused tree
+  // row is still allocated, so reading it is harmless.
+  if (a.vec_ok && u < total) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
+  }
+
+  const bool cache = a.B <= kStatsCache;
+  if (cache) {
+    for (int i = threadIdx.x; i <= a.B; i += kThreads) {
+      if (a.tree) {
+        if (i < a.B) {
+          s_i[i] = a.n_nodes ? a.n_nodes[i] : a.N;
+          s_f0[i] = a.temp_a[i];
+        }
+      } else {
+        s_i[i] = a.offsets[i];
+        if (i < a.B) {
+          s_f0[i] = a.temp_a[i];
+          s_f1[i] = a.temp_b[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (u >= total) return;
+
+  // Whether a row's partials are needed (tree rows past n_nodes are not).
+  auto row_used = [&](uint32_t r) -> bool {
+    if (!a.tree) return true;
+    const uint32_t b = r / (uint32_t)a.N;
+    const int node = (int)(r - b * (uint32_t)a.N);
+    const int nn = cache ? s_i[b] : (a.n_nodes ? a.n_nodes[b] : a.N);
+    return node < nn;
+  };
+  auto row_temp = [&](uint32_t r) -> float {
+    if (a.tree) {
+      const uint32_t b = r / (uint32_t)a.N;
+      return cache ? s_f0[b] : a.temp_a[b];
+    }
+    if (r < a.n_a) {
+      if (cache) return s_f0[wave_find_batch_row(s_i, a.B, r, 1)];
+      return a.temp_a[wave_find_batch_row(a.offsets, a.B, r, 1)];
+    }
+    const long long x = (long long)r - a.n_a;
+    if (cache) return s_f1[wave_find_batch_row(s_i, a.B, x, 0)];
+    return a.temp_b[wave_find_batch_row(a.offsets, a.B, x, 0)];
+  };
+  auto advance = [&](uint32_t& r, uint32_t& c) {
+    c += Gr;
+    r += Gq;
+    if (c >= nc) {
+      c -= nc;
+      ++r;
+    }
+  };
+  auto chunk_begin = [&](uint32_t c, float T, bool& greedy, float& k2) {
+    greedy = T == 0.0f;
+    k2 = greedy ? 0.0f : log2e_over_t(T);
+    return LaneStats{-__builtin_huge_valf(), (int)c * kChunk + lane * SegLoad<DT>::EPV, 0.0};
+  };
+  auto chunk_end = [&](uint32_t r, uint32_t c, bool ok, bool greedy, const LaneStats& st) {
+    // a bad temperature is reported by the finish pass
+    const Partial p = ok ? wave_combine(st, greedy) : Partial{0.0f, 0, 0.0};
+    if (lane == 0) a.part[(long long)r * nc + c] = p;
+  };
+
+  if (!a.vec_ok) {                        // unaligned rows: plain loads, no prefetch
+    for (; u < total; u += G, advance(row, ch)) {
+      if (!row_used(row)) continue;
+      const float T = row_temp(row);
+      const bool ok = temp_ok(T);
+      bool greedy;
+      float k2;
+      LaneStats st = chunk_begin(ch, T, greedy, k2);
+      if (ok) {
+        for (int k = 0; k < kSubs; ++k) {
+          float v[kPerLane];
+          const int seg0 = (int)ch * kChunk + k * kSubSpan;
+          seg_load_scalar<DT>(row_ptr(row), V, seg0, v);
+          lane_fold<DT>(v, seg0, greedy, k2, st);
+        }
+      }
+      chunk_end(row, ch, ok, greedy, st);
+    }
+    return;
+  }
+
+  bool used = row_used(row);
+  float T = used ? row_temp(row) : 0.0f;
+  for (;;) {
+    uint32_t row1 = row, ch1 = ch;
+    advance(row1, ch1);
+    const bool has1 = u + G < total;
+    const bool used1 = has1 && row_used(row1);
+    const float T1 = used1 ? row_temp(row1) : 0.0f;
+    const char* p0 = row_ptr(row);
+    const char* p1 = row_ptr(row1);
+    const bool ok = used && temp_ok(T);
+    bool greedy;
+    float k2;
+    LaneStats st = chunk_begin(ch, T, greedy, k2);
+#pragma unroll
+    for (int k = 0; k < kSubs; ++k) {
+      SegLoad<DT>& cur = ring[k % RING];
+      const int seg0 = (int)ch * kChunk + k * kSubSpan;
+      if (ok) {
+        float v[kPerLane];
+        cur.unpack(v);
+        lane_fold<DT>(v, seg0, greedy, k2, st);
+      }
+      // refill this slot with the sub-segment RING ahead
+      const int kn = k + RING;
+      if (kn < kSubs) {
+        if (used) cur.issue(p0, V, (int)ch * kChunk + kn * kSubSpan);
+      } else if (used1) {
+        cur.issue(p1, V, (int)ch1 * kChunk + (kn - kSubs) * kSubSpan);
+      }
+    }
+    if (used) chunk_end(row, ch, ok, greedy, st);
+    if (!has1) break;
+    u += G;
+    row = row1;
+    ch = ch1;
+    used = used1;
+    T = T1;
+  }
+}
+// ---------------------------------------------------------------------------
+// Raw Philox words (diagnostic entry point).
+
+__global__ __launch_bounds__(kThreads) void philox_words_kernel(uint64_t seed, uint64_t step,
+                                                                const uint32_t* row_ids,
+                                                                int n_rows, int n_slots,
+                                                                uint32_t* out) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (long long)n_rows * n_slots) return;
+  const int r = (int)(i / n_slots), s = (int)(i - (long long)r * n_slots);
+  const uint4 w = verify_words(seed, step, row_ids ? row_ids[r] : (uint32_t)r, (uint32_t)s);
+  uint4* o = (uint4*)(out + i * 4);
+  *o = w;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+
+// Chunks per stats work item: one while a single round of work items fills
+// the GPU (short critical path), two beyond (more loads in flight per item).
+long long stats_items(long long n_rows, int n_chunks) {
+  return n_rows * n_chunks * kPartsPerChunk;
+}
+
+static int stats_resident_blocks(int dt, int ring) {
+  if (dt == 1)
+    return ring == 4 ? resident_blocks(0, stats_kernel<1, 4>, kThreads)
+                     : resident_blocks(1, stats_kernel<1, 2>, kThreads);
+  return resident_blocks(2, stats_kernel<0, 2>, kThreads);
+}
+
+// Pass 1.  Launched with events, the events bracket the kernel's dispatch.
+hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_t ev_start,
+                        hipEvent_t ev_stop) {
+  const long long units = stats_items(a.n_rows, a.n_chunks);
+  if (units <= 0) return hipSuccess;
+  const int dt = dtype == 1 ? 1 : 0;
+  const bool timed = ev_start && ev_stop;
+  const dim3 block(kThreads);
+#define SV_LAUNCH(K)                                                          \
+  do {                                                                        \
+    if (timed) hipExtLaunchKernelGGL(K, grid, block, 0, st, ev_start, ev_stop, 0, a); \
+    else K<<<grid, block, 0, st>>>(a);                                        \
+  } while (0)
+  const long long want = (units + kWaves - 1) / kWaves;
+  // a whole chunk in flight per wave when one round of waves covers the call
+  const int ring = (dt == 1 && want <= stats_resident_blocks(1, 4)) ? 4 : 2;
+  const dim3 grid((unsigned)(std::min<long long>(want, stats_resident_blocks(dt, ring)) +
+                             gather_blocks(a)));
+  if (dt == 1 && ring == 4) SV_LAUNCH((stats_kernel<1, 4>));
+  else if (dt == 1) SV_LAUNCH((stats_kernel<1, 2>));
+  else SV_LAUNCH((stats_kernel<0, 2>));
+#undef SV_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids,
+                               int n_rows, int n_slots, uint32_t* out, hipStream_t st) {
+  const long long n = (long long)n_rows * n_slots;
+  const long long blocks = (n + kThreads - 1) / kThreads;
+  philox_words_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(seed, step, row_ids,
+                                                                         n_rows, n_slots, out);
+  return hipGetLastError();
+}
+
+}  // namespace sv
