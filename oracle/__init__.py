@@ -25,5 +25,5 @@ from .philox import philox4x32_10, verify_uniforms  # noqa: F401
 from .decode import decode_logits, bf16_bits_to_f64  # noqa: F401
 from .linear import verify_linear, verify_linear_row, LinearRowResult  # noqa: F401
 from .tree import (verify_tree_topk, verify_tree_topk_row,  # noqa: F401
-                   verify_tree_sampled_wor_row, TreeRowResult)
+                   verify_tree_sampled_wor, verify_tree_sampled_wor_row, TreeRowResult)
 from .attention import verify_attention, attention_head, ancestor_mask  # noqa: F401

@@ -35,7 +35,7 @@ import numpy as np
 
 from .decode import decode_logits
 from .linear import (FLAG_EPS, ROW_BAD_SHAPE, ROW_BAD_TEMP, ROW_BAD_TOKEN, ROW_NONFINITE,
-                     ROW_OK, ROW_WARN_RZERO, inverse_cdf, softmax_t)
+                     ROW_OK, ROW_WARN_QZERO, ROW_WARN_RZERO, inverse_cdf, softmax_t)
 from .philox import verify_uniforms
 
 TREE_TOPK = 0
@@ -150,6 +150,13 @@ def verify_tree_sampled_wor_row(x, y, parents, node_tokens, n_nodes, temp_t, tem
     if st == ROW_OK and (not (np.isfinite(temp_t) and np.isfinite(temp_d))
                          or temp_t < 0 or temp_d < 0):
         st = ROW_BAD_TEMP
+    if st == ROW_OK:
+        # every distribution the walk may read must exist: the target row of
+        # each node, the draft row of each node that has children
+        inner = sorted({parents[c] for c in range(1, n_nodes)})
+        if not (np.all(np.isfinite(np.max(x[:n_nodes], axis=1)))
+                and all(np.isfinite(np.max(y[n])) for n in inner)):
+            st = ROW_NONFINITE
     if st != ROW_OK:
         return TreeRowResult(-1, path, out, p_at, st, None, False, -1, "error")
 
@@ -169,6 +176,9 @@ def verify_tree_sampled_wor_row(x, y, parents, node_tokens, n_nodes, temp_t, tem
             if qj[tok] > 0:
                 ratio = pj[tok] / qj[tok]
             else:
+                # a sampled child the draft could not have drawn (as in the
+                # linear verify: the ratio is +inf, or 0 when p is 0 too)
+                status |= ROW_WARN_QZERO
                 ratio = np.inf if pj[tok] > 0 else 0.0
             if flagged is None and abs(u_acc[c] - ratio) < FLAG_EPS:
                 flagged = depth
@@ -219,6 +229,39 @@ def verify_tree_topk(target_logits, dtype, parents, node_tokens, n_nodes, temp_t
         u_acc, u_smp = verify_uniforms(seed, step, rid, N)
         r = verify_tree_topk_row(x, parents[b], node_tokens[b], nn, float(temp_target[b]),
                                  u_acc, u_smp)
+        results.append(r)
+        num_acc[b] = r.num_accepted
+        path_nodes[b] = r.path_nodes
+        out_tokens[b] = r.out_tokens
+        p_at[b] = r.p_at_node
+        status[b] = r.status
+    return num_acc, path_nodes, out_tokens, p_at, status, results
+
+
+def verify_tree_sampled_wor(target_logits, draft_logits, dtype, parents, node_tokens, n_nodes,
+                            temp_target, temp_draft, seed=0, step=0, row_ids=None):
+    """Batch SAMPLED_WOR verify.  target_logits, draft_logits: [B, N, V] as stored.
+
+    Returns the same tuple as :func:`verify_tree_topk`.
+    """
+    parents = np.asarray(parents)
+    node_tokens = np.asarray(node_tokens)
+    B, N = parents.shape
+    num_acc = np.full(B, -1, dtype=np.int64)
+    path_nodes = np.full((B, N - 1), -1, dtype=np.int64)
+    out_tokens = np.full((B, N), -1, dtype=np.int64)
+    p_at = np.zeros((B, N))
+    status = np.zeros(B, dtype=np.int64)
+    results = []
+    for b in range(B):
+        nn = N if n_nodes is None else int(n_nodes[b])
+        x = decode_logits(target_logits[b], dtype)
+        y = decode_logits(draft_logits[b], dtype)
+        rid = b if row_ids is None else int(row_ids[b])
+        u_acc, u_smp = verify_uniforms(seed, step, rid, N)
+        r = verify_tree_sampled_wor_row(x, y, parents[b], node_tokens[b], nn,
+                                        float(temp_target[b]), float(temp_draft[b]),
+                                        u_acc, u_smp)
         results.append(r)
         num_acc[b] = r.num_accepted
         path_nodes[b] = r.path_nodes

@@ -224,6 +224,59 @@ def test_chain_tree_equals_linear_with_greedy_draft():
     assert len(set(depths)) >= 4
 
 
+def test_sampled_wor_chain_equals_linear_with_draft_q():
+    """A chain has one child per node, so q_j = q and p_j = p at every test:
+    SAMPLED_WOR reduces to the linear verify with the draft's own q."""
+    rng = np.random.default_rng(44)
+    gamma, V = 5, 48
+    depths = []
+    for trial in range(80):
+        x = rng.normal(0, 1.5, size=(gamma + 1, V))
+        y = x[:gamma] + rng.normal(0, 0.4, size=(gamma, V))
+        Tt, Td = [(1.0, 1.0), (0.8, 1.2), (1.3, 0.6), (0.0, 1.0)][trial % 4]
+        d = np.array([rng.choice(V, p=lib_softmax(y[i], Td)) for i in range(gamma)])
+        yt = np.vstack([y, rng.normal(0, 1.5, size=(1, V))])   # the leaf's draft row is unused
+        parents = [-1] + list(range(gamma))
+        tokens = [0] + list(d)
+        u_acc, u_smp = oracle.verify_uniforms(trial, 3, 7, gamma + 1)
+        lin = L.verify_linear_row(x, y, d, Tt, Td, u_acc, u_smp)
+        tr = TR.verify_tree_sampled_wor_row(x, yt, parents, tokens, gamma + 1, Tt, Td,
+                                            u_acc, u_smp)
+        assert lin.num_accepted == tr.num_accepted
+        if not tr.flagged_sample:
+            assert np.array_equal(lin.out_tokens, tr.out_tokens)
+        assert list(tr.path_nodes[:tr.num_accepted]) == list(range(1, tr.num_accepted + 1))
+        for i in range(gamma):
+            assert tr.p_at_node[i + 1] == lin.p_at_draft[i]
+        depths.append(tr.num_accepted)
+    assert len(set(depths)) >= 4
+
+
+def test_sampled_wor_error_and_warning_rows():
+    V = 6
+    x = np.zeros((4, V))
+    y = np.zeros((4, V))
+    u = [0.5] * 4
+    par, tok = [-1, 0, 0, 1], [0, 1, 2, 3]
+    run = TR.verify_tree_sampled_wor_row
+    assert run(x, y, par, tok, 4, 1.0, -1.0, u, u).status == L.ROW_BAD_TEMP
+    assert run(x, y, [-1, 0, 3, 1], tok, 4, 1.0, 1.0, u, u).status == L.ROW_BAD_SHAPE
+    assert run(x, y, par, [0, 1, 2, V], 4, 1.0, 1.0, u, u).status == L.ROW_BAD_TOKEN
+    xb = x.copy()
+    xb[3] = -np.inf          # a leaf's target row is read by its bonus draw
+    assert run(xb, y, par, tok, 4, 1.0, 1.0, u, u).status == L.ROW_NONFINITE
+    yb = y.copy()
+    yb[1] = -np.inf          # node 1 has a child, so its draft row is read
+    assert run(x, yb, par, tok, 4, 1.0, 1.0, u, u).status == L.ROW_NONFINITE
+    yb = y.copy()
+    yb[2] = -np.inf          # leaves' draft rows are never read
+    assert run(x, yb, par, tok, 4, 1.0, 1.0, u, u).status == L.ROW_OK
+    yq = y.copy()
+    yq[0, 1] = -np.inf       # child token 1 impossible under the root's draft
+    r = run(x, yq, par, tok, 4, 1.0, 1.0, [0.5, 0.999, 0.999, 0.999], u)
+    assert r.status & L.ROW_WARN_QZERO and r.num_accepted >= 1 and r.path_nodes[0] == 1
+
+
 def test_greedy_tree_accepts_target_argmax_child():
     rng = np.random.default_rng(41)
     V = 16
