@@ -74,7 +74,7 @@ extern "C" {
 
 /* Tree candidate modes. */
 #define SV_TREE_TOPK 0        /* children are the draft's deterministic top-k */
-#define SV_TREE_SAMPLED_WOR 1 /* children drawn from q without replacement (not built yet) */
+#define SV_TREE_SAMPLED_WOR 1 /* children drawn from q without replacement */
 
 /* Per-row status bits.  Bits 0-7 are errors, bits 8+ are warnings. */
 #define SV_ROW_OK 0
@@ -82,7 +82,7 @@ extern "C" {
 #define SV_ROW_BAD_SHAPE 2      /* bad offsets (gamma_b < 0 or > 64) or parents / n_nodes */
 #define SV_ROW_NONFINITE 4      /* a logit row without a finite maximum */
 #define SV_ROW_BAD_TEMP 8       /* negative or non-finite temperature */
-#define SV_ROW_WARN_QZERO 256   /* q(d) = 0 for a draft token (ratio taken as +inf or 0) */
+#define SV_ROW_WARN_QZERO 256   /* q(d) = 0 for a tested draft token (ratio taken as +inf or 0) */
 #define SV_ROW_WARN_RZERO 512   /* rejection with zero residual mass: drew from p instead */
 
 #define SV_MAX_GAMMA 64
@@ -151,24 +151,43 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
  * rejected the emitted token is drawn from p with all of them removed; at a
  * leaf the bonus token is drawn from p (draws use u_smp of the stop node).
  *
+ * SAMPLED_WOR mode (the tree-attention paragraph's temperature-sampled
+ * children): the children of a node were drawn from its draft distribution
+ * q without replacement.  Child c_j is accepted when
+ * u_acc(c_j) < p_j(c_j) / q_j(c_j), where q_j is q with the tokens of
+ * c_1..c_{j-1} removed and renormalised, p_1 = p, and each rejection sets
+ * p_{j+1} = norm(max(0, p_j - q_j)) (left as p_j when that is empty,
+ * SV_ROW_WARN_RZERO); when every child is rejected the token is drawn from
+ * the last p_{k+1}; at a leaf the bonus is drawn from p.  A tested child
+ * with q_j(c_j) = 0 sets SV_ROW_WARN_QZERO (ratio +inf, or 0 if p_j is 0 too).
+ * Each rejected sibling costs one extra pass over its node's two rows.
+ *
  *   target_logits  [B, N, V] `dtype`; row n is the target's distribution for
  *                  the token that follows node n (node 0 = root = the last
  *                  committed token).
- *   draft_logits   [B, N, V] or NULL; read only by SV_TREE_SAMPLED_WOR.
+ *   draft_logits   [B, N, V] `dtype`, SAMPLED_WOR only (else may be NULL):
+ *                  row n is the draft distribution that n's children were
+ *                  drawn from; rows of nodes without children are not read.
  *   N              nodes per tree including the root, 1..64.
  *   parents        [B, N] int32; parents[b][0] is ignored; for 0 < i <
  *                  n_nodes[b], 0 <= parents[b][i] < i.
  *   node_tokens    [B, N] int32; node 0's entry is ignored.
  *   n_nodes        [B] int32 in 1..N, or NULL for N everywhere.
- *   cand_mode      SV_TREE_TOPK (SV_TREE_SAMPLED_WOR returns SV_ERR_UNSUPPORTED).
- *   temp_target    [B]; temp_draft [B] or NULL (read by SAMPLED_WOR only).
+ *   cand_mode      SV_TREE_TOPK or SV_TREE_SAMPLED_WOR; any other value is
+ *                  SV_ERR_INVALID_ARG, as is SAMPLED_WOR without draft_logits
+ *                  or temp_draft.
+ *   temp_target    [B]; temp_draft [B] (SAMPLED_WOR; else may be NULL).
+ *                  Every target row n < n_nodes[b], and the draft row of
+ *                  every node with a child, needs a finite maximum
+ *                  (SV_ROW_NONFINITE otherwise).
  * Outputs:
  *   num_accepted   [B] depth of the accepted path, -1 for an error row.
  *   path_nodes     [B, N-1] node ids of the accepted path, then -1.
  *   out_tokens     [B, N] tokens of the accepted path, then the drawn token, then -1.
  *   p_at_node      [B, N] p_parent(n)(token_n) for 0 < n < n_nodes, else 0; may be NULL.
  *   row_status     [B]; may be NULL.
- *   workspace      spec_verify_tree_workspace_size() bytes, as for the linear call.
+ *   workspace      spec_verify_tree_workspace_size() bytes (enough for either
+ *                  mode), as for the linear call.
  */
 size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype);
 int spec_verify_tree(const void* target_logits, const void* draft_logits, int dtype,

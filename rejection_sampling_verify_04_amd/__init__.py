@@ -170,13 +170,21 @@ def verify_tree(target_logits, parents, node_tokens, temp_target, n_nodes=None, 
                 row_ids=None, cand_mode=SV_TREE_TOPK, draft_logits=None, temp_draft=None,
                 want_probs=True, workspace=None, outputs=None, stream=None):
     """Tree verify (see spec_verify_tree).  target_logits [B, N, V]; parents,
-    node_tokens [B, N] int32; n_nodes [B] int32 or None."""
+    node_tokens [B, N] int32; n_nodes [B] int32 or None.  SV_TREE_SAMPLED_WOR
+    also takes draft_logits (same shape and dtype) and temp_draft [B]."""
     L = library()
     _dev(target_logits, "target_logits")
     dt = _logit_code(target_logits, "target_logits")
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, N, V]")
     B, N, V = target_logits.shape
+    if cand_mode == SV_TREE_SAMPLED_WOR:
+        if draft_logits is None or temp_draft is None:
+            raise ValueError("SV_TREE_SAMPLED_WOR needs draft_logits and temp_draft")
+        _dev(draft_logits, "draft_logits")
+        if draft_logits.dtype != target_logits.dtype or draft_logits.shape != target_logits.shape:
+            raise ValueError("draft_logits must match target_logits in shape and dtype")
+        _dev(temp_draft, "temp_draft", torch.float32)
     _dev(parents, "parents", torch.int32)
     _dev(node_tokens, "node_tokens", torch.int32)
     _dev(temp_target, "temp_target", torch.float32)

@@ -150,10 +150,12 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   return SV_OK;
 }
 
+// Sized for either candidate mode (SAMPLED_WOR keeps the draft rows' partials
+// and gathers too).
 size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype) {
   (void)dtype;
   if (B < 0 || N < 1 || V < 1) return 0;
-  return layout((long long)B * N, B, V, (long long)B * N, false).total;
+  return layout(2LL * B * N, B, V, 2LL * B * N, false).total;
 }
 
 int spec_verify_tree(const void* target_logits, const void* draft_logits, int dtype, int B,
@@ -163,31 +165,32 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
                      const uint32_t* row_ids, int32_t* num_accepted, int32_t* path_nodes,
                      int32_t* out_tokens, float* p_at_node, int32_t* row_status,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)draft_logits;
-  (void)temp_draft;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
   if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1) return SV_ERR_INVALID_ARG;
-  if (cand_mode == SV_TREE_SAMPLED_WOR) return SV_ERR_UNSUPPORTED;
-  if (cand_mode != SV_TREE_TOPK) return SV_ERR_INVALID_ARG;
+  if (cand_mode != SV_TREE_TOPK && cand_mode != SV_TREE_SAMPLED_WOR) return SV_ERR_INVALID_ARG;
+  const bool wor = cand_mode == SV_TREE_SAMPLED_WOR;
   if (B == 0) return SV_OK;
   if (n_chunks_for(V) > sv::kMaxChunks) return SV_ERR_UNSUPPORTED;
   if (!target_logits || !parents || !node_tokens || !temp_target || !num_accepted ||
       !path_nodes || !out_tokens)
     return SV_ERR_INVALID_ARG;
-  const long long n_rows = (long long)B * N;
+  if (wor && (!draft_logits || !temp_draft)) return SV_ERR_INVALID_ARG;
+  const long long n_nodes_all = (long long)B * N;
+  const long long n_rows = wor ? 2 * n_nodes_all : n_nodes_all;
   const int nc = n_chunks_for(V);
   if (sv::stats_items(n_rows, nc) >= (1LL << 31)) return SV_ERR_INVALID_ARG;
   const Layout l = layout(n_rows, B, V, n_rows, false);
   const int wst = check_workspace(workspace, workspace_bytes, l.total);
   if (wst != SV_OK) return wst;
   const int es = dtype == SV_BF16 ? 2 : 4;
-  const int vec_ok = ((long long)V * es) % 16 == 0 && aligned16(target_logits);
+  const int vec_ok = ((long long)V * es) % 16 == 0 && aligned16(target_logits) &&
+                     (!wor || aligned16(draft_logits));
   char* ws = (char*)workspace;
 
   sv::StatsArgs s{};
   s.rows_a = target_logits;
-  s.rows_b = nullptr;
-  s.n_a = n_rows;
+  s.rows_b = wor ? draft_logits : nullptr;
+  s.n_a = n_nodes_all;
   s.n_rows = n_rows;
   s.V = V;
   s.n_chunks = nc;
@@ -197,7 +200,7 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
   s.N = N;
   s.n_nodes = n_nodes;
   s.temp_a = temp_target;
-  s.temp_b = temp_target;
+  s.temp_b = wor ? temp_draft : temp_target;
   s.part = (sv::Partial*)(ws + l.part);
   s.vec_ok = vec_ok;
   s.tokens = node_tokens;
@@ -208,6 +211,8 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
 
   sv::TreeArgs f{};
   f.target = target_logits;
+  f.draft = wor ? draft_logits : nullptr;
+  f.mode = wor ? 1 : 0;
   f.V = V;
   f.n_chunks = nc;
   f.B = B;
@@ -216,6 +221,7 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int dt
   f.tokens = node_tokens;
   f.n_nodes = n_nodes;
   f.temp = temp_target;
+  f.temp_d = wor ? temp_draft : temp_target;
   f.seed = seed;
   f.step = step;
   f.row_ids = row_ids;

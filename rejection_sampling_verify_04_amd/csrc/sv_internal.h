@@ -14,12 +14,12 @@ namespace sv {
 struct Partial;
 
 struct StatsArgs {
-  const void* rows_a;    // target rows (linear) or all node rows (tree)
-  const void* rows_b;    // draft rows (linear) or null
+  const void* rows_a;    // target rows (linear) or the node rows [B N] (tree)
+  const void* rows_b;    // draft rows (linear, SAMPLED_WOR tree) or null
   long long n_a;         // rows in rows_a
   long long n_rows;      // rows_a + rows_b
   int V, n_chunks;
-  int tree;              // 0: linear (temperatures via offsets), 1: tree (row / N)
+  int tree;              // 0: linear (temperatures via offsets), 1: tree (node row / N)
   const int* offsets;
   int B;
   int N;
@@ -29,7 +29,8 @@ struct StatsArgs {
   Partial* part;         // [n_rows][n_chunks]
   int vec_ok;            // 16-byte vector loads are valid for every row
   // Logits gathered at the draft tokens: linear, x_i[d_i] at [i] and y_i[d_i]
-  // at [total_draft + i]; tree, node n's token under its parent at [b N + n].
+  // at [total_draft + i]; tree, node n's token under its parent at [b N + n]
+  // (target) and [B N + b N + n] (draft rows, when present).
   const int* tokens;
   const int* parents;
   int total_draft;
@@ -70,15 +71,18 @@ struct LinearArgs {
 
 struct TreeArgs {
   const void* target;
+  const void* draft;     // SAMPLED_WOR: draft rows [B N]
+  int mode;              // 0: TOPK, 1: SAMPLED_WOR
   int V, n_chunks, B, N;
   const int* parents;
   const int* tokens;
   const int* n_nodes;
   const float* temp;
+  const float* temp_d;   // SAMPLED_WOR: draft temperatures
   uint64_t seed, step;
   const uint32_t* row_ids;
-  const Partial* part;
-  const float* gath;     // logit of each node's token under its parent
+  const Partial* part;    // [B N] target rows, then (SAMPLED_WOR) [B N] draft rows
+  const float* gath;     // logit of each node's token under its parent (target, then draft)
   int* num_accepted;
   int* path_nodes;
   int* out_tokens;

@@ -100,6 +100,7 @@ __device__ __forceinline__ void seg_load_scalar(const char* rowp, int V, int seg
 }
 
 constexpr int kStatsCache = 1024;  // batch rows whose offsets/temperatures go to LDS
+constexpr int kInnerCache = 512;   // trees whose inner-node masks go to LDS (draft rows read)
 
 // Largest j in [0, B) whose key off[j] + add * j is <= x, found by one wave
 // with 64 probes per round (B <= 64: one round; B <= 4096: two).
@@ -141,7 +142,8 @@ __host__ __device__ inline int gather_blocks(const StatsArgs& a) {
 
 // gath[i] = logit of item i's token: linear, x_i[d_i] at [i] and y_i[d_i]
 // at [total_draft + i] (target row i + b for position i of batch row b,
-// draft row i); tree, node j's token under its parent row at [j].  Tokens
+// draft row i); tree, node j's token under its parent's target row at [j]
+// and, with draft rows, under its parent's draft row at [B N + j].  Tokens
 // and parents outside their range read index 0 (the finish pass flags them).
 template <int DT>
 __device__ void gather_logits(const StatsArgs& a, int* s_off) {
@@ -160,6 +162,7 @@ __device__ void gather_logits(const StatsArgs& a, int* s_off) {
     const int par = a.parents[it];
     const long long xr = it - it % a.N + ((par >= 0 && par < a.N) ? par : 0);
     a.gath[it] = load_logit<DT>(a.rows_a, xr * V + tc);
+    if (a.rows_b) a.gath[n + it] = load_logit<DT>(a.rows_b, xr * V + tc);
   } else {
     const int b = cache ? lane_batch_row(s_off, a.B, it) : lane_batch_row(a.offsets, a.B, it);
     a.gath[it] = load_logit<DT>(a.rows_a, (it + b) * V + tc);
@@ -235,6 +238,7 @@ template <int DT, int RING>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   __shared__ int s_i[kStatsCache + 1];
   __shared__ float s_f0[kStatsCache], s_f1[kStatsCache];
+  __shared__ unsigned long long s_inner[kInnerCache];   // tree b: bit n set if node n has a child
 
   const int V = a.V;
   // The first work items gather the logits at the draft tokens; being
@@ -269,12 +273,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
 
   const bool cache = a.B <= kStatsCache;
+  // Tree draft rows are read only for nodes with children.
+  const bool tree_q = a.tree && a.rows_b;
+  const bool cache_inner = tree_q && a.B <= kInnerCache;
   if (cache) {
     for (int i = threadIdx.x; i <= a.B; i += kThreads) {
       if (a.tree) {
         if (i < a.B) {
           s_i[i] = a.n_nodes ? a.n_nodes[i] : a.N;
           s_f0[i] = a.temp_a[i];
+          s_f1[i] = a.temp_b[i];
+          if (cache_inner) s_inner[i] = 0ull;
         }
       } else {
         s_i[i] = a.offsets[i];
@@ -285,20 +294,39 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       }
     }
     __syncthreads();
+    if (cache_inner) {
+      const int N = a.N;
+      for (int i = threadIdx.x; i < a.B * N; i += kThreads) {
+        const int b = i / N, c = i - b * N;
+        const int par = a.parents[i];
+        if (c > 0 && c < s_i[b] && par >= 0 && par < c) atomicOr(&s_inner[b], 1ull << par);
+      }
+      __syncthreads();
+    }
   }
   if (u >= total) return;
 
-  // Whether a row's partials are needed (tree rows past n_nodes are not).
+  // Whether a row's partials are needed: tree rows past n_nodes are not, nor
+  // the draft rows of nodes without children.  Called by whole waves.
   auto row_used = [&](uint32_t r) -> bool {
     if (!a.tree) return true;
-    const uint32_t b = r / (uint32_t)a.N;
-    const int node = (int)(r - b * (uint32_t)a.N);
+    const bool is_q = r >= a.n_a;
+    const uint32_t x = is_q ? r - (uint32_t)a.n_a : r;
+    const uint32_t b = x / (uint32_t)a.N;
+    const int node = (int)(x - b * (uint32_t)a.N);
     const int nn = cache ? s_i[b] : (a.n_nodes ? a.n_nodes[b] : a.N);
-    return node < nn;
+    if (node >= nn) return false;
+    if (!is_q) return true;
+    if (cache_inner) return ((s_inner[b] >> node) & 1ull) != 0ull;
+    const int c = lane;
+    const bool kid = c > node && c < nn && a.parents[(long long)b * a.N + c] == node;
+    return __ballot(kid) != 0ull;
   };
   auto row_temp = [&](uint32_t r) -> float {
     if (a.tree) {
-      const uint32_t b = r / (uint32_t)a.N;
+      const bool is_q = r >= a.n_a;
+      const uint32_t b = (is_q ? r - (uint32_t)a.n_a : r) / (uint32_t)a.N;
+      if (is_q) return cache ? s_f1[b] : a.temp_b[b];
       return cache ? s_f0[b] : a.temp_a[b];
     }
     if (r < a.n_a) {

@@ -1,10 +1,15 @@
-// Finish pass of the tree verify, gfx950: one work item per tree walks it
-// with one lane per node and draws in one chunk of the stop row.
+// Finish passes of the tree verify, gfx950: one work item per tree.
+//   TOPK          tree_kernel walks the tree with one lane per node and draws
+//                 in one chunk of the stop row.
+//   SAMPLED_WOR   tree_wor_kernel walks it with the whole block: one
+//                 vocabulary pass over the node's target and draft rows per
+//                 rejected sibling, then the draw.
 //
-// Sources: tree walk over top-k siblings (kwkr.cn/news/620872 §5.3;
-// blog.lonae.com/posts/2026-draft-model-kv-jDwzYp, tree-attention
-// paragraphs); acceptance rule and residual draw as in the linear verify
-// (kwkr §2.3, §4.1; lonae formal-definition paragraph).
+// Sources: tree walk over siblings drawn by top-k or by temperature sampling
+// (kwkr.cn/news/620872 §5.3; blog.lonae.com/posts/
+// 2026-draft-model-kv-jDwzYp, tree-attention paragraphs); acceptance rule
+// and residual draw as in the linear verify (kwkr §2.3, §4.1; lonae
+// formal-definition paragraph).
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -239,11 +244,488 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Tree verify (SAMPLED_WOR): the children of a node were drawn from the
+// draft's q without replacement.  Child j is tested against p_j and q_j,
+// where q_j is q without the tokens of the rejected siblings (renormalised);
+// each rejection replaces p_j by the normalised residual max(0, p_j - q_j).
+//
+// No residual is ever stored.  With a = p(v) and b = q(v), every p_j has the
+// form max(0, a - L_v b) / P: L_v = lambda for tokens still in q_j, and the
+// value lambda took when a rejected sibling's token left q (it leaves with
+// the residual taken at its own test).  Rejecting child j with
+// Q = q's mass left in q_j sets mu = lambda + P / Q and
+// G = sum_v max(0, a - L'_v b), L'_v = mu for tokens still in q_j; then
+// lambda = mu and P = G (both unchanged when G = 0: the residual is empty).
+// One vocabulary pass over the node's two rows forms G per chunk and the
+// draft mass that stays after t_j leaves, so a walk costs one pass per
+// rejected sibling, plus the draw.  When every child is rejected, the
+// draw's weights are the last pass's, and its chunk masses are reused.
+
+// The rows of one tree node as the SAMPLED_WOR passes read them, with
+// p(v) = 2^(x p_k - p_c) p_inv_s + [v = p_amax] (and q likewise): a sampled
+// row has p_amax = -1; a greedy one has p_k = 1, p_c = +inf, p_inv_s = 0,
+// so that the exponential term is 0 (its x is finite or -inf: rows with a
+// +inf logit are reported before any pass).  An unread draft row has every
+// q term 0.  Every field is uniform over the block.
+struct WorDist {
+  const char* xrow;      // target row of the node
+  const char* yrow;      // draft row of the node (the target row when unread)
+  float p_k, p_c, p_inv_s;
+  int p_amax;
+  float q_k, q_c, q_inv_s;
+  int q_amax;
+};
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ __forceinline__ double uni(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const unsigned long long lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const unsigned long long hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+// lambda as the float32 weights use it (finite: -lambda * 0 must stay 0).
+__device__ __forceinline__ float lam_f32(double lam) { return uni((float)fmin(lam, 3.0e38)); }
+
+// The node's distributions; `use_q` = 0 leaves q at 0 (bonus draw at a leaf).
+__device__ __forceinline__ WorDist wor_dist(const char* xrow, const char* yrow, const RowStats& ps,
+                                            const RowStats& qs, bool gt, bool gd, float kt,
+                                            float kd, bool use_q) {
+  const float inf = __builtin_huge_valf();
+  WorDist d;
+  d.xrow = xrow;
+  d.yrow = use_q ? yrow : xrow;
+  d.p_k = uni(gt ? 1.0f : kt);
+  d.p_c = uni(gt ? inf : ps.c);
+  d.p_inv_s = uni(gt ? 0.0f : (float)ps.inv_s);
+  d.p_amax = uni(gt ? ps.amax : -1);
+  const bool qe = use_q && !gd;   // sampled draft term
+  d.q_k = uni(qe ? kd : 1.0f);
+  d.q_c = uni(qe ? qs.c : inf);
+  d.q_inv_s = uni(qe ? (float)qs.inv_s : 0.0f);
+  d.q_amax = uni((use_q && gd) ? qs.amax : -1);
+  return d;
+}
+
+constexpr int kWorGroup = 2;   // chunks whose loads are in flight together
+
+
+// This thread's 16-byte loads of one chunk of both rows (VEC: V a multiple
+// of the vector width and rows 16-byte aligned; addresses clamped into the
+// row past V).
+template <int DT, bool VEC>
+__device__ __forceinline__ void wor_load(const WorDist& d, int V, int chunk, StopVec<DT>& r) {
+  if (!VEC) return;   // the weights load element by element
+  constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV;
+  const int e0 = chunk * kChunk + threadIdx.x * kPerThread;
+#pragma unroll
+  for (int j = 0; j < StopVec<DT>::NV; ++j) {
+    const int ej = e0 + j * EPV;
+    const long long off = ej < V ? (long long)ej * ES : 0;
+    r.p[j] = *(const uint4*)(d.xrow + off);
+    r.q[j] = *(const uint4*)(d.yrow + off);
+  }
+}
+
+// Weights of this thread's 8 elements of `chunk`: w = max(0, a - L b), with
+// L = lam or, for the tokens in ex_tok, their own ex_lam; be = b outside
+// ex_tok and t_cur (WANT_E only).  Both are 0 past V.  Every pass and the
+// draw form weights through this code.
+template <int DT, bool VEC, bool WANT_E>
+__device__ __forceinline__ void wor_weights(const WorDist& d, int V, int chunk,
+                                            const StopVec<DT>& r, float lam, const int* ex_tok,
+                                            const float* ex_lam, int nex, int t_cur,
+                                            float w[kPerThread], float be[kPerThread]) {
+  constexpr int EPV = StopVec<DT>::EPV;
+  const int e0 = chunk * kChunk + threadIdx.x * kPerThread;
+  float xp[kPerThread], xq[kPerThread];
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < StopVec<DT>::NV; ++j) {
+      const uint32_t rw[4] = {r.p[j].x, r.p[j].y, r.p[j].z, r.p[j].w};
+      const uint32_t sw[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (DT == 1) {
+          xp[j * 8 + 2 * h] = bf16_lo(rw[h]);
+          xp[j * 8 + 2 * h + 1] = bf16_hi(rw[h]);
+          xq[j * 8 + 2 * h] = bf16_lo(sw[h]);
+          xq[j * 8 + 2 * h + 1] = bf16_hi(sw[h]);
+        } else {
+          xp[j * EPV + h] = __uint_as_float(rw[h]);
+          xq[j * EPV + h] = __uint_as_float(sw[h]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int idx = e0 + e;
+      xp[e] = idx < V ? load_logit<DT>(d.xrow, idx) : 0.0f;
+      xq[e] = idx < V ? load_logit<DT>(d.yrow, idx) : 0.0f;
+    }
+  }
+  float lv[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) lv[e] = lam;
+  uint32_t exm = 0u;
+  for (int k = 0; k < nex; ++k) {
+    const int off = ex_tok[k] - e0;
+    if ((unsigned)off < (unsigned)kPerThread) {
+      const float l = ex_lam[k];
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        if (e == off) {
+          lv[e] = l;
+          exm |= 1u << e;
+        }
+      }
+    }
+  }
+  if (WANT_E && (unsigned)(t_cur - e0) < (unsigned)kPerThread) exm |= 1u << (t_cur - e0);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int idx = e0 + e;
+    const float a = fmaf(exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)), d.p_inv_s,
+                         idx == d.p_amax ? 1.0f : 0.0f);
+    const float b = fmaf(exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)), d.q_inv_s,
+                         idx == d.q_amax ? 1.0f : 0.0f);
+    const float wv = fmaxf(fmaf(-lv[e], b, a), 0.0f);
+    const bool in = idx < V;
+    w[e] = in ? wv : 0.0f;
+    if (WANT_E) be[e] = (in && !((exm >> e) & 1u)) ? b : 0.0f;
+  }
+}
+
+// Block totals of NV per-thread values, each formed exactly as
+// block_exclusive_scan forms its total (so a chunk's mass here equals the
+// total of the draw's in-chunk scan bit for bit).  All threads get them.
+template <int NV>
+__device__ __forceinline__ void block_totals(const double v[NV], double* s_red, double t[NV]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const double incl = wave_inclusive_scan(v[i]);
+    if (lane == 63) s_red[w * NV + i] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    double s = s_red[i];
+#pragma unroll
+    for (int k = 1; k < kFinWaves; ++k) s += s_red[k * NV + i];
+    t[i] = s;
+  }
+}
+
+// One pass over the node's rows: chunk masses of the weights into s_mass
+// (written by thread 0), their sum G returned to every thread, and with
+// WANT_E the draft mass outside ex_tok and t_cur in *E.
+template <int DT, bool VEC, bool WANT_E>
+__device__ double wor_pass(const WorDist& d, int V, int nc, float lam,
+                           const int* ex_tok, const float* ex_lam, int nex, int t_cur,
+                           double* s_mass, double* s_red, double* E) {
+  double e_acc = 0.0, G = 0.0;
+  for (int g0 = 0; g0 < nc; g0 += kWorGroup) {
+    StopVec<DT> r[kWorGroup];
+#pragma unroll
+    for (int k = 0; k < kWorGroup; ++k) wor_load<DT, VEC>(d, V, min(g0 + k, nc - 1), r[k]);
+    double v[kWorGroup + 1];
+#pragma unroll
+    for (int k = 0; k < kWorGroup; ++k) {
+      float w[kPerThread], be[kPerThread];
+      const int c = g0 + k;
+      wor_weights<DT, VEC, WANT_E>(d, V, min(c, nc - 1), r[k], lam, ex_tok, ex_lam, nex, t_cur, w,
+                                   be);
+      v[k] = c < nc ? thread_total(w) : 0.0;
+      if (WANT_E && c < nc) e_acc += thread_total(be);
+    }
+    v[kWorGroup] = e_acc;
+    double t[kWorGroup + 1];
+    block_totals<kWorGroup + 1>(v, s_red, t);
+#pragma unroll
+    for (int k = 0; k < kWorGroup; ++k) {
+      if (g0 + k < nc) {
+        G += t[k];
+        if (threadIdx.x == 0) s_mass[g0 + k] = t[k];
+      }
+    }
+    if (WANT_E) *E = t[kWorGroup];
+  }
+  return G;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
+  constexpr int kNodesPerWave = kMaxNodes / kFinWaves;
+  __shared__ RowStats s_rows[kMaxNodes], s_qrows[kMaxNodes];
+  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes];
+  __shared__ int s_rowok[kMaxNodes], s_qrowok[kMaxNodes];
+  __shared__ double s_pa[kMaxNodes], s_qb[kMaxNodes], s_uacc[kMaxNodes];
+  __shared__ double s_cm[kMaxNodes * kMaxChunks];  // p's mass per (node, chunk)
+  __shared__ int s_ex_tok[kMaxNodes];              // tokens of the rejected siblings
+  __shared__ float s_ex_lamf[kMaxNodes];           // their lambda (weights)
+  __shared__ double s_ex_lam[kMaxNodes];           // their lambda (ratios)
+  __shared__ unsigned long long s_inner;
+  __shared__ int s_flags;
+  __shared__ double s_red[kFinWaves * (kWorGroup + 1)];
+  __shared__ double s_scan[kFinWaves];
+  __shared__ double s_mass[kMaxChunks];
+  __shared__ int s_found[kFinWaves], s_last[kFinWaves];
+  __shared__ int s_jc;
+  __shared__ double s_base, s_t;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = a.n_chunks;
+  const int n_parts = nc * kPartsPerChunk;
+  const int b = blockIdx.x;
+  const int V = a.V, N = a.N;
+  const int nn = uni(a.n_nodes ? a.n_nodes[b] : N);
+  const float Tt = uni(a.temp[b]), Td = uni(a.temp_d[b]);
+  const long long rb = (long long)b * N;
+  const long long qb = (long long)a.B * N;   // first draft row / draft gathers
+
+  int err0 = 0;
+  if (nn < 1 || nn > N) err0 = kRowBadShape;
+  else if (!temp_ok(Tt) || !temp_ok(Td)) err0 = kRowBadTemp;
+  const bool gt = Tt == 0.0f, gd = Td == 0.0f;
+  const float kt = (gt || err0) ? 0.0f : log2e_over_t(Tt);
+  const float kd = (gd || err0) ? 0.0f : log2e_over_t(Td);
+  const uint32_t rid = uni((int)(a.row_ids ? a.row_ids[b] : (uint32_t)b));
+
+  // Partials of both rows of this wave's nodes, and one node per lane, all
+  // loaded ahead of any branch (rows clamped into the tree).
+  Partial pp[kNodesPerWave], pq[kNodesPerWave];
+#pragma unroll
+  for (int k = 0; k < kNodesPerWave; ++k) {
+    const int n = min(wave + k * kFinWaves, N - 1);
+    pp[k] = lane_partial(a.part + (rb + n) * n_parts, n_parts);
+    pq[k] = lane_partial(a.part + (qb + rb + n) * n_parts, n_parts);
+  }
+  const int li = lane < N ? lane : 0;
+  int par = a.parents[rb + li];
+  int tok = a.tokens[rb + li];
+  const float xg = a.gath[rb + li];
+  const float yg = a.gath[qb + rb + li];
+  const bool mine = !err0 && tid > 0 && tid < nn;
+  const bool badpar = mine && (par < 0 || par >= tid);
+  const bool badtok = mine && (tok < 0 || tok >= V);
+  if (!mine || badpar) {
+    par = -1;
+    tok = 0;
+  }
+  if (tid == 0) s_inner = 0ull;
+  if (!err0) {
+#pragma unroll
+    for (int k = 0; k < kNodesPerWave; ++k) {
+      const int n = wave + k * kFinWaves;
+      if (n < nn) {
+        RowStats rs, qs;
+        const bool ok = merge_parts_wave(pp[k], n_parts, gt, &rs);
+        const bool qok = merge_parts_wave(pq[k], n_parts, gd, &qs);
+        if (lane == 0) {
+          s_rows[n] = rs;
+          s_qrows[n] = qs;
+          s_rowok[n] = ok;
+          s_qrowok[n] = qok;
+        }
+        if (!gt && lane < nc)
+          s_cm[n * nc + lane] =
+              pp[k].s > 0.0 ? scale_pow2(pp[k].s, pp[k].c - rs.c) / rs.s : 0.0;
+      }
+    }
+  }
+  if (tid < kMaxNodes) {
+    s_par[tid] = par;
+    s_tok[tid] = tok;
+  }
+  __syncthreads();
+  if (tid < 64 && par >= 0) atomicOr(&s_inner, 1ull << par);
+  __syncthreads();
+  if (tid < 64) {
+    const unsigned long long inner = s_inner;
+    const int n = tid < kMaxNodes ? tid : 0;
+    const bool bad_row = tid < nn && !err0 &&
+                         (!s_rowok[n] || (((inner >> n) & 1ull) && !s_qrowok[n]));
+    const int flags = (__ballot(badpar) ? kRowBadShape : 0) | (__ballot(badtok) ? kRowBadToken : 0) |
+                      (__ballot(bad_row) ? kRowNonFinite : 0);
+    if (tid == 0) s_flags = err0 | flags;
+  }
+  __syncthreads();
+  const int err = s_flags & kRowErrorMask;
+  if (err) {
+    for (int i = tid; i < N; i += kFinThreads) {
+      a.out_tokens[rb + i] = -1;
+      if (i < N - 1) a.path_nodes[(long long)b * (N - 1) + i] = -1;
+      if (a.p_at) a.p_at[rb + i] = 0.0f;
+    }
+    if (tid == 0) {
+      a.num_accepted[b] = -1;
+      if (a.row_status) a.row_status[b] = err;
+    }
+    return;
+  }
+
+  // p and q of each node's token under its parent (float64), and the node's
+  // acceptance uniform.
+  if (tid > 0 && tid < nn) {
+    s_pa[tid] = row_prob(s_rows[par], gt, kt, xg, tok);
+    s_qb[tid] = row_prob(s_qrows[par], gd, kd, yg, tok);
+    s_uacc[tid] = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)tid).x);
+  }
+  __syncthreads();
+
+  // The walk.  Every thread runs it on the same values (read from shared
+  // memory and made scalar), so its control flow is uniform; thread 0 writes
+  // what is shared.
+  const int es = DT ? 2 : 4;
+  const long long rowbytes = (long long)V * es;
+  int node = 0, depth = 0, warn = 0;
+  unsigned long long kids;
+  WorDist d;
+  double lam = 0.0;
+  int nex = 0;
+  bool have_masses = false;   // s_mass holds the masses of the current weights
+  for (;;) {
+    kids = __ballot(lane > node && lane < nn && s_par[lane] == node);
+    d = wor_dist((const char*)a.target + (rb + node) * rowbytes,
+                 (const char*)a.draft + (rb + node) * rowbytes, s_rows[node], s_qrows[node], gt,
+                 gd, kt, kd, kids != 0ull);
+    lam = 0.0;
+    double P = 1.0, Q = 1.0;
+    nex = 0;
+    have_masses = false;
+    int accepted = -1;
+    unsigned long long rest = kids;
+    while (rest) {
+      const int c = __ffsll((long long)rest) - 1;
+      rest &= rest - 1ull;
+      const int t = uni(s_tok[c]);
+      int dupk = -1;
+      for (int k = 0; k < nex; ++k)
+        if (uni(s_ex_tok[k]) == t) dupk = k;
+      const double av = uni(s_pa[c]), bv = uni(s_qb[c]);
+      double ratio;
+      if (dupk >= 0) {
+        // the token already left q: q_j(t) = 0
+        warn |= kRowWarnQZero;
+        ratio = fmax(av - uni(s_ex_lam[dupk]) * bv, 0.0) > 0.0 ? __builtin_huge_val() : 0.0;
+      } else {
+        const double pj = fmax(av - lam * bv, 0.0) / P;
+        const double qj = Q > 0.0 ? bv / Q : 0.0;
+        if (qj > 0.0) {
+          ratio = pj / qj;
+        } else {
+          warn |= kRowWarnQZero;
+          ratio = pj > 0.0 ? __builtin_huge_val() : 0.0;
+        }
+      }
+      if (uni(s_uacc[c]) < ratio) {
+        accepted = c;
+        break;
+      }
+      // (bounded so that a near-empty q cannot make it infinite: 0 * inf)
+      const double mu = fmin(Q > 0.0 ? lam + P / Q : lam, 1.0e300);
+      double E = 0.0;
+      const double G = uni(wor_pass<DT, VEC, true>(d, V, nc, lam_f32(mu), s_ex_tok, s_ex_lamf, nex,
+                                                   dupk >= 0 ? -1 : t, s_mass, s_red, &E));
+      E = uni(E);
+      if (G > 0.0) {
+        lam = mu;
+        P = G;
+        have_masses = true;
+      } else {
+        warn |= kRowWarnRZero;   // p_j <= q_j everywhere: the residual is empty
+        have_masses = false;
+      }
+      if (dupk < 0) {
+        if (tid == 0) {
+          s_ex_tok[nex] = t;
+          s_ex_lamf[nex] = lam_f32(lam);
+          s_ex_lam[nex] = lam;
+        }
+        ++nex;
+      }
+      Q = E;
+      __syncthreads();
+    }
+    if (accepted < 0) break;
+    if (tid == 0) s_path[depth] = accepted;
+    ++depth;
+    node = accepted;
+  }
+  const int stop = node;
+
+  int token;
+  if (gt) {
+    // p is one-hot at the argmax, and so is every residual of it
+    token = s_rows[stop].amax;
+  } else {
+    if (!kids) {
+      // leaf: bonus draw from p
+      if (tid < nc) s_mass[tid] = s_cm[stop * nc + tid];
+    } else if (!have_masses) {
+      // the last rejection left p_j as it was: masses of its weights
+      wor_pass<DT, VEC, false>(d, V, nc, lam_f32(lam), s_ex_tok, s_ex_lamf, nex, -1, s_mass, s_red,
+                               nullptr);
+    }
+    __syncthreads();
+    double R = 0.0;
+    for (int j = 0; j < nc; ++j) R += s_mass[j];
+    R = uni(R);
+    __syncthreads();
+    if (!(R > 0.0)) {
+      // rounding emptied the weights: draw from p
+      warn |= kRowWarnRZero;
+      if (tid < nc) s_mass[tid] = s_cm[stop * nc + tid];
+      d = wor_dist(d.xrow, d.xrow, s_rows[stop], s_qrows[stop], gt, gd, kt, kd, false);
+      lam = 0.0;
+      nex = 0;
+      __syncthreads();
+    }
+    const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)stop).y);
+    choose_chunk(s_mass, nc, u, &s_jc, &s_base, &s_t);
+    const int jc = uni(s_jc);
+    StopVec<DT> r;
+    wor_load<DT, VEC>(d, V, jc, r);
+    float w[kPerThread], be[kPerThread];
+    wor_weights<DT, VEC, false>(d, V, jc, r, lam_f32(lam), s_ex_tok, s_ex_lamf, nex, -1, w, be);
+    const double acc = thread_total(w);
+    double total;
+    const double excl = block_exclusive_scan<kFinWaves>(acc, s_scan, &total);
+    token = find_in_chunk(w, jc, s_base, excl, s_t, s_found, s_last);
+  }
+  __syncthreads();
+
+  for (int i = tid; i < N; i += kFinThreads) {
+    a.out_tokens[rb + i] = i < depth ? s_tok[s_path[i]] : (i == depth ? token : -1);
+    if (i < N - 1) a.path_nodes[(long long)b * (N - 1) + i] = i < depth ? s_path[i] : -1;
+    if (a.p_at) a.p_at[rb + i] = (i > 0 && i < nn) ? (float)s_pa[i] : 0.0f;
+  }
+  if (tid == 0) {
+    a.num_accepted[b] = depth;
+    if (a.row_status) a.row_status[b] = warn;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host launcher.
 
 hipError_t launch_tree_finish(int dtype, const TreeArgs& a, hipStream_t st) {
-  if (dtype == 1) tree_kernel<1><<<dim3((unsigned)a.B), dim3(kFinThreads), 0, st>>>(a);
-  else tree_kernel<0><<<dim3((unsigned)a.B), dim3(kFinThreads), 0, st>>>(a);
+  const dim3 grid((unsigned)a.B), block(kFinThreads);
+  if (a.mode == 1) {
+    if (dtype == 1 && a.vec_ok) tree_wor_kernel<1, true><<<grid, block, 0, st>>>(a);
+    else if (dtype == 1) tree_wor_kernel<1, false><<<grid, block, 0, st>>>(a);
+    else if (a.vec_ok) tree_wor_kernel<0, true><<<grid, block, 0, st>>>(a);
+    else tree_wor_kernel<0, false><<<grid, block, 0, st>>>(a);
+  } else {
+    if (dtype == 1) tree_kernel<1><<<grid, block, 0, st>>>(a);
+    else tree_kernel<0><<<grid, block, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

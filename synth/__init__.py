@@ -21,6 +21,11 @@ this step):
 * ``tree_v32k``     B=64 token trees of at most 64 nodes (root included) over
   V=32000 bf16: best-first top-4 expansion to depth 4 by cumulative draft
   probability; node rows draft N(0, 2^2), target = draft + N(0, 0.5^2), T=1.
+* ``tree_wor_v32k`` B=64 trees of at most 64 nodes over V=32000 bf16 whose
+  children are 4 draws without replacement from the node's draft softmax
+  (Gumbel-top-4 of the bf16 draft row), best-first by cumulative draft
+  probability to depth 4; draft N(0, 2^2), target = draft + N(0, 0.5^2),
+  T=1 for both (the SAMPLED_WOR candidate mode).
 * ``attn_tree``     Q, K, V ~ N(0, 1) bf16, B=64, H=32, N=64, d=128, prefix
   L=4096 (cache length 4160), masked by the ``tree_v32k`` trees.
 * ``bimodal_v152k`` B=256, V=152064 bf16; half the rows sigma=3.0, half
@@ -247,6 +252,92 @@ def tree_v32k(seed=4, B=64, N=64, V=32000, pert=0.5, draft_sd=2.0, temp=1.0, dty
                 depth_hist=depth_hist, nodes_passing_0p1=passing)
 
 
+def build_wor_tree(rng, V, n_max=64, width=4, depth=4, draft_sd=2.0, temp=1.0, dtype=BF16):
+    """Best-first expansion to `depth` of trees whose children are `width` draws
+    without replacement from the node's draft softmax (temperature `temp`),
+    ranked by cumulative draft probability along the path.
+
+    Draws use the draft row as the verifier reads it (rounded to bf16 when
+    dtype is BF16): the Gumbel-top-k of logits / temp, in draw order.
+    Returns (draft_rows [n, V] float32 before rounding, parents [n],
+    tokens [n], depth [n]) in BFS order (depth, parent, draw rank).
+    """
+    rows, sel = [], []
+    heap = []
+
+    def expand(idx):
+        y = rows[idx]
+        yv = bf16_values(bf16_bits(y)) if dtype == BF16 else y
+        z = yv.astype(np.float64) / temp + rng.gumbel(size=V)
+        order = np.lexsort((np.arange(V), -z))[:width]
+        lq = scipy.special.log_softmax(yv.astype(np.float64) / temp)
+        for rank, tok in enumerate(order):
+            cum = sel[idx][3] + lq[tok]
+            heapq.heappush(heap, (-cum, sel[idx][1] + 1, idx, rank, int(tok)))
+
+    rows.append(rng.standard_normal(V).astype(np.float32) * np.float32(draft_sd))
+    sel.append((-1, 0, 0, 0.0, 0))   # (parent, depth, rank, cum_logprob, token)
+    if depth > 0:
+        expand(0)
+    while len(sel) < n_max and heap:
+        negcum, dep, parent, rank, tok = heapq.heappop(heap)
+        rows.append(rng.standard_normal(V).astype(np.float32) * np.float32(draft_sd))
+        sel.append((parent, dep, rank, -negcum, tok))
+        if dep < depth:
+            expand(len(sel) - 1)
+    n = len(sel)
+    new = {0: 0}
+    order = [0]
+    for dep in range(1, depth + 1):
+        level = [i for i in range(n) if sel[i][1] == dep]
+        level.sort(key=lambda i: (new[sel[i][0]], sel[i][2]))
+        for i in level:
+            new[i] = len(order)
+            order.append(i)
+    parents = np.array([-1] + [new[sel[i][0]] for i in order[1:]], dtype=np.int32)
+    tokens = np.array([0] + [sel[i][4] for i in order[1:]], dtype=np.int32)
+    depths = np.array([sel[i][1] for i in order], dtype=np.int32)
+    return np.stack([rows[i] for i in order]), parents, tokens, depths
+
+
+def tree_wor(seed=7, B=64, N=64, V=32000, pert=0.5, draft_sd=2.0, temp=1.0, dtype=BF16,
+             width=4, depth=4):
+    """SAMPLED_WOR trees: children drawn from the draft without replacement."""
+    rng = np.random.default_rng(seed)
+    tgt = np.empty((B, N, V), dtype=np.float32)
+    dft = np.empty((B, N, V), dtype=np.float32)
+    parents = np.full((B, N), -1, dtype=np.int32)
+    tokens = np.zeros((B, N), dtype=np.int32)
+    n_nodes = np.zeros(B, dtype=np.int32)
+    n_inner = 0
+    for b in range(B):
+        y, par, tok, dep = build_wor_tree(rng, V, N, width=width, depth=depth,
+                                          draft_sd=draft_sd, temp=temp, dtype=dtype)
+        n = len(par)
+        x = y + rng.standard_normal(y.shape, dtype=np.float32) * np.float32(pert)
+        tgt[b, :n] = x
+        dft[b, :n] = y
+        if n < N:
+            tgt[b, n:] = rng.standard_normal((N - n, V), dtype=np.float32)
+            dft[b, n:] = rng.standard_normal((N - n, V), dtype=np.float32)
+        parents[b, :n] = par
+        tokens[b, :n] = tok
+        n_nodes[b] = n
+        n_inner += len(set(par[1:].tolist()))
+    if dtype == BF16:
+        tgt_s, dft_s = bf16_bits(tgt), bf16_bits(dft)
+    else:
+        tgt_s, dft_s = tgt, dft
+    T = np.full(B, temp, dtype=np.float32)
+    return dict(kind="tree_wor", dtype=dtype, B=B, N=N, V=V, target=tgt_s, draft=dft_s,
+                parents=parents, tokens=tokens, n_nodes=n_nodes, temp_target=T,
+                temp_draft=T.copy(), seed=0, step=0, n_inner=n_inner)
+
+
+def tree_wor_v32k(seed=7, B=64, N=64, V=32000):
+    return tree_wor(seed=seed, B=B, N=N, V=V)
+
+
 def peaked_tree(seed=6, B=32, N=21, V=64, draft_sd=6.0, pert=0.5, temp=1.0, dtype=F32):
     """Small trees whose target agrees with a peaked draft, so walks reach depth >= 2."""
     return tree_v32k(seed=seed, B=B, N=N, V=V, pert=pert, draft_sd=draft_sd, temp=temp,
@@ -277,6 +368,9 @@ def logits_bytes(d):
     esize = 2 if d["dtype"] == BF16 else 4
     if d["kind"] == "linear":
         rows = d["target"].shape[0] + d["draft"].shape[0]
+    elif d["kind"] == "tree_wor":
+        # every node's target row, and the draft rows of the nodes with children
+        rows = int(np.sum(d["n_nodes"])) + int(d["n_inner"])
     else:
         rows = int(np.sum(d["n_nodes"]))
     return rows * d["V"] * esize
@@ -287,5 +381,6 @@ WORKLOADS = {
     "linear_v32k": linear_v32k,
     "linear_v128k": linear_v128k,
     "tree_v32k": tree_v32k,
+    "tree_wor_v32k": tree_wor_v32k,
     "bimodal_v152k": bimodal_v152k,
 }

@@ -150,13 +150,27 @@ def compare_linear(gpu, ref, d):
 def run_tree(d, seed=None, step=None):
     import rejection_sampling_verify_04_amd as sv
     torch = torch_mod()
+    wor = d["kind"] == "tree_wor"
     out = sv.verify_tree(logits_to_dev(d["target"], d["dtype"]), i32(d["parents"]),
                          i32(d["tokens"]), f32(d["temp_target"]),
                          n_nodes=None if d.get("n_nodes") is None else i32(d["n_nodes"]),
                          seed=d["seed"] if seed is None else seed,
-                         step=d["step"] if step is None else step)
+                         step=d["step"] if step is None else step,
+                         cand_mode=sv.SV_TREE_SAMPLED_WOR if wor else sv.SV_TREE_TOPK,
+                         draft_logits=logits_to_dev(d["draft"], d["dtype"]) if wor else None,
+                         temp_draft=f32(d["temp_draft"]) if wor else None)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def run_oracle_tree(d):
+    if d["kind"] == "tree_wor":
+        return oracle.verify_tree_sampled_wor(d["target"], d["draft"], d["dtype"], d["parents"],
+                                              d["tokens"], d.get("n_nodes"), d["temp_target"],
+                                              d["temp_draft"], seed=d["seed"], step=d["step"])
+    return oracle.verify_tree_topk(d["target"], d["dtype"], d["parents"], d["tokens"],
+                                   d.get("n_nodes"), d["temp_target"], seed=d["seed"],
+                                   step=d["step"])
 
 
 def compare_tree(gpu, ref, d):
@@ -184,6 +198,9 @@ def compare_tree(gpu, ref, d):
                         b, r.stop_kind, r.stop_node, gpu["out_tokens"][b][n], r.out_tokens[n]))
             assert np.all(gpu["out_tokens"][b][n + 1:] == -1)
             assert np.all(gpu["path_nodes"][b][n:] == -1)
+            # the same walk tests the same children: the zero-q warning agrees
+            assert (gpu["row_status"][b] & OL.ROW_WARN_QZERO) == (r.status & OL.ROW_WARN_QZERO), (
+                "tree row %d: status gpu %d oracle %d" % (b, gpu["row_status"][b], r.status))
         else:
             n_flag += 1
             assert gpu["num_accepted"][b] >= f

@@ -56,7 +56,8 @@ def test_workspace_sizes(lib):
     # partials (352 rows x 4 chunks x 16 B) + chunk masses (32 rows x 4 chunks x 8 B)
     assert n >= 352 * 4 * 16 + 32 * 4 * 8
     assert lib.spec_verify_linear_workspace_size(-1, 0, 10, 1) == 0
-    assert lib.spec_verify_tree_workspace_size(64, 64, 32000, 1) >= 64 * 64 * 4 * 16
+    # partials and gathers of the target and (SAMPLED_WOR) draft rows
+    assert lib.spec_verify_tree_workspace_size(64, 64, 32000, 1) >= 2 * 64 * 64 * (4 * 16 + 4)
 
 
 def _linear(lib, **kw):
@@ -89,7 +90,9 @@ def test_tree_and_attn_host_validation(lib):
     p = ctypes.c_void_p(256)
     common = (p, None, 1, 4, 8, 100, p, p, None)
     tail = (p, None, 0, 0, None, p, p, p, None, None, p, 1 << 20, None)
-    assert lib.spec_verify_tree(*common, 1, *tail) == -2        # SAMPLED_WOR not built
+    assert lib.spec_verify_tree(*common, 1, *tail) == -1        # SAMPLED_WOR without draft rows
+    wor = (p, p, 1, 4, 8, 100, p, p, None, 1, p, None)          # ... or without temp_draft
+    assert lib.spec_verify_tree(*wor, *tail[2:]) == -1
     assert lib.spec_verify_tree(*common, 5, *tail) == -1
     assert lib.spec_verify_tree(p, None, 1, 4, 65, 100, p, p, None, 0, *tail) == -1
     assert lib.spec_verify_attn(p, p, p, p, None, 2, 4, 8, 64, 100, 0.1, p, None, None) == -2

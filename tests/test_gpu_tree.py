@@ -5,15 +5,13 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import compare_tree, run_linear, run_tree, say
+from gpu_util import compare_tree, run_linear, run_oracle_tree, run_tree, say
 
 pytestmark = pytest.mark.gpu
 
 
 def run_oracle(d):
-    return oracle.verify_tree_topk(d["target"], d["dtype"], d["parents"], d["tokens"],
-                                   d.get("n_nodes"), d["temp_target"], seed=d["seed"],
-                                   step=d["step"])
+    return run_oracle_tree(d)
 
 
 def check(d, label):

@@ -1,0 +1,160 @@
+"""GPU parity of spec_verify_tree in SAMPLED_WOR mode against the oracle.
+
+Children are draws without replacement from each node's draft softmax.  The
+cases cover the full-size workload (B=64 trees of 64 nodes over V=32000
+bf16), small peaked trees whose walks go deep and reject several siblings in
+a row, multi-chunk and ragged vocabularies (one to ten groups of chunk
+loads per pass), rows whose length in bytes is not a multiple of 16, greedy
+target or draft rows, repeated sibling tokens, partial trees and error rows.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import compare_tree, run_linear, run_oracle_tree, run_tree, say
+
+pytestmark = pytest.mark.gpu
+
+
+def check(d, label):
+    say("[wor] %s: B=%d N=%d V=%d" % (label, d["B"], d["N"], d["V"]))
+    gpu = run_tree(d)
+    ref = run_oracle_tree(d)
+    s = compare_tree(gpu, ref, d)
+    depth = np.bincount(np.maximum(gpu["num_accepted"], 0), minlength=5)
+    rej = sum(_rejections(r, d, b) for b, r in enumerate(ref[5]))
+    say("[wor] %s: ok %s depth histogram %s, rejected siblings %d" % (
+        label, s, depth.tolist(), rej))
+    return gpu, ref
+
+
+def _rejections(r, d, b):
+    """Siblings the oracle's walk rejected (each is one extra vocabulary pass)."""
+    if r.num_accepted < 0:
+        return 0
+    par = d["parents"][b]
+    nn = d["N"] if d.get("n_nodes") is None else int(d["n_nodes"][b])
+    path = [0] + [int(v) for v in r.path_nodes[:r.num_accepted]]
+    n = 0
+    for i, node in enumerate(path):
+        kids = [c for c in range(1, nn) if par[c] == node]
+        if i + 1 < len(path):
+            n += kids.index(path[i + 1])
+        else:
+            n += len(kids)
+    return n
+
+
+def test_tree_wor_v32k_full():
+    d = synth.tree_wor_v32k()
+    check(d, "tree_wor v32k bf16")
+
+
+def test_peaked_wor_trees_reject_and_go_deep():
+    d = synth.tree_wor(seed=11, B=48, N=21, V=64, draft_sd=6.0, pert=1.0, dtype=synth.F32)
+    gpu, ref = check(d, "peaked V=64 fp32")
+    assert np.mean(gpu["num_accepted"] >= 2) > 0.3
+    assert sum(_rejections(r, d, b) for b, r in enumerate(ref[5])) >= 40
+
+
+def test_wor_multichunk_ragged_bf16():
+    # V = 20000: 3 chunks (groups of 2 and 1), ragged last chunk
+    d = synth.tree_wor(seed=12, B=16, N=40, V=20000, draft_sd=4.0, pert=1.0)
+    check(d, "V=20000 bf16")
+
+
+def test_wor_large_vocab_bf16():
+    # V = 152064: 19 chunks (10 groups), last chunk 4608 wide
+    d = synth.tree_wor(seed=13, B=4, N=16, V=152064, draft_sd=3.0, pert=1.0, width=3, depth=3)
+    check(d, "V=152064 bf16")
+
+
+def test_wor_unaligned_rows():
+    # 1001 bf16 logits per row: rows are not 16-byte multiples (element loads)
+    d = synth.tree_wor(seed=14, B=16, N=21, V=1001, draft_sd=5.0, pert=1.0)
+    check(d, "V=1001 bf16 unaligned")
+    d = synth.tree_wor(seed=15, B=8, N=21, V=8195, draft_sd=5.0, pert=1.0, dtype=synth.F32)
+    check(d, "V=8195 fp32 unaligned")
+
+
+def test_wor_greedy_and_mixed_temperatures():
+    d = synth.tree_wor(seed=16, B=24, N=21, V=64, draft_sd=6.0, pert=1.0, dtype=synth.F32)
+    tt, td = d["temp_target"].copy(), d["temp_draft"].copy()
+    tt[0::4] = 0.0                  # greedy target
+    td[1::4] = 0.0                  # greedy draft
+    tt[2::4], td[2::4] = 0.0, 0.0   # both
+    tt[3::4], td[3::4] = 0.7, 1.3   # different temperatures
+    d["temp_target"], d["temp_draft"] = tt, td
+    check(d, "greedy and mixed temperatures")
+
+
+def test_wor_repeated_sibling_tokens():
+    # duplicate children (a sampler with replacement): the zero-q path and warning
+    d = synth.tree_wor(seed=17, B=24, N=21, V=64, draft_sd=6.0, pert=1.0, dtype=synth.F32)
+    tok = d["tokens"].copy()
+    par = d["parents"]
+    for b in range(0, 24, 2):
+        kids = [c for c in range(1, d["N"]) if par[b, c] == 0]
+        if len(kids) >= 3:
+            tok[b, kids[2]] = tok[b, kids[0]]
+    d["tokens"] = tok
+    gpu, ref = check(d, "repeated sibling tokens")
+
+
+def test_wor_partial_trees_and_error_rows():
+    d = synth.tree_wor(seed=18, B=14, N=21, V=64, draft_sd=6.0, pert=1.0, dtype=synth.F32)
+    d["n_nodes"] = d["n_nodes"].copy()
+    d["n_nodes"][:4] = [1, 5, 9, 20]
+    d["parents"] = d["parents"].copy()
+    d["tokens"] = d["tokens"].copy()
+    d["target"] = d["target"].copy()
+    d["draft"] = d["draft"].copy()
+    d["parents"][5, 3] = 7            # parent after child: bad shape
+    d["tokens"][6, 2] = d["V"]        # token out of range
+    d["n_nodes"][7] = 0               # bad node count
+    d["temp_draft"] = d["temp_draft"].copy()
+    d["temp_draft"][8] = np.nan       # bad draft temperature
+    d["target"][9, 4] = -np.inf       # a node's target row without a finite maximum
+    d["draft"][10, 0] = -np.inf       # the root's draft row: non-finite
+    leaf = int(max(c for c in range(1, 21) if c not in set(d["parents"][11, 1:].tolist())))
+    d["draft"][11, leaf] = -np.inf    # a leaf's draft row is never read: fine
+    gpu, ref = check(d, "partial trees and error rows")
+    assert list(gpu["num_accepted"][[5, 6, 7, 8, 9, 10]]) == [-1] * 6
+    assert gpu["num_accepted"][11] >= 0 and gpu["row_status"][11] & 0xFF == 0
+
+
+def test_wor_chain_equals_linear():
+    """One child per node: SAMPLED_WOR is the linear verify with the draft's q."""
+    rng = np.random.default_rng(19)
+    B, g, V = 16, 6, 3000
+    y = rng.normal(0, 2, size=(B, g + 1, V)).astype(np.float32)
+    x = y + rng.normal(0, 0.6, size=(B, g + 1, V)).astype(np.float32)
+    xb, yb = synth.bf16_bits(x), synth.bf16_bits(y)
+    yv = synth.bf16_values(yb).astype(np.float64)
+    T = np.linspace(0.6, 1.4, B).astype(np.float32)
+    dtok = np.zeros((B, g), np.int32)
+    for b in range(B):
+        for i in range(g):
+            z = yv[b, i] / T[b] + rng.gumbel(size=V)
+            dtok[b, i] = int(np.argmax(z))
+    lin = dict(kind="linear", dtype=1, B=B, V=V, target=xb.reshape(B * (g + 1), V),
+               draft=yb[:, :g].reshape(B * g, V), offsets=np.arange(B + 1, dtype=np.int32) * g,
+               tokens=dtok.reshape(-1), temp_target=T, temp_draft=T.copy(), seed=4, step=2)
+    tree = dict(kind="tree_wor", dtype=1, B=B, N=g + 1, V=V, target=xb, draft=yb,
+                parents=np.tile(np.arange(-1, g, dtype=np.int32), (B, 1)),
+                tokens=np.concatenate([np.zeros((B, 1), np.int32), dtok], 1),
+                n_nodes=None, temp_target=T, temp_draft=T.copy(), seed=4, step=2)
+    gl = run_linear(lin)
+    gt = run_tree(tree)
+    assert np.array_equal(gl["num_accepted"], gt["num_accepted"])
+    same = np.array_equal(gl["out_tokens"].reshape(B, g + 1), gt["out_tokens"])
+    say("[wor] chain == linear: depths %s, tokens identical: %s" % (
+        gt["num_accepted"].tolist(), same))
+    # the drawn token may differ only where the oracle flags the draw
+    ref = run_oracle_tree(tree)
+    for b in range(B):
+        n = gt["num_accepted"][b]
+        assert np.array_equal(gl["out_tokens"].reshape(B, g + 1)[b][:n], gt["out_tokens"][b][:n])
+        if not ref[5][b].flagged_sample and ref[5][b].flagged_accept is None:
+            assert gl["out_tokens"].reshape(B, g + 1)[b][n] == gt["out_tokens"][b][n]
