@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear_v32k",
                     choices=["linear_v1000", "linear_v32k", "linear_v128k", "bimodal_v152k",
-                             "tree_v32k", "attn_tree"])
+                             "tree_v32k", "tree_wor_v32k", "attn_tree"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying one HIP graph")
@@ -113,9 +113,15 @@ def cpu_baseline_tree(d, seconds):
     rows = nodes = 0
     while time.perf_counter() - t0 < seconds:
         b = rows % B
-        oracle.verify_tree_topk(d["target"][b:b + 1], d["dtype"], d["parents"][b:b + 1],
-                                d["tokens"][b:b + 1], d["n_nodes"][b:b + 1],
-                                d["temp_target"][b:b + 1], row_ids=np.array([b]))
+        if d["kind"] == "tree_wor":
+            oracle.verify_tree_sampled_wor(d["target"][b:b + 1], d["draft"][b:b + 1], d["dtype"],
+                                           d["parents"][b:b + 1], d["tokens"][b:b + 1],
+                                           d["n_nodes"][b:b + 1], d["temp_target"][b:b + 1],
+                                           d["temp_draft"][b:b + 1], row_ids=np.array([b]))
+        else:
+            oracle.verify_tree_topk(d["target"][b:b + 1], d["dtype"], d["parents"][b:b + 1],
+                                    d["tokens"][b:b + 1], d["n_nodes"][b:b + 1],
+                                    d["temp_target"][b:b + 1], row_ids=np.array([b]))
         nodes += int(d["n_nodes"][b]) - 1
         rows += 1
     dt = time.perf_counter() - t0
@@ -256,7 +262,10 @@ def main():
                           input_copies=nc)
             unit = "verified draft positions/s"
         else:
+            wor = d["kind"] == "tree_wor"
             sets = [to_dev_logits(torch, d["target"], d["dtype"]) for _ in range(nc)]
+            dsets = [to_dev_logits(torch, d["draft"], d["dtype"]) for _ in range(nc)] if wor else None
+            td = torch.from_numpy(d["temp_draft"]).cuda() if wor else None
             par = torch.from_numpy(d["parents"]).cuda()
             tok = torch.from_numpy(d["tokens"]).cuda()
             nn = torch.from_numpy(d["n_nodes"]).cuda()
@@ -275,9 +284,14 @@ def main():
                 if ev is not None:
                     sv.profile_next(ev[0], ev[1])
                 sv.verify_tree(sets[i % nc], par, tok, tt, n_nodes=nn, seed=0, step=i,
-                               workspace=ws, outputs=outs)
-            config = dict(workload=wl, B=Bn, nodes=N, V=d["V"], mode="TOPK", input_dtype="bf16",
+                               workspace=ws, outputs=outs,
+                               cand_mode=sv.SV_TREE_SAMPLED_WOR if wor else sv.SV_TREE_TOPK,
+                               draft_logits=dsets[i % nc] if wor else None, temp_draft=td)
+            config = dict(workload=wl, B=Bn, nodes=N, V=d["V"],
+                          mode="SAMPLED_WOR" if wor else "TOPK", input_dtype="bf16",
                           input_copies=nc)
+            if wor:
+                config["draft_rows_read"] = int(d["n_inner"])
             unit = "verified draft nodes/s"
         alg_bytes = per_call
         flops = 0

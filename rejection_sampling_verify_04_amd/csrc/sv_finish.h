@@ -63,6 +63,91 @@ __device__ bool merge_parts_wave(const Partial& q_in, int n_parts, bool greedy, 
   return finite_c && S > 0.0 && S < __builtin_huge_val();
 }
 
+// Segmented forms of the merge: lanes in groups of P (a power of two, 1..64,
+// uniform over the wave) each hold one partial of the group's row, so a wave
+// merges 64 / P rows at once.  Within 16 lanes the groups combine through
+// DPP butterflies; wider groups through lane permutes.  Every lane of a group
+// gets the same result.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m) {
+  const int src = ((int)(threadIdx.x & 63) ^ m) << 2;
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v);
+}
+__device__ __forceinline__ float seg_max_f32(float v, int P) {
+  if (P >= 2) v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  if (P >= 4) v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  if (P >= 8) v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  if (P >= 16) v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  if (P >= 32) v = fmaxf(v, __uint_as_float(lane_xor_u32(__float_as_uint(v), 16)));
+  if (P >= 64) v = fmaxf(v, __uint_as_float(lane_xor_u32(__float_as_uint(v), 32)));
+  return v;
+}
+__device__ __forceinline__ double lane_xor_f64(double v, int m) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = lane_xor_u32((uint32_t)b, m), hi = lane_xor_u32((uint32_t)(b >> 32), m);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+__device__ __forceinline__ double seg_sum_f64(double v, int P) {
+  if (P >= 2) v += dpp_f64<kDppXor1>(v);
+  if (P >= 4) v += dpp_f64<kDppXor2>(v);
+  if (P >= 8) v += dpp_f64<kDppHalfMirror>(v);
+  if (P >= 16) v += dpp_f64<kDppMirror>(v);
+  if (P >= 32) v += lane_xor_f64(v, 16);
+  if (P >= 64) v += lane_xor_f64(v, 32);
+  return v;
+}
+__device__ __forceinline__ uint64_t seg_max_u64(uint64_t v, int P) {
+  uint64_t w;
+  if (P >= 2) { w = dpp_u64<kDppXor1>(v); v = w > v ? w : v; }
+  if (P >= 4) { w = dpp_u64<kDppXor2>(v); v = w > v ? w : v; }
+  if (P >= 8) { w = dpp_u64<kDppHalfMirror>(v); v = w > v ? w : v; }
+  if (P >= 16) { w = dpp_u64<kDppMirror>(v); v = w > v ? w : v; }
+  if (P >= 32) {
+    w = ((uint64_t)lane_xor_u32((uint32_t)(v >> 32), 16) << 32) | lane_xor_u32((uint32_t)v, 16);
+    v = w > v ? w : v;
+  }
+  if (P >= 64) {
+    w = ((uint64_t)lane_xor_u32((uint32_t)(v >> 32), 32) << 32) | lane_xor_u32((uint32_t)v, 32);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// The group merge of one row (`valid`: this lane holds one of its partials);
+// returns false when the row has no finite maximum.  Same results as
+// merge_parts_wave up to the order of the float64 additions.
+__device__ __forceinline__ bool merge_parts_seg(const Partial& q_in, bool valid, int P,
+                                                bool greedy, RowStats* out) {
+  const float qc = valid ? q_in.c : -__builtin_huge_valf();
+  const double qs = valid ? q_in.s : 0.0;
+  const unsigned long long key =
+      valid ? ((unsigned long long)float_order_key(q_in.c) << 32) | (0xffffffffu - (uint32_t)q_in.amax)
+            : 0ull;
+  const unsigned long long best = seg_max_u64(key, P);
+  const float gm = float_from_order_key((uint32_t)(best >> 32));
+  const float C = seg_max_f32(qc, P);
+  const double S = seg_sum_f64(qs > 0.0 ? scale_pow2(qs, qc - C) : 0.0, P);
+  if (greedy) {
+    out->c = gm;
+    out->amax = (int)(0xffffffffu - (uint32_t)best);
+    out->s = 0.0;
+    out->inv_s = 0.0;
+    return gm > -__builtin_huge_valf() && gm < __builtin_huge_valf();
+  }
+  out->c = C;
+  out->amax = 0;
+  out->s = S;
+  out->inv_s = 1.0 / S;
+  const bool finite_c = C > -__builtin_huge_valf() && C < __builtin_huge_valf();
+  return finite_c && S > 0.0 && S < __builtin_huge_val();
+}
+
+// Lanes per row of a segmented merge: n_parts rounded up to a power of two.
+__host__ __device__ inline int seg_width(int n_parts) {
+  int P = 1;
+  while (P < n_parts) P <<= 1;
+  return P;
+}
+
 __device__ __forceinline__ bool merge_row_wave(const Partial* __restrict__ p, int n_parts,
                                                bool greedy, RowStats* out) {
   return merge_parts_wave(lane_partial(p, n_parts), n_parts, greedy, out);

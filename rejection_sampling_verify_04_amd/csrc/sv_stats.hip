@@ -232,13 +232,30 @@ __device__ __forceinline__ Partial wave_combine(const LaneStats& st, bool greedy
   return Partial{C, 0, wave_sum(t)};
 }
 
+// The k-th set bit of m (whole waves; 0 if m has fewer than k + 1 bits).
+__device__ __forceinline__ int wave_kth_bit(unsigned long long m, int k) {
+  const int lane = threadIdx.x & 63;
+  const bool set = ((m >> lane) & 1ull) != 0ull;
+  const int rank = __popcll(m & ((1ull << lane) - 1ull));
+  const unsigned long long hit = __ballot(set && rank == k);
+  return hit ? __ffsll((long long)hit) - 1 : 0;
+}
+
 // RING = sub-segments in flight per wave: 2 for streaming many chunks per
 // wave, 4 (a whole chunk) when every wave has about one chunk.
+//
+// Tree rows are compacted when the trees' shapes fit in LDS: the units run
+// over the used rows only (each tree's first n_nodes target rows, then the
+// draft rows of the nodes that have children), so that every wave gets an
+// equal share of the work whatever the shapes.  Otherwise unused rows are
+// skipped as they come.
 template <int DT, int RING>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   __shared__ int s_i[kStatsCache + 1];
   __shared__ float s_f0[kStatsCache], s_f1[kStatsCache];
   __shared__ unsigned long long s_inner[kInnerCache];   // tree b: bit n set if node n has a child
+  __shared__ int s_pt[kInnerCache + 1], s_pq[kInnerCache + 1];   // used-row prefixes
+  __shared__ double s_scan[kWaves];
 
   const int V = a.V;
   // The first work items gather the logits at the draft tokens; being
@@ -252,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nc = (uint32_t)a.n_chunks;
-  const uint32_t total = (uint32_t)a.n_rows * nc;   // < 2^31 (checked by the host)
+  uint32_t total = (uint32_t)a.n_rows * nc;   // < 2^31 (checked by the host)
   const uint32_t G = (gridDim.x - n_gblk) * kWaves;
   const uint32_t Gq = G / nc, Gr = G - Gq * nc;
   const long long rowbytes = (long long)V * SegLoad<DT>::ES;
@@ -261,26 +278,30 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
                      : (const char*)a.rows_b + ((long long)r - a.n_a) * rowbytes;
   };
 
-  uint32_t u = blk * kWaves + wave;
-  uint32_t row = u / nc, ch = u - row * nc;
-
-  SegLoad<DT> ring[RING];
-  // The first chunk's loads go out before anything else; an unused tree
-  // row is still allocated, so reading it is harmless.
-  if (a.vec_ok && u < total) {
-#pragma unroll
-    for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
-  }
-
   const bool cache = a.B <= kStatsCache;
   // Tree draft rows are read only for nodes with children.
   const bool tree_q = a.tree && a.rows_b;
   const bool cache_inner = tree_q && a.B <= kInnerCache;
+  const bool compact = a.tree && a.B <= kInnerCache;
+
+  uint32_t u = blk * kWaves + wave;
+  uint32_t ur = u / nc, ch = u - ur * nc;   // ur: row in the order the units run
+
+  SegLoad<DT> ring[RING];
+  // The first chunk's loads go out before anything else (compacted trees:
+  // once the row map is known); an unused tree row is still allocated, so
+  // reading it is harmless.
+  if (!compact && a.vec_ok && u < total) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(ur), V, (int)ch * kChunk + r * kSubSpan);
+  }
+
   if (cache) {
     for (int i = threadIdx.x; i <= a.B; i += kThreads) {
       if (a.tree) {
         if (i < a.B) {
-          s_i[i] = a.n_nodes ? a.n_nodes[i] : a.N;
+          const int nn = a.n_nodes ? a.n_nodes[i] : a.N;
+          s_i[i] = (nn >= 1 && nn <= a.N) ? nn : 0;   // a bad count: no row is read
           s_f0[i] = a.temp_a[i];
           s_f1[i] = a.temp_b[i];
           if (cache_inner) s_inner[i] = 0ull;
@@ -295,29 +316,81 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
     __syncthreads();
     if (cache_inner) {
-      const int N = a.N;
-      for (int i = threadIdx.x; i < a.B * N; i += kThreads) {
-        const int b = i / N, c = i - b * N;
-        const int par = a.parents[i];
-        if (c > 0 && c < s_i[b] && par >= 0 && par < c) atomicOr(&s_inner[b], 1ull << par);
+      // 16 parents per thread in flight at once (clamped indices: no load
+      // behind a branch, so none is waited for alone)
+      const int N = a.N, BN = a.B * N;
+      constexpr int kBatch = 16;
+      for (int i0 = threadIdx.x; i0 < BN; i0 += kThreads * kBatch) {
+        int pv[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) pv[k] = a.parents[min(i0 + k * kThreads, BN - 1)];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int i = i0 + k * kThreads;
+          const int b = i / N, c = i - b * N;
+          const int par = pv[k];
+          if (i < BN && c > 0 && c < s_i[b] && par >= 0 && par < c)
+            atomicOr(&s_inner[b], 1ull << par);
+        }
       }
       __syncthreads();
     }
   }
+  uint32_t n_t = 0;   // compacted: used target rows (they come first)
+  if (compact) {
+    // exclusive prefixes of the used rows per tree, two trees per thread
+    for (int h = 0; h < 2; ++h) {
+      const bool q = h == 1;
+      if (q && !tree_q) break;
+      int* pre = q ? s_pq : s_pt;
+      const int i0 = 2 * threadIdx.x;
+      auto cnt = [&](int b) -> int {
+        if (b >= a.B) return 0;
+        return q ? __popcll(s_inner[b]) : s_i[b];
+      };
+      const int c0 = cnt(i0), c1 = cnt(i0 + 1);
+      double tot;
+      const int ex = (int)block_exclusive_scan<kWaves>((double)(c0 + c1), s_scan, &tot);
+      if (i0 < a.B) pre[i0] = ex;
+      if (i0 + 1 < a.B) pre[i0 + 1] = ex + c0;
+      if (threadIdx.x == 0) pre[a.B] = (int)tot;
+      __syncthreads();
+    }
+    n_t = (uint32_t)s_pt[a.B];
+    total = (n_t + (tree_q ? (uint32_t)s_pq[a.B] : 0u)) * nc;
+  }
+  // The row of iteration row x.
+  auto row_of = [&](uint32_t x) -> uint32_t {
+    if (!compact) return x;
+    const int N = a.N;
+    if (x < n_t) {
+      const int b = wave_find_batch_row(s_pt, a.B, (long long)x, 0);
+      return (uint32_t)(b * N + ((int)x - s_pt[b]));
+    }
+    const uint32_t y = x - n_t;
+    const int b = wave_find_batch_row(s_pq, a.B, (long long)y, 0);
+    return (uint32_t)a.n_a + (uint32_t)(b * N + wave_kth_bit(s_inner[b], (int)y - s_pq[b]));
+  };
   if (u >= total) return;
+  uint32_t row = row_of(ur);
+  if (compact && a.vec_ok) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
+  }
 
-  // Whether a row's partials are needed: tree rows past n_nodes are not, nor
-  // the draft rows of nodes without children.  Called by whole waves.
+  // Whether a row's partials are needed (always, for compacted rows): tree
+  // rows past n_nodes are not, nor the draft rows of nodes without
+  // children.  Called by whole waves.
   auto row_used = [&](uint32_t r) -> bool {
-    if (!a.tree) return true;
+    if (!a.tree || compact) return true;
     const bool is_q = r >= a.n_a;
     const uint32_t x = is_q ? r - (uint32_t)a.n_a : r;
     const uint32_t b = x / (uint32_t)a.N;
     const int node = (int)(x - b * (uint32_t)a.N);
-    const int nn = cache ? s_i[b] : (a.n_nodes ? a.n_nodes[b] : a.N);
+    int nn = cache ? s_i[b] : (a.n_nodes ? a.n_nodes[b] : a.N);
+    if (nn > a.N) nn = 0;
     if (node >= nn) return false;
     if (!is_q) return true;
-    if (cache_inner) return ((s_inner[b] >> node) & 1ull) != 0ull;
     const int c = lane;
     const bool kid = c > node && c < nn && a.parents[(long long)b * a.N + c] == node;
     return __ballot(kid) != 0ull;
@@ -357,7 +430,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   };
 
   if (!a.vec_ok) {                        // unaligned rows: plain loads, no prefetch
-    for (; u < total; u += G, advance(row, ch)) {
+    for (; u < total; u += G, advance(ur, ch)) {
+      row = row_of(ur);
       if (!row_used(row)) continue;
       const float T = row_temp(row);
       const bool ok = temp_ok(T);
@@ -377,13 +451,21 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     return;
   }
 
+  // The wave's next unit whose row is used (u >= total: none), so that the
+  // loads in flight always belong to a unit that is reduced.
+  auto next_used = [&](uint32_t& uu, uint32_t& x, uint32_t& c, uint32_t& r) {
+    do {
+      uu += G;
+      advance(x, c);
+    } while (uu < total && !row_used(r = row_of(x)));
+  };
   bool used = row_used(row);
   float T = used ? row_temp(row) : 0.0f;
   for (;;) {
-    uint32_t row1 = row, ch1 = ch;
-    advance(row1, ch1);
-    const bool has1 = u + G < total;
-    const bool used1 = has1 && row_used(row1);
+    uint32_t u1 = u, ur1 = ur, ch1 = ch, row1 = row;
+    next_used(u1, ur1, ch1, row1);
+    const bool has1 = u1 < total;
+    const bool used1 = has1;
     const float T1 = used1 ? row_temp(row1) : 0.0f;
     const char* p0 = row_ptr(row);
     const char* p1 = row_ptr(row1);
@@ -410,9 +492,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
     if (used) chunk_end(row, ch, ok, greedy, st);
     if (!has1) break;
-    u += G;
-    row = row1;
+    u = u1;
+    ur = ur1;
     ch = ch1;
+    row = row1;
     used = used1;
     T = T1;
   }

@@ -25,7 +25,6 @@ namespace sv {
 
 template <int DT>
 __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
-  constexpr int kNodesPerWave = kMaxNodes / kFinWaves;
   __shared__ RowStats s_rows[kMaxNodes];
   __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes], s_rowok[kMaxNodes];
   __shared__ double s_pn[kMaxNodes];
@@ -54,16 +53,18 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
   const bool greedy = T == 0.0f;
   const float k2 = (greedy || err0) ? 0.0f : log2e_over_t(T);
 
-  // Every wave loads its node rows' partials (rows clamped into the tree)
-  // and one node per lane: its parent, its token and the logit of the token
-  // under the parent (gathered by the vocabulary pass).  Only wave 0's lanes
-  // 1..nn-1 keep the latter.  No load sits behind a branch.
-  Partial q[kNodesPerWave];
-#pragma unroll
-  for (int k = 0; k < kNodesPerWave; ++k) {
-    const int n = min(wave + k * kFinWaves, N - 1);
-    q[k] = lane_partial(a.part + (rb + n) * n_parts, n_parts);
-  }
+  // Partials of the node rows, merged in groups of P lanes per row (64 / P
+  // rows per wave and round), and one node per lane: its parent, its token
+  // and the logit of the token under the parent (gathered by the vocabulary
+  // pass).  Only wave 0's lanes 1..nn-1 keep the latter.  The first round's
+  // loads sit ahead of any branch.
+  const int P = seg_width(n_parts), R = 64 / P;
+  const int part = lane & (P - 1), sub = lane / P;
+  auto load_part = [&](int row) {
+    const int n = min(row, N - 1);
+    return a.part[(rb + n) * n_parts + min(part, n_parts - 1)];
+  };
+  Partial q0 = load_part(wave * R + sub);
   const int li = lane < N ? lane : 0;
   int par = a.parents[rb + li];
   int tok = a.tokens[rb + li];
@@ -76,19 +77,18 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
     tok = 0;
   }
   if (!err0) {
-#pragma unroll
-    for (int k = 0; k < kNodesPerWave; ++k) {
-      const int n = wave + k * kFinWaves;
+    for (int base = wave * R; base < nn; base += kFinWaves * R) {
+      const Partial q = base == wave * R ? q0 : load_part(base + sub);
+      const int n = base + sub;
+      RowStats rs;
+      const bool ok = merge_parts_seg(q, n < nn && part < n_parts, P, greedy, &rs);
       if (n < nn) {
-        RowStats rs;
-        const bool ok = merge_parts_wave(q[k], n_parts, greedy, &rs);
-        if (lane == 0) {
+        if (part == 0) {
           s_rows[n] = rs;
           s_rowok[n] = ok;
         }
-        if (!greedy && lane < n_chunks)
-          s_cm[n * n_chunks + lane] =
-              q[k].s > 0.0 ? scale_pow2(q[k].s, q[k].c - rs.c) / rs.s : 0.0;
+        if (!greedy && part < n_chunks)
+          s_cm[n * n_chunks + part] = q.s > 0.0 ? scale_pow2(q.s, q.c - rs.c) / rs.s : 0.0;
       }
     }
   }
@@ -256,10 +256,12 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
 // Q = q's mass left in q_j sets mu = lambda + P / Q and
 // G = sum_v max(0, a - L'_v b), L'_v = mu for tokens still in q_j; then
 // lambda = mu and P = G (both unchanged when G = 0: the residual is empty).
-// One vocabulary pass over the node's two rows forms G per chunk and the
-// draft mass that stays after t_j leaves, so a walk costs one pass per
-// rejected sibling, plus the draw.  When every child is rejected, the
-// draw's weights are the last pass's, and its chunk masses are reused.
+// One vocabulary pass over the node's two rows forms G per chunk (and, when
+// q(t_j) is more than half of Q, the draft mass that stays once t_j leaves;
+// otherwise that is Q - q(t_j)), so a walk costs one pass per rejected
+// sibling, plus the draw.  When every child is rejected, the draw's weights
+// are the last pass's, and its chunk masses are reused.  A pass is bound by
+// the vector ALU of its one CU (two exponentials per element).
 
 // The rows of one tree node as the SAMPLED_WOR passes read them, with
 // p(v) = 2^(x p_k - p_c) p_inv_s + [v = p_amax] (and q likewise): a sampled
@@ -274,6 +276,7 @@ struct WorDist {
   int p_amax;
   float q_k, q_c, q_inv_s;
   int q_amax;
+  int onehot;            // a greedy row is present (one-hot terms to add)
 };
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -307,6 +310,7 @@ __device__ __forceinline__ WorDist wor_dist(const char* xrow, const char* yrow, 
   d.q_c = uni(qe ? qs.c : inf);
   d.q_inv_s = uni(qe ? (float)qs.inv_s : 0.0f);
   d.q_amax = uni((use_q && gd) ? qs.amax : -1);
+  d.onehot = d.p_amax >= 0 || d.q_amax >= 0;
   return d;
 }
 
@@ -386,6 +390,17 @@ __device__ __forceinline__ void wor_weights(const WorDist& d, int V, int chunk,
     }
   }
   if (WANT_E && (unsigned)(t_cur - e0) < (unsigned)kPerThread) exm |= 1u << (t_cur - e0);
+  if (!d.onehot && e0 + kPerThread <= V) {
+    // sampled rows, elements all inside the row (the same values as below)
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const float a = exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
+      const float b = exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
+      w[e] = fmaxf(fmaf(-lv[e], b, a), 0.0f);
+      if (WANT_E) be[e] = ((exm >> e) & 1u) ? 0.0f : b;
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const int idx = e0 + e;
@@ -461,7 +476,6 @@ __device__ double wor_pass(const WorDist& d, int V, int nc, float lam,
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
-  constexpr int kNodesPerWave = kMaxNodes / kFinWaves;
   __shared__ RowStats s_rows[kMaxNodes], s_qrows[kMaxNodes];
   __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes];
   __shared__ int s_rowok[kMaxNodes], s_qrowok[kMaxNodes];
@@ -497,15 +511,18 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   const float kd = (gd || err0) ? 0.0f : log2e_over_t(Td);
   const uint32_t rid = uni((int)(a.row_ids ? a.row_ids[b] : (uint32_t)b));
 
-  // Partials of both rows of this wave's nodes, and one node per lane, all
-  // loaded ahead of any branch (rows clamped into the tree).
-  Partial pp[kNodesPerWave], pq[kNodesPerWave];
-#pragma unroll
-  for (int k = 0; k < kNodesPerWave; ++k) {
-    const int n = min(wave + k * kFinWaves, N - 1);
-    pp[k] = lane_partial(a.part + (rb + n) * n_parts, n_parts);
-    pq[k] = lane_partial(a.part + (qb + rb + n) * n_parts, n_parts);
-  }
+  // Partials of the 2 nn rows (target rows of the nodes, then their draft
+  // rows), merged in groups of P lanes per row, and one node per lane.  The
+  // first round's loads sit ahead of any branch.
+  const int P = seg_width(n_parts), R = 64 / P;
+  const int part = lane & (P - 1), sub = lane / P;
+  const int n_rows = err0 ? 0 : 2 * nn;
+  auto load_part = [&](int row) {
+    const int r = min(row, 2 * N - 1);
+    const long long at = r < nn ? rb + r : qb + rb + min(r - nn, N - 1);
+    return a.part[at * n_parts + min(part, n_parts - 1)];
+  };
+  Partial q0 = load_part(wave * R + sub);
   const int li = lane < N ? lane : 0;
   int par = a.parents[rb + li];
   int tok = a.tokens[rb + li];
@@ -519,24 +536,27 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     tok = 0;
   }
   if (tid == 0) s_inner = 0ull;
-  if (!err0) {
-#pragma unroll
-    for (int k = 0; k < kNodesPerWave; ++k) {
-      const int n = wave + k * kFinWaves;
-      if (n < nn) {
-        RowStats rs, qs;
-        const bool ok = merge_parts_wave(pp[k], n_parts, gt, &rs);
-        const bool qok = merge_parts_wave(pq[k], n_parts, gd, &qs);
-        if (lane == 0) {
+  for (int base = wave * R; base < n_rows; base += kFinWaves * R) {
+    const Partial q = base == wave * R ? q0 : load_part(base + sub);
+    const int r = base + sub;
+    const bool draft = r >= nn;
+    const int n = draft ? r - nn : r;
+    RowStats rs;
+    // a wave may hold target and draft rows: the greedy choice is per lane
+    const bool g = draft ? gd : gt;
+    const bool ok = merge_parts_seg(q, r < n_rows && part < n_parts, P, g, &rs);
+    if (r < n_rows) {
+      if (part == 0) {
+        if (draft) {
+          s_qrows[n] = rs;
+          s_qrowok[n] = ok;
+        } else {
           s_rows[n] = rs;
-          s_qrows[n] = qs;
           s_rowok[n] = ok;
-          s_qrowok[n] = qok;
         }
-        if (!gt && lane < nc)
-          s_cm[n * nc + lane] =
-              pp[k].s > 0.0 ? scale_pow2(pp[k].s, pp[k].c - rs.c) / rs.s : 0.0;
       }
+      if (!draft && !gt && part < nc)
+        s_cm[n * nc + part] = q.s > 0.0 ? scale_pow2(q.s, q.c - rs.c) / rs.s : 0.0;
     }
   }
   if (tid < kMaxNodes) {
@@ -630,10 +650,19 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
       }
       // (bounded so that a near-empty q cannot make it infinite: 0 * inf)
       const double mu = fmin(Q > 0.0 ? lam + P / Q : lam, 1.0e300);
-      double E = 0.0;
-      const double G = uni(wor_pass<DT, VEC, true>(d, V, nc, lam_f32(mu), s_ex_tok, s_ex_lamf, nex,
-                                                   dupk >= 0 ? -1 : t, s_mass, s_red, &E));
-      E = uni(E);
+      // The draft mass left once t leaves q: Q - q(t) while that difference
+      // is well conditioned, else summed over the vocabulary in the pass.
+      double E = Q;
+      double G;
+      if (dupk < 0 && bv > 0.5 * Q) {
+        G = uni(wor_pass<DT, VEC, true>(d, V, nc, lam_f32(mu), s_ex_tok, s_ex_lamf, nex, t, s_mass,
+                                        s_red, &E));
+        E = uni(E);
+      } else {
+        G = uni(wor_pass<DT, VEC, false>(d, V, nc, lam_f32(mu), s_ex_tok, s_ex_lamf, nex, -1,
+                                         s_mass, s_red, nullptr));
+        if (dupk < 0) E = Q - bv;
+      }
       if (G > 0.0) {
         lam = mu;
         P = G;
