@@ -27,3 +27,4 @@ from .linear import verify_linear, verify_linear_row, LinearRowResult  # noqa: F
 from .tree import (verify_tree_topk, verify_tree_topk_row,  # noqa: F401
                    verify_tree_sampled_wor, verify_tree_sampled_wor_row, TreeRowResult)
 from .attention import verify_attention, attention_head, ancestor_mask  # noqa: F401
+from .kv import kv_commit, commit_row_plan  # noqa: F401
