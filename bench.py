@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear_v32k",
                     choices=["linear_v1000", "linear_v32k", "linear_v128k", "bimodal_v152k",
-                             "tree_v32k", "tree_wor_v32k", "attn_tree"])
+                             "tree_v32k", "tree_wor_v32k", "attn_tree", "kv_commit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying one HIP graph")
@@ -149,6 +149,29 @@ def cpu_baseline_attn(q, k, v, L, parents, seconds):
                        "(BLAS matmul threads)" % (heads, dt))
 
 
+def cpu_baseline_kv(kc, vc, L0, n_acc, path, N, seconds):
+    """The oracle's commit on a bounded sample: one (batch row, all heads, all layers) slice
+    at a time, copied to the host first (copy time excluded)."""
+    import oracle
+    layers, B = kc.shape[0], kc.shape[1]
+    ks = kc[:, :, :, L0:L0 + N].float().cpu().numpy()
+    vs = vc[:, :, :, L0:L0 + N].float().cpu().numpy()
+    t_total = 0.0
+    rows = toks = 0
+    while t_total < seconds:
+        b = rows % B
+        t0 = time.perf_counter()
+        oracle.kv_commit(ks[:, b:b + 1], vs[:, b:b + 1], np.array([0]), n_acc[b:b + 1],
+                         path[b:b + 1], N)
+        t_total += time.perf_counter() - t0
+        toks += max(int(n_acc[b]), 0)
+        rows += 1
+    return dict(value=toks / t_total, unit="committed tokens/s", cores=1, kind="oracle",
+                sample="%d batch rows (%d committed tokens, %d layers) of the same workload, "
+                       "the %d new slots of every head, in %.2f s of NumPy copying"
+                       % (rows, toks, layers, N, t_total))
+
+
 def load_traffic(path, workload, kernel_sig):
     """HBM bytes per launch of the dominant kernel, from counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size); None when
@@ -168,8 +191,8 @@ def kernel_source_sig(wl):
     own file and the headers that file includes)."""
     import hashlib
     csrc = os.path.join(ROOT, "rejection_sampling_verify_04_amd", "csrc")
-    names = (["sv_attn.hip", "sv_common.h", "sv_internal.h"] if wl == "attn_tree"
-             else ["sv_stats.hip", "sv_common.h", "sv_internal.h"])
+    own = {"attn_tree": "sv_attn.hip", "kv_commit": "sv_kv.hip"}.get(wl, "sv_stats.hip")
+    names = [own, "sv_common.h", "sv_internal.h"]
     h = hashlib.sha1()
     for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
@@ -195,7 +218,46 @@ def main():
     stream = torch.cuda.current_stream()
     dev = torch.device("cuda", 0)
 
-    if wl == "attn_tree":
+    if wl == "kv_commit":
+        # The commit after a SAMPLED_WOR tree round: paths from the library's
+        # own verify of the tree_wor_v32k trees, caches of 4 layers.
+        B, H, N, dd, L0, layers = 64, 32, 64, 128, 4096, 4
+        S = L0 + N
+        tr = synth.tree_wor_v32k()
+        g = sv.verify_tree(to_dev_logits(torch, tr["target"], 1), torch.from_numpy(tr["parents"]).cuda(),
+                           torch.from_numpy(tr["tokens"]).cuda(),
+                           torch.from_numpy(tr["temp_target"]).cuda(),
+                           n_nodes=torch.from_numpy(tr["n_nodes"]).cuda(),
+                           cand_mode=sv.SV_TREE_SAMPLED_WOR,
+                           draft_logits=to_dev_logits(torch, tr["draft"], 1),
+                           temp_draft=torch.from_numpy(tr["temp_draft"]).cuda())
+        n_acc = g["num_accepted"]
+        path = g["path_nodes"]
+        torch.cuda.synchronize()
+        kc = torch.empty((layers, B, H, S, dd), dtype=torch.bfloat16, device=dev).normal_()
+        vc = torch.empty_like(kc).normal_()
+        pl = torch.full((B,), L0, dtype=torch.int32, device=dev)
+        nl = torch.empty(B, dtype=torch.int32, device=dev)
+        na, pa = n_acc.cpu().numpy(), path.cpu().numpy()
+        moved = 0
+        for b in range(B):
+            n = int(na[b])
+            i0 = next((i for i in range(n) if pa[b, i] != i + 1), n)
+            moved += n - i0
+        alg_bytes = moved * layers * H * dd * 2 * 2 * 2    # K and V rows, read and written
+        flops = 0
+        units = int(np.maximum(na, 0).sum())
+
+        def step(i, ev=None):
+            if ev is not None:
+                sv.profile_next(ev[0], ev[1])
+            sv.kv_commit(kc, vc, pl, n_acc, path, new_len=nl)
+        config = dict(workload=wl, B=B, H=H, head_dim=dd, prefix_len=L0, nodes=N, layers=layers,
+                      paths="SAMPLED_WOR verify of tree_wor_v32k",
+                      accepted_tokens=units, rows_moved_per_layer_head=moved, input_dtype="bf16")
+        unit = "committed tokens/s"
+        metric = "KV commit: committed tokens/sec + achieved HBM GB/s (% of peak)"
+    elif wl == "attn_tree":
         B, H, N, dd, L = 64, 32, 64, 128, 4096
         tree = synth.tree_v32k(seed=4, B=B, N=N, V=64)
         q, k, v, pl = synth.attn_tensors(B=B, H=H, N=N, L=L)
@@ -300,7 +362,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    use_graph = not args.no_graph and wl != "attn_tree"
+    use_graph = not args.no_graph and wl not in ("attn_tree",)
     if use_graph:
         # The K timed steps are captured once and replayed as one graph, so
         # the host does not pace the GPU.
@@ -336,7 +398,8 @@ def main():
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=traffic,
-                kernel=("attn_kernel" if wl == "attn_tree" else "stats_kernel"),
+                kernel={"attn_tree": "attn_kernel", "kv_commit": "kv_commit_kernel"}.get(
+                    wl, "stats_kernel"),
                 algorithmic_bytes_per_launch=int(alg_bytes),
                 avg_kernel_us=round(avg_kern_s * 1e6, 2))
     if flops:
@@ -349,7 +412,9 @@ def main():
                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
                data="synthetic", config=config, roofline=roof)
     if not args.no_cpu_baseline:
-        if wl == "attn_tree":
+        if wl == "kv_commit":
+            out["cpu_baseline"] = cpu_baseline_kv(kc, vc, L0, na, pa, N, args.cpu_seconds)
+        elif wl == "attn_tree":
             out["cpu_baseline"] = cpu_baseline_attn(q, k, v, pl, tree["parents"], args.cpu_seconds)
         elif d["kind"] == "linear":
             out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)

@@ -226,6 +226,38 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      void* out, float* lse, hipStream_t stream);
 
 /*
+ * KV-cache commit after a verify round (cf-1 §3.3: reuse the cached prefix,
+ * keep the accepted positions, drop every entry after the accept point;
+ * kwkr §5.1: one pre-allocated cache spliced by offsets).  The round's
+ * forward pass stored the entries of its N new tokens (node 0 = the root,
+ * the last committed token) at slots [L, L + N), L = prefix_len[b].  For
+ * each batch row with n = num_accepted[b] >= 0 and a valid path, the entry
+ * at slot L + path[i] moves to slot L + 1 + i (i < n) in every layer and
+ * head of both caches, every source read before any write, and
+ * new_len[b] = L + 1 + n.  A row with n < 0 (flagged by the verify call) is
+ * left as it is with new_len[b] = L; a row whose L, n or path is malformed
+ * (L < 0, L + N > S_max, n > N - 1, node ids not strictly increasing
+ * within [1, N)) is left as it is with new_len[b] = -1.  Entries at slots
+ * >= new_len[b] are unspecified afterwards.
+ *
+ *   k_cache, v_cache  [layers][B, H, S_max, d] bf16, 16-byte aligned; layer l
+ *                  starts layer_stride elements after layer l - 1 (ignored
+ *                  when layers == 1; else >= B H S_max d, a multiple of 8).
+ *   prefix_len     [B] int32, the L of the round.
+ *   num_accepted   [B] int32, as the verify call returned it.
+ *   path_nodes     [B, path_stride] int32 accepted node ids (spec_verify_tree's
+ *                  path_nodes, path_stride = N - 1), or NULL for a linear round
+ *                  (a chain: nothing moves, only new_len is written).
+ *   N 1..64, d 8..256 (a multiple of 8), S_max >= N.
+ *   new_len        [B] int32 out.
+ * Work items: one per (layer, b); each thread moves 16-byte columns of one head.
+ */
+int spec_verify_kv_commit(void* k_cache, void* v_cache, int layers, long long layer_stride,
+                          const int32_t* prefix_len, const int32_t* num_accepted,
+                          const int32_t* path_nodes, int path_stride, int B, int H, int N, int d,
+                          int S_max, int32_t* new_len, hipStream_t stream);
+
+/*
  * Diagnostic: the raw Philox-4x32-10 words the verify calls draw, for
  * n_rows rows (row id row_ids[r], or r when NULL) and slots 0..n_slots-1:
  * out_words[(r * n_slots + s) * 4 + w] = word w of counter
@@ -236,9 +268,10 @@ int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_i
 
 /*
  * Diagnostic timing hook (for benchmarks): the next spec_verify_linear,
- * spec_verify_tree or spec_verify_attn call attaches `begin` and `end` to the
- * dispatch of its dominant kernel (the vocabulary pass, or the attention
- * kernel), so the events bracket that kernel alone, as a profiler sees it;
+ * spec_verify_tree, spec_verify_attn or spec_verify_kv_commit call attaches
+ * `begin` and `end` to the dispatch of its dominant kernel (the vocabulary
+ * pass, the attention kernel or the commit kernel), so the events bracket
+ * that kernel alone, as a profiler sees it;
  * then the hook forgets both.  Either may be NULL to clear the hook.  Not
  * for use under stream capture.  Process-wide and not thread-safe; it
  * changes no output and skips no work.

@@ -67,6 +67,9 @@ def library():
     L.spec_verify_profile_next.argtypes = [vp, vp]
     L.spec_verify_philox_words.restype = i32
     L.spec_verify_philox_words.argtypes = [u64, u64, vp, i32, i32, vp, vp]
+    L.spec_verify_kv_commit.restype = i32
+    L.spec_verify_kv_commit.argtypes = [vp, vp, i32, ctypes.c_longlong, vp, vp, vp, i32, i32, i32,
+                                        i32, i32, i32, vp, vp]
     _lib = L
     return L
 
@@ -241,6 +244,48 @@ def verify_attn(q, k_cache, v_cache, prefix_len, parents=None, scale=None, want_
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_attn")
     return outputs
+
+
+def kv_commit(k_cache, v_cache, prefix_len, num_accepted, path_nodes=None, n_new=None,
+              new_len=None, stream=None):
+    """KV-cache commit after a verify round (see spec_verify_kv_commit), in place.
+
+    k_cache, v_cache: [B, H, S_max, d] or [layers, B, H, S_max, d] bf16;
+    prefix_len, num_accepted: [B] int32; path_nodes: [B, N-1] int32 from
+    verify_tree, or None for a linear round (then n_new = gamma + 1 must be
+    given).  Returns new_len [B] int32.
+    """
+    L = library()
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, name, torch.bfloat16)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if k_cache.dim() == 4:
+        layers, (B, H, S_max, d) = 1, k_cache.shape
+    elif k_cache.dim() == 5:
+        layers, B, H, S_max, d = k_cache.shape
+    else:
+        raise ValueError("k_cache must be [B, H, S_max, d] or [layers, B, H, S_max, d]")
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(num_accepted, "num_accepted", torch.int32)
+    if path_nodes is not None:
+        _dev(path_nodes, "path_nodes", torch.int32)
+        if n_new is None:
+            n_new = path_nodes.shape[1] + 1
+        stride = path_nodes.shape[1]
+    else:
+        stride = 0
+    if n_new is None:
+        raise ValueError("n_new is needed for a linear round")
+    if new_len is None:
+        new_len = torch.empty(B, dtype=torch.int32, device=k_cache.device)
+    st = L.spec_verify_kv_commit(
+        _ptr(k_cache), _ptr(v_cache), layers, B * H * S_max * d, _ptr(prefix_len),
+        _ptr(num_accepted), _ptr(path_nodes), stride, B, H, int(n_new), d, S_max, _ptr(new_len),
+        _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_kv_commit")
+    return new_len
 
 
 def profile_next(begin_event, end_event, ensure_created=True):

@@ -267,6 +267,41 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
   return SV_OK;
 }
 
+int spec_verify_kv_commit(void* k_cache, void* v_cache, int layers, long long layer_stride,
+                          const int32_t* prefix_len, const int32_t* num_accepted,
+                          const int32_t* path_nodes, int path_stride, int B, int H, int N, int d,
+                          int S_max, int32_t* new_len, hipStream_t stream) {
+  if (layers < 1 || B < 0 || H < 1 || N < 1 || N > SV_MAX_TREE_NODES || S_max < N)
+    return SV_ERR_INVALID_ARG;
+  if (d < 8 || d > 256 || d % 8 != 0) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!k_cache || !v_cache || !prefix_len || !num_accepted || !new_len) return SV_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return SV_ERR_INVALID_ARG;
+  const long long per_layer = (long long)B * H * S_max * d;
+  if (layers > 1 && (layer_stride < per_layer || layer_stride % 8 != 0)) return SV_ERR_INVALID_ARG;
+  if (path_nodes && path_stride < N - 1) return SV_ERR_INVALID_ARG;
+  if ((long long)layers * B >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  sv::KvArgs a{};
+  a.k = (uint16_t*)k_cache;
+  a.v = (uint16_t*)v_cache;
+  a.layer_stride = layers > 1 ? layer_stride : per_layer;
+  a.prefix_len = prefix_len;
+  a.num_accepted = num_accepted;
+  a.path = path_nodes;
+  a.path_stride = path_stride;
+  a.layers = layers;
+  a.B = B;
+  a.H = H;
+  a.S_max = S_max;
+  a.d = d;
+  a.n_new = N;
+  a.new_len = new_len;
+  hipEvent_t eb = g_prof_begin, ee = g_prof_end;
+  g_prof_begin = g_prof_end = nullptr;
+  if (sv::launch_kv_commit(a, stream, eb, ee) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
 int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids, int n_rows,
                              int n_slots, uint32_t* out_words, hipStream_t stream) {
   if (n_rows < 0 || n_slots < 0) return SV_ERR_INVALID_ARG;

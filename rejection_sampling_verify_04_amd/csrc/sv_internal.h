@@ -103,6 +103,18 @@ struct AttnArgs {
   float* lse;
 };
 
+struct KvArgs {
+  uint16_t* k;           // [layers][B][H][S_max][d] bf16 (layers layer_stride elements apart)
+  uint16_t* v;
+  long long layer_stride;
+  const int* prefix_len;
+  const int* num_accepted;
+  const int* path;       // [B][path_stride] accepted node ids, or null (a chain)
+  int path_stride;
+  int layers, B, H, S_max, d, n_new;
+  int* new_len;
+};
+
 // Workgroups of a kernel that fit on the current device at once (cached per
 // kernel slot and device; slots are unique across the library).
 template <typename K>
@@ -131,5 +143,6 @@ hipError_t launch_tree_finish(int dtype, const TreeArgs& a, hipStream_t st);
 hipError_t launch_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids,
                                int n_rows, int n_slots, uint32_t* out, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_kv_commit(const KvArgs& a, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace sv

@@ -99,6 +99,15 @@ def test_tree_and_attn_host_validation(lib):
     assert lib.spec_verify_attn(p, p, p, p, None, 2, 4, 65, 128, 100, 0.1, p, None, None) == -1
     assert lib.spec_verify_attn(p, p, p, p, None, 2, 4, 8, 128, 4, 0.1, p, None, None) == -1
     assert lib.spec_verify_attn(p, p, p, p, None, 0, 4, 8, 128, 100, 0.1, p, None, None) == 0
+    kv = lambda *a: lib.spec_verify_kv_commit(p, p, *a)
+    # layers, layer_stride, prefix_len, num_accepted, path, stride, B, H, N, d, S_max, new_len, stream
+    assert kv(1, 0, p, p, None, 0, 0, 4, 8, 128, 100, p, None) == 0       # empty batch: no-op
+    assert kv(1, 0, p, p, None, 0, 2, 4, 65, 128, 100, p, None) == -1     # N > 64
+    assert kv(1, 0, p, p, None, 0, 2, 4, 8, 100, 100, p, None) == -1     # d not a multiple of 8
+    assert kv(1, 0, p, p, None, 0, 2, 4, 8, 128, 4, p, None) == -1       # S_max < N
+    assert kv(2, 16, p, p, None, 0, 2, 4, 8, 128, 100, p, None) == -1     # layer stride too small
+    assert kv(1, 0, p, p, p, 3, 2, 4, 8, 128, 100, p, None) == -1         # path stride < N - 1
+    assert kv(1, 0, None, p, None, 0, 2, 4, 8, 128, 100, p, None) == -1   # no prefix lengths
     assert lib.spec_verify_philox_words(0, 0, None, 0, 5, None, None) == 0
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, None, None) == -1
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, ctypes.c_void_p(8), None) == -1
