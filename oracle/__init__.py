@@ -28,3 +28,4 @@ from .tree import (verify_tree_topk, verify_tree_topk_row,  # noqa: F401
                    verify_tree_sampled_wor, verify_tree_sampled_wor_row, TreeRowResult)
 from .attention import verify_attention, attention_head, ancestor_mask  # noqa: F401
 from .kv import kv_commit, commit_row_plan  # noqa: F401
+from . import telemetry  # noqa: F401
