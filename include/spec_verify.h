@@ -258,6 +258,57 @@ int spec_verify_kv_commit(void* k_cache, void* v_cache, int layers, long long la
                           int S_max, int32_t* new_len, hipStream_t stream);
 
 /*
+ * Round telemetry (blog.lonae.com/posts/2026-draft-model-kv-jDwzYp,
+ * observability paragraphs: acceptance rate and its per-request histogram,
+ * which must keep the low and the high peak apart; Speculative Efficiency;
+ * Tree Width Effective).  Counters are added on the device into a caller-
+ * owned sv_telemetry block (zero it to open a window); the summary call
+ * derives the signals from a block.
+ *
+ * Per row of a verify call (rows with num_accepted < 0, or a malformed
+ * shape, only add to error_rows): rounds += 1; drafted += the round's draft
+ * steps (gamma_b for a linear row, the depth of the deepest node for a
+ * tree); accepted += num_accepted; full_accepts += 1 when every step was
+ * accepted (a tree walk that ended on a leaf); acc_rate_hist[k] for
+ * accepted / drafted in [k/20, (k+1)/20) (1.0 in the last bin; rows with no
+ * draft step not binned); accepted_hist[min(n, 64)]; trees also add their
+ * root-to-leaf paths to tree_paths, those through the first accepted node
+ * to tree_paths_hit, and the rank of every accepted node among its
+ * siblings (0 = first child tested) to sibling_rank_hist.
+ */
+#define SV_TELEM_ACC_BINS 20
+#define SV_TELEM_POS_BINS 65
+#define SV_TELEM_RANK_BINS 64
+typedef struct sv_telemetry {
+  uint64_t rounds, error_rows, drafted, accepted, full_accepts, tree_paths, tree_paths_hit;
+  uint64_t acc_rate_hist[SV_TELEM_ACC_BINS];
+  uint64_t accepted_hist[SV_TELEM_POS_BINS];
+  uint64_t sibling_rank_hist[SV_TELEM_RANK_BINS];
+} sv_telemetry;
+
+/* Linear rounds: num_accepted [B] and draft_offsets [B+1] as given to and
+ * returned by spec_verify_linear. */
+int spec_verify_telemetry_linear(const int32_t* num_accepted, const int32_t* draft_offsets,
+                                 int B, sv_telemetry* acc, hipStream_t stream);
+
+/* Tree rounds: num_accepted [B] and path_nodes [B, N-1] as returned by
+ * spec_verify_tree for parents [B, N] and n_nodes [B] (NULL: N). */
+int spec_verify_telemetry_tree(const int32_t* num_accepted, const int32_t* path_nodes,
+                               const int32_t* parents, const int32_t* n_nodes, int B, int N,
+                               sv_telemetry* acc, hipStream_t stream);
+
+/* Derived signals of a block, out[8] float64 (device memory):
+ *   [0] acceptance_rate = accepted / drafted
+ *   [1] avg_accepted_tokens = accepted / rounds
+ *   [2] draft_steps = drafted / rounds
+ *   [3] Speculative Efficiency = [0] * [1] / [2] (with these readings it is
+ *       (accepted / drafted)^2, at most 1)
+ *   [4] Tree Width Effective = tree_paths_hit / tree_paths
+ *   [5..7] bins of acc_rate_hist holding its P50, P95, P99 rows (-1 if empty)
+ * NaN where a ratio has no rows. */
+int spec_verify_telemetry_summary(const sv_telemetry* acc, double* out, hipStream_t stream);
+
+/*
  * Diagnostic: the raw Philox-4x32-10 words the verify calls draw, for
  * n_rows rows (row id row_ids[r], or r when NULL) and slots 0..n_slots-1:
  * out_words[(r * n_slots + s) * 4 + w] = word w of counter

@@ -67,6 +67,12 @@ def library():
     L.spec_verify_profile_next.argtypes = [vp, vp]
     L.spec_verify_philox_words.restype = i32
     L.spec_verify_philox_words.argtypes = [u64, u64, vp, i32, i32, vp, vp]
+    L.spec_verify_telemetry_linear.restype = i32
+    L.spec_verify_telemetry_linear.argtypes = [vp, vp, i32, vp, vp]
+    L.spec_verify_telemetry_tree.restype = i32
+    L.spec_verify_telemetry_tree.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp]
+    L.spec_verify_telemetry_summary.restype = i32
+    L.spec_verify_telemetry_summary.argtypes = [vp, vp, vp]
     L.spec_verify_kv_commit.restype = i32
     L.spec_verify_kv_commit.argtypes = [vp, vp, i32, ctypes.c_longlong, vp, vp, vp, i32, i32, i32,
                                         i32, i32, i32, vp, vp]
@@ -286,6 +292,72 @@ def kv_commit(k_cache, v_cache, prefix_len, num_accepted, path_nodes=None, n_new
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_kv_commit")
     return new_len
+
+
+TELEMETRY_FIELDS = ["rounds", "error_rows", "drafted", "accepted", "full_accepts", "tree_paths",
+                    "tree_paths_hit"]
+TELEMETRY_BINS = [("acc_rate_hist", 20), ("accepted_hist", 65), ("sibling_rank_hist", 64)]
+TELEMETRY_WORDS = len(TELEMETRY_FIELDS) + sum(n for _, n in TELEMETRY_BINS)
+SUMMARY_FIELDS = ["acceptance_rate", "avg_accepted_tokens", "draft_steps",
+                  "speculative_efficiency", "tree_width_effective", "acc_rate_p50_bin",
+                  "acc_rate_p95_bin", "acc_rate_p99_bin"]
+
+
+def telemetry_block(device="cuda"):
+    """A zeroed sv_telemetry block (int64 words) that opens a window."""
+    return torch.zeros(TELEMETRY_WORDS, dtype=torch.int64, device=device)
+
+
+def telemetry_linear(num_accepted, draft_offsets, acc, stream=None):
+    """Add the rows of a linear verify call to `acc` (see spec_verify_telemetry_linear)."""
+    L = library()
+    _dev(num_accepted, "num_accepted", torch.int32)
+    _dev(draft_offsets, "draft_offsets", torch.int32)
+    _dev(acc, "acc", torch.int64)
+    st = L.spec_verify_telemetry_linear(_ptr(num_accepted), _ptr(draft_offsets),
+                                        num_accepted.shape[0], _ptr(acc), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_telemetry_linear")
+    return acc
+
+
+def telemetry_tree(num_accepted, path_nodes, parents, acc, n_nodes=None, stream=None):
+    """Add the rows of a tree verify call to `acc` (see spec_verify_telemetry_tree)."""
+    L = library()
+    _dev(num_accepted, "num_accepted", torch.int32)
+    _dev(path_nodes, "path_nodes", torch.int32)
+    _dev(parents, "parents", torch.int32)
+    _dev(acc, "acc", torch.int64)
+    if n_nodes is not None:
+        _dev(n_nodes, "n_nodes", torch.int32)
+    B, N = parents.shape
+    st = L.spec_verify_telemetry_tree(_ptr(num_accepted), _ptr(path_nodes), _ptr(parents),
+                                      _ptr(n_nodes), B, N, _ptr(acc), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_telemetry_tree")
+    return acc
+
+
+def telemetry_summary(acc, stream=None):
+    """The derived signals of a block, [8] float64 on the device (SUMMARY_FIELDS order)."""
+    L = library()
+    _dev(acc, "acc", torch.int64)
+    out = torch.empty(8, dtype=torch.float64, device=acc.device)
+    st = L.spec_verify_telemetry_summary(_ptr(acc), _ptr(out), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_telemetry_summary")
+    return out
+
+
+def telemetry_fields(acc):
+    """Name the words of a block (host copy; no arithmetic)."""
+    words = acc.cpu().tolist()
+    out = dict(zip(TELEMETRY_FIELDS, words[:len(TELEMETRY_FIELDS)]))
+    i = len(TELEMETRY_FIELDS)
+    for name, n in TELEMETRY_BINS:
+        out[name] = words[i:i + n]
+        i += n
+    return out
 
 
 def profile_next(begin_event, end_event, ensure_created=True):

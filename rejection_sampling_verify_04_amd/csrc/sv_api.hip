@@ -302,6 +302,35 @@ int spec_verify_kv_commit(void* k_cache, void* v_cache, int layers, long long la
   return SV_OK;
 }
 
+int spec_verify_telemetry_linear(const int32_t* num_accepted, const int32_t* draft_offsets,
+                                 int B, sv_telemetry* acc, hipStream_t stream) {
+  if (B < 0) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!num_accepted || !draft_offsets || !acc || ((uintptr_t)acc & 7u)) return SV_ERR_INVALID_ARG;
+  if (sv::launch_telemetry_linear(num_accepted, draft_offsets, B, acc, stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_telemetry_tree(const int32_t* num_accepted, const int32_t* path_nodes,
+                               const int32_t* parents, const int32_t* n_nodes, int B, int N,
+                               sv_telemetry* acc, hipStream_t stream) {
+  if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!num_accepted || !parents || !acc || ((uintptr_t)acc & 7u)) return SV_ERR_INVALID_ARG;
+  if (N > 1 && !path_nodes) return SV_ERR_INVALID_ARG;
+  if (sv::launch_telemetry_tree(num_accepted, path_nodes, parents, n_nodes, B, N, acc, stream) !=
+      hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_telemetry_summary(const sv_telemetry* acc, double* out, hipStream_t stream) {
+  if (!acc || !out || ((uintptr_t)acc & 7u) || ((uintptr_t)out & 7u)) return SV_ERR_INVALID_ARG;
+  if (sv::launch_telemetry_summary(acc, out, stream) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
 int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids, int n_rows,
                              int n_slots, uint32_t* out_words, hipStream_t stream) {
   if (n_rows < 0 || n_slots < 0) return SV_ERR_INVALID_ARG;

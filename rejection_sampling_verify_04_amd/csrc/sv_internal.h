@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <atomic>
 
+#include "spec_verify.h"
 #include "sv_common.h"
 
 namespace sv {
@@ -144,5 +145,11 @@ hipError_t launch_philox_words(uint64_t seed, uint64_t step, const uint32_t* row
                                int n_rows, int n_slots, uint32_t* out, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_kv_commit(const KvArgs& a, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_telemetry_linear(const int* num_accepted, const int* off, int B,
+                                   sv_telemetry* acc, hipStream_t st);
+hipError_t launch_telemetry_tree(const int* num_accepted, const int* path, const int* parents,
+                                 const int* n_nodes, int B, int N, sv_telemetry* acc,
+                                 hipStream_t st);
+hipError_t launch_telemetry_summary(const sv_telemetry* acc, double* out, hipStream_t st);
 
 }  // namespace sv

@@ -1,0 +1,187 @@
+// Round telemetry of the verify step, gfx950: counters accumulated on the
+// device over a window of calls, and the derived health signals.
+//
+// The signals are those blog.lonae.com/posts/2026-draft-model-kv-jDwzYp
+// names for a speculative deployment (observability paragraphs): the
+// acceptance rate with a per-request histogram that keeps the low and the
+// high peak apart, Speculative Efficiency = acceptance_rate *
+// avg_accepted_tokens / draft_steps, and Tree Width Effective = paths hit /
+// paths offered.  draft_steps of a round is gamma for a linear row and the
+// depth of the deepest node for a tree; a tree path is hit when the round
+// accepted its first node below the root.
+//
+// Linear rows: one thread per row, counts gathered in LDS, one device-scope
+// atomic add per non-zero counter per work item.  Tree rows: one wave per
+// tree, one lane per node.
+#include <hip/hip_runtime.h>
+
+#include "spec_verify.h"
+#include "sv_common.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kTmFields = 7;
+constexpr int kTmCounters = kTmFields + SV_TELEM_ACC_BINS + SV_TELEM_POS_BINS + SV_TELEM_RANK_BINS;
+static_assert(sizeof(sv_telemetry) == kTmCounters * sizeof(uint64_t), "flat counter block");
+constexpr int kTmRounds = 0, kTmErrors = 1, kTmDrafted = 2, kTmAccepted = 3, kTmFull = 4,
+              kTmPaths = 5, kTmPathsHit = 6, kTmRate = kTmFields,
+              kTmPos = kTmRate + SV_TELEM_ACC_BINS, kTmRank = kTmPos + SV_TELEM_POS_BINS;
+
+// Bin of n / g (g > 0): the k with k / 20 <= n / g < (k + 1) / 20, in integers.
+__device__ __forceinline__ int rate_bin(int n, int g) {
+  return min(SV_TELEM_ACC_BINS - 1, (SV_TELEM_ACC_BINS * n) / g);
+}
+
+__global__ __launch_bounds__(256) void telemetry_linear_kernel(const int* num_accepted,
+                                                               const int* off, int B,
+                                                               unsigned long long* acc) {
+  __shared__ uint32_t s_c[kTmCounters];
+  for (int i = threadIdx.x; i < kTmCounters; i += 256) s_c[i] = 0u;
+  __syncthreads();
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < B) {
+    const int n = num_accepted[b];
+    const int g = off[b + 1] - off[b];
+    if (n < 0 || g < 0 || n > g) {
+      atomicAdd(&s_c[kTmErrors], 1u);
+    } else {
+      atomicAdd(&s_c[kTmRounds], 1u);
+      atomicAdd(&s_c[kTmDrafted], (uint32_t)g);
+      atomicAdd(&s_c[kTmAccepted], (uint32_t)n);
+      if (n == g) atomicAdd(&s_c[kTmFull], 1u);
+      if (g > 0) atomicAdd(&s_c[kTmRate + rate_bin(n, g)], 1u);
+      atomicAdd(&s_c[kTmPos + min(n, SV_TELEM_POS_BINS - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTmCounters; i += 256)
+    if (s_c[i]) atomicAdd(&acc[i], (unsigned long long)s_c[i]);
+}
+
+__global__ __launch_bounds__(64) void telemetry_tree_kernel(const int* num_accepted,
+                                                            const int* path, const int* parents,
+                                                            const int* n_nodes, int N,
+                                                            unsigned long long* acc) {
+  __shared__ int s_par[kMaxNodes], s_depth[kMaxNodes];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int nn = n_nodes ? n_nodes[b] : N;
+  const int n = num_accepted[b];
+  const bool node = lane < nn && lane < N;
+  int par = -1;
+  if (node && lane > 0) par = parents[(long long)b * N + lane];
+  const bool shape_ok = nn >= 1 && nn <= N && n >= 0 && n < nn;
+  const bool bad_par = node && lane > 0 && (par < 0 || par >= lane);
+  int pj = 0;   // this lane's accepted node (lane < n)
+  if (lane < n && lane < N - 1 && shape_ok) pj = path[(long long)b * (N - 1) + lane];
+  const bool bad_path = lane < n && shape_ok && (pj < 1 || pj >= nn);
+  if (!shape_ok || __ballot(bad_par) || __ballot(bad_path)) {
+    if (lane == 0) atomicAdd(&acc[kTmErrors], 1ull);
+    return;
+  }
+  s_par[lane] = node ? par : -1;
+  __syncthreads();
+  // depth: walk up the ancestors (parents precede children)
+  int depth = 0;
+  if (node) {
+    for (int x = lane; x > 0; x = s_par[x]) ++depth;
+  }
+  s_depth[lane] = node ? depth : 0;
+  const unsigned long long inner = [&] {
+    unsigned long long m = 0ull;
+    for (int c = 1; c < nn; ++c) m |= 1ull << s_par[c];
+    return m;
+  }();
+  __syncthreads();
+  // rank among the siblings (test order = node index)
+  int rank = 0;
+  if (node && lane > 0)
+    for (int y = 1; y < lane; ++y) rank += s_par[y] == par;
+  int g = depth;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) g = max(g, __shfl_xor(g, o));
+  const bool leaf = node && !((inner >> lane) & 1ull);
+  const int first = __shfl(pj, 0);
+  bool hit = false;
+  if (leaf && n > 0) {
+    int x = lane;
+    while (x > 0 && s_depth[x] > 1) x = s_par[x];
+    hit = x == first;
+  }
+  const int n_leaves = __popcll(__ballot(leaf));
+  const int n_hit = __popcll(__ballot(hit));
+  const int last = n > 0 ? __shfl(pj, n - 1) : 0;
+  const int rank_acc = __shfl(rank, pj);   // rank of this lane's accepted node
+  if (lane < n) atomicAdd(&acc[kTmRank + min(rank_acc, SV_TELEM_RANK_BINS - 1)], 1ull);
+  if (lane == 0) {
+    atomicAdd(&acc[kTmRounds], 1ull);
+    atomicAdd(&acc[kTmDrafted], (unsigned long long)g);
+    atomicAdd(&acc[kTmAccepted], (unsigned long long)n);
+    if (!((inner >> last) & 1ull)) atomicAdd(&acc[kTmFull], 1ull);
+    if (g > 0) atomicAdd(&acc[kTmRate + rate_bin(n, g)], 1ull);
+    atomicAdd(&acc[kTmPos + min(n, SV_TELEM_POS_BINS - 1)], 1ull);
+    atomicAdd(&acc[kTmPaths], (unsigned long long)n_leaves);
+    atomicAdd(&acc[kTmPathsHit], (unsigned long long)n_hit);
+  }
+}
+
+// The derived signals of a window (one thread): acceptance rate, average
+// accepted tokens, draft steps, Speculative Efficiency, Tree Width Effective
+// (NaN where undefined), and the P50 / P95 / P99 bins of the per-row
+// acceptance histogram (-1 when empty).
+__global__ void telemetry_summary_kernel(const unsigned long long* acc, double* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const double nan = __builtin_nan("");
+  const double rounds = (double)acc[kTmRounds], drafted = (double)acc[kTmDrafted];
+  const double accepted = (double)acc[kTmAccepted], paths = (double)acc[kTmPaths];
+  const double rate = drafted > 0.0 ? accepted / drafted : nan;
+  const double avg = rounds > 0.0 ? accepted / rounds : nan;
+  const double steps = rounds > 0.0 ? drafted / rounds : nan;
+  out[0] = rate;
+  out[1] = avg;
+  out[2] = steps;
+  out[3] = (drafted > 0.0 && rounds > 0.0) ? rate * avg / steps : nan;
+  out[4] = paths > 0.0 ? (double)acc[kTmPathsHit] / paths : nan;
+  unsigned long long tot = 0ull;
+  for (int k = 0; k < SV_TELEM_ACC_BINS; ++k) tot += acc[kTmRate + k];
+  const int qs[3] = {50, 95, 99};
+  for (int j = 0; j < 3; ++j) {
+    int bin = -1;
+    if (tot) {
+      // first bin whose cumulative count reaches q% of the rows
+      unsigned long long run = 0ull;
+      bin = SV_TELEM_ACC_BINS - 1;
+      for (int k = 0; k < SV_TELEM_ACC_BINS; ++k) {
+        run += acc[kTmRate + k];
+        if (run * 100ull >= (unsigned long long)qs[j] * tot) {
+          bin = k;
+          break;
+        }
+      }
+    }
+    out[5 + j] = (double)bin;
+  }
+}
+
+hipError_t launch_telemetry_linear(const int* num_accepted, const int* off, int B,
+                                   sv_telemetry* acc, hipStream_t st) {
+  telemetry_linear_kernel<<<dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st>>>(
+      num_accepted, off, B, (unsigned long long*)acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_telemetry_tree(const int* num_accepted, const int* path, const int* parents,
+                                 const int* n_nodes, int B, int N, sv_telemetry* acc,
+                                 hipStream_t st) {
+  telemetry_tree_kernel<<<dim3((unsigned)B), dim3(64), 0, st>>>(num_accepted, path, parents,
+                                                              n_nodes, N,
+                                                              (unsigned long long*)acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_telemetry_summary(const sv_telemetry* acc, double* out, hipStream_t st) {
+  telemetry_summary_kernel<<<dim3(1), dim3(64), 0, st>>>((const unsigned long long*)acc, out);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -28,6 +28,16 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
 
 
+def test_telemetry_block_layout():
+    import rejection_sampling_verify_04_amd as sv
+    from oracle import telemetry as TM
+    # the binding's word layout is the header's struct: 7 counters then the bins
+    assert sv.TELEMETRY_WORDS == 7 + TM.ACC_BINS + TM.POS_BINS + TM.RANK_BINS
+    assert sv.TELEMETRY_FIELDS == TM.FIELDS
+    text = open(HEADER).read()
+    assert "uint64_t rounds, error_rows, drafted, accepted, full_accepts, tree_paths, tree_paths_hit;" in text
+
+
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ["spec_verify_linear", "spec_verify_tree", "spec_verify_attn",
@@ -108,6 +118,12 @@ def test_tree_and_attn_host_validation(lib):
     assert kv(2, 16, p, p, None, 0, 2, 4, 8, 128, 100, p, None) == -1     # layer stride too small
     assert kv(1, 0, p, p, p, 3, 2, 4, 8, 128, 100, p, None) == -1         # path stride < N - 1
     assert kv(1, 0, None, p, None, 0, 2, 4, 8, 128, 100, p, None) == -1   # no prefix lengths
+    assert lib.spec_verify_telemetry_linear(p, p, 0, p, None) == 0          # empty: no-op
+    assert lib.spec_verify_telemetry_linear(p, None, 4, p, None) == -1
+    assert lib.spec_verify_telemetry_linear(p, p, 4, ctypes.c_void_p(260), None) == -1   # misaligned
+    assert lib.spec_verify_telemetry_tree(p, p, p, None, 4, 65, p, None) == -1     # N > 64
+    assert lib.spec_verify_telemetry_tree(p, None, p, None, 4, 8, p, None) == -1   # no paths
+    assert lib.spec_verify_telemetry_summary(None, p, None) == -1
     assert lib.spec_verify_philox_words(0, 0, None, 0, 5, None, None) == 0
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, None, None) == -1
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, ctypes.c_void_p(8), None) == -1
