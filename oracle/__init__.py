@@ -29,3 +29,4 @@ from .tree import (verify_tree_topk, verify_tree_topk_row,  # noqa: F401
 from .attention import verify_attention, attention_head, ancestor_mask  # noqa: F401
 from .kv import kv_commit, commit_row_plan  # noqa: F401
 from . import telemetry  # noqa: F401
+from . import control  # noqa: F401
