@@ -30,3 +30,4 @@ from .attention import verify_attention, attention_head, ancestor_mask  # noqa: 
 from .kv import kv_commit, commit_row_plan  # noqa: F401
 from . import telemetry  # noqa: F401
 from . import control  # noqa: F401
+from . import draft  # noqa: F401
