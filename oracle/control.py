@@ -34,7 +34,8 @@ def push(word, n, g):
 
 
 def gamma_of(word, temp=None, couple_temperature=False):
-    if couple_temperature and temp is not None and temp > 0.8:
+    # the temperature is a float32 input: the threshold test is taken in float32
+    if couple_temperature and temp is not None and np.float32(temp) > np.float32(0.8):
         return 1
     hist, count = word & 0xFFFF, (word >> 16) & 0x1F
     if count == 0:

@@ -58,3 +58,5 @@ def test_temperature_coupling_and_offsets():
     assert list(off) == [0, 8, 9, 10]
     h, g, off = C.gamma_update(hist, np.array([2, 0, -1]), np.array([8, 2, 4]))
     assert list(g) == [8, 2, 4] and list(off) == [0, 8, 10, 14]
+    # 0.8 itself (as the float32 a caller passes) is not above 0.8
+    assert C.gamma_of(word(0, 16), np.float32(0.8), True) == 2
