@@ -87,6 +87,8 @@ extern "C" {
 
 #define SV_MAX_GAMMA 64
 #define SV_MAX_TREE_NODES 64
+#define SV_MAX_TOPK 64
+#define SV_MAX_CANDIDATES 1024
 #define SV_WORKSPACE_ALIGN 256
 
 /* Library version, (major << 16) | minor. */
@@ -307,6 +309,69 @@ int spec_verify_telemetry_tree(const int32_t* num_accepted, const int32_t* path_
  *   [5..7] bins of acc_rate_hist holding its P50, P95, P99 rows (-1 if empty)
  * NaN where a ratio has no rows. */
 int spec_verify_telemetry_summary(const sv_telemetry* acc, double* out, hipStream_t stream);
+
+/*
+ * Draft candidates (blog.lonae.com/posts/2026-draft-model-kv-jDwzYp,
+ * tree-attention paragraphs: every draft position branches into the
+ * draft's top-k candidates).  For each of R draft rows [R, V] `dtype`, the
+ * k tokens of largest logit, largest first (ties to the lower id), and
+ * their log-probabilities log softmax(x / T)[token] at the row's
+ * temperature (temp [R], NULL for 1; T = 0: 0 for the first token and -inf
+ * for the rest; a negative or non-finite T: tokens -1, NaN).  1 <= k <= 64,
+ * k <= V.  tokens, logprob: [R, k].  One work item per row (a radix select
+ * on order-preserving keys, then the keys above the k-th and, in index
+ * order, enough keys equal to it).
+ */
+int spec_verify_draft_topk(const void* logits, int dtype, int R, int V, int k,
+                           const float* temp, int32_t* tokens, float* logprob, hipStream_t stream);
+
+/*
+ * Tree pruning (same paragraphs: the production tree is pruned by
+ * cumulative draft probability up to a node budget, not fully expanded).
+ * Each batch row holds a forest of C <= 1024 drafted candidates: candidate
+ * i has parent cand_parent[i] (-1: a child of the root, else an earlier
+ * candidate), token cand_token[i] and cand_logq[i] = log q of the token
+ * under its parent's draft row (<= 0).  The kept tree is the n_max - 1
+ * candidates of largest cumulative log q (the sum along the path), ties to
+ * the shallower, then the earlier parent, then the lower sibling rank, with
+ * -inf never kept; it is closed under parents.  Its nodes are numbered
+ * breadth first (depth, then the parent's new index, then sibling rank)
+ * behind the root, node 0 (parent -1, token -1, cumulative 0): parents and
+ * tokens [B, n_max] are spec_verify_tree's inputs, cum_logprob [B, n_max]
+ * float, n_nodes [B] (0 for a forest whose parents are malformed), and
+ * n_pass [B] (may be NULL) the kept nodes with cumulative probability
+ * >= tau.  Slots past n_nodes hold -1 (cumulative -inf).  n_cand [B] may
+ * be NULL (C everywhere).  n_max 1..64.
+ */
+int spec_verify_tree_prune(const int32_t* cand_parent, const int32_t* cand_token,
+                           const float* cand_logq, const int32_t* n_cand, int B, int C, int n_max,
+                           double tau, int32_t* parents, int32_t* tokens, float* cum_logprob,
+                           int32_t* n_nodes, int32_t* n_pass, hipStream_t stream);
+
+/*
+ * Dynamic speculation length (blog.lonae.com/posts/2026-draft-model-kv-jDwzYp,
+ * bimodal-acceptance paragraph): after a linear round, each request's
+ * acceptance over its last 16 steps sets its next gamma: 8 above 60%, 4
+ * from 30% to 60%, 2 below 30%; with couple_temperature, a request whose
+ * temp_target is above 0.8 gets gamma 1.  A step is one tested draft
+ * position: a round that accepted n of its gamma_b drafts adds n accepted
+ * steps, then one rejected step if n < gamma_b; a flagged round (n < 0)
+ * adds nothing.  The rate is taken over the last min(16, steps seen)
+ * steps; a request with none yet gets 4.
+ *
+ *   history            [B] uint32 in/out: bits 0..15 the last steps (bit 0
+ *                      the newest, 1 = accepted), bits 16..20 how many of
+ *                      them are valid (0..16).  Zero for a new request.
+ *   num_accepted       [B] as returned by spec_verify_linear.
+ *   draft_offsets      [B+1] the offsets of that round.
+ *   temp_target        [B] or NULL (required with couple_temperature).
+ *   gamma_next         [B] int32 out.
+ *   draft_offsets_next [B+1] int32 out (running sum of gamma_next), or NULL.
+ */
+int spec_verify_gamma_update(uint32_t* history, const int32_t* num_accepted,
+                             const int32_t* draft_offsets, const float* temp_target,
+                             int couple_temperature, int B, int32_t* gamma_next,
+                             int32_t* draft_offsets_next, hipStream_t stream);
 
 /*
  * Diagnostic: the raw Philox-4x32-10 words the verify calls draw, for

@@ -73,6 +73,13 @@ def library():
     L.spec_verify_telemetry_tree.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp]
     L.spec_verify_telemetry_summary.restype = i32
     L.spec_verify_telemetry_summary.argtypes = [vp, vp, vp]
+    L.spec_verify_draft_topk.restype = i32
+    L.spec_verify_draft_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.spec_verify_tree_prune.restype = i32
+    L.spec_verify_tree_prune.argtypes = [vp, vp, vp, vp, i32, i32, i32, ctypes.c_double, vp, vp,
+                                         vp, vp, vp, vp]
+    L.spec_verify_gamma_update.restype = i32
+    L.spec_verify_gamma_update.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
     L.spec_verify_kv_commit.restype = i32
     L.spec_verify_kv_commit.argtypes = [vp, vp, i32, ctypes.c_longlong, vp, vp, vp, i32, i32, i32,
                                         i32, i32, i32, vp, vp]
@@ -292,6 +299,84 @@ def kv_commit(k_cache, v_cache, prefix_len, num_accepted, path_nodes=None, n_new
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_kv_commit")
     return new_len
+
+
+def draft_topk(logits, k, temp=None, stream=None):
+    """Top-k candidates of draft rows (see spec_verify_draft_topk).
+
+    logits: [R, V] bf16 or fp32; temp: [R] float32 or None (1).
+    Returns (tokens [R, k] int32, logprob [R, k] float32).
+    """
+    L = library()
+    _dev(logits, "logits")
+    dt = _logit_code(logits, "logits")
+    R, V = logits.shape
+    if temp is not None:
+        _dev(temp, "temp", torch.float32)
+    tokens = torch.empty((R, k), dtype=torch.int32, device=logits.device)
+    logprob = torch.empty((R, k), dtype=torch.float32, device=logits.device)
+    st = L.spec_verify_draft_topk(_ptr(logits), dt, R, V, int(k), _ptr(temp), _ptr(tokens),
+                                  _ptr(logprob), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_draft_topk")
+    return tokens, logprob
+
+
+def tree_prune(cand_parent, cand_token, cand_logq, n_max, tau=0.1, n_cand=None, stream=None):
+    """Prune drafted candidate forests into verify trees (see spec_verify_tree_prune).
+
+    cand_*: [B, C] (int32, int32, float32).  Returns dict with parents, tokens
+    [B, n_max] int32, cum_logprob [B, n_max] float32, n_nodes [B], n_pass [B].
+    """
+    L = library()
+    _dev(cand_parent, "cand_parent", torch.int32)
+    _dev(cand_token, "cand_token", torch.int32)
+    _dev(cand_logq, "cand_logq", torch.float32)
+    if n_cand is not None:
+        _dev(n_cand, "n_cand", torch.int32)
+    B, C = cand_parent.shape
+    dev = cand_parent.device
+    out = dict(parents=torch.empty((B, n_max), dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, n_max), dtype=torch.int32, device=dev),
+               cum_logprob=torch.empty((B, n_max), dtype=torch.float32, device=dev),
+               n_nodes=torch.empty(B, dtype=torch.int32, device=dev),
+               n_pass=torch.empty(B, dtype=torch.int32, device=dev))
+    st = L.spec_verify_tree_prune(_ptr(cand_parent), _ptr(cand_token), _ptr(cand_logq),
+                                  _ptr(n_cand), B, C, int(n_max), float(tau),
+                                  _ptr(out["parents"]), _ptr(out["tokens"]),
+                                  _ptr(out["cum_logprob"]), _ptr(out["n_nodes"]),
+                                  _ptr(out["n_pass"]), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_tree_prune")
+    return out
+
+
+def gamma_update(history, num_accepted, draft_offsets, temp_target=None,
+                 couple_temperature=False, gamma_next=None, draft_offsets_next=None,
+                 stream=None):
+    """Dynamic speculation length after a linear round (see spec_verify_gamma_update).
+
+    history: [B] int32 words updated in place (zeros for new requests).
+    Returns (gamma_next [B], draft_offsets_next [B+1]) int32 on the device.
+    """
+    L = library()
+    _dev(history, "history", torch.int32)
+    _dev(num_accepted, "num_accepted", torch.int32)
+    _dev(draft_offsets, "draft_offsets", torch.int32)
+    if temp_target is not None:
+        _dev(temp_target, "temp_target", torch.float32)
+    B = history.shape[0]
+    dev = history.device
+    if gamma_next is None:
+        gamma_next = torch.empty(B, dtype=torch.int32, device=dev)
+    if draft_offsets_next is None:
+        draft_offsets_next = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    st = L.spec_verify_gamma_update(_ptr(history), _ptr(num_accepted), _ptr(draft_offsets),
+                                    _ptr(temp_target), int(bool(couple_temperature)), B,
+                                    _ptr(gamma_next), _ptr(draft_offsets_next), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_gamma_update")
+    return gamma_next, draft_offsets_next
 
 
 TELEMETRY_FIELDS = ["rounds", "error_rows", "drafted", "accepted", "full_accepts", "tree_paths",

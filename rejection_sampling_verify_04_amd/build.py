@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 SOURCES = ["sv_api.hip", "sv_stats.hip", "sv_linear.hip", "sv_tree.hip", "sv_attn.hip",
-           "sv_kv.hip", "sv_telemetry.hip"]
+           "sv_kv.hip", "sv_telemetry.hip", "sv_control.hip",
+           "sv_draft.hip"]
 HEADERS = ["sv_common.h", "sv_internal.h", "sv_finish.h"]
 
 HIPCC_FLAGS = [

@@ -331,6 +331,62 @@ int spec_verify_telemetry_summary(const sv_telemetry* acc, double* out, hipStrea
   return SV_OK;
 }
 
+int spec_verify_draft_topk(const void* logits, int dtype, int R, int V, int k,
+                           const float* temp, int32_t* tokens, float* logprob,
+                           hipStream_t stream) {
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
+  if (R < 0 || V < 1 || k < 1 || k > SV_MAX_TOPK || k > V) return SV_ERR_INVALID_ARG;
+  if (R == 0) return SV_OK;
+  if (!logits || !tokens || !logprob) return SV_ERR_INVALID_ARG;
+  if (sv::launch_draft_topk(dtype, logits, R, V, k, temp, tokens, logprob, stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_tree_prune(const int32_t* cand_parent, const int32_t* cand_token,
+                           const float* cand_logq, const int32_t* n_cand, int B, int C, int n_max,
+                           double tau, int32_t* parents, int32_t* tokens, float* cum_logprob,
+                           int32_t* n_nodes, int32_t* n_pass, hipStream_t stream) {
+  if (B < 0 || C < 0 || C > SV_MAX_CANDIDATES || n_max < 1 || n_max > SV_MAX_TREE_NODES)
+    return SV_ERR_INVALID_ARG;
+  if (!(tau >= 0.0)) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!parents || !tokens || !cum_logprob || !n_nodes) return SV_ERR_INVALID_ARG;
+  if (C > 0 && (!cand_parent || !cand_token || !cand_logq)) return SV_ERR_INVALID_ARG;
+  sv::TreePruneArgs a{};
+  a.cand_parent = cand_parent;
+  a.cand_token = cand_token;
+  a.cand_logq = cand_logq;
+  a.n_cand = n_cand;
+  a.B = B;
+  a.C = C;
+  a.n_max = n_max;
+  a.tau = tau;
+  a.parents = parents;
+  a.tokens = tokens;
+  a.cum_logprob = cum_logprob;
+  a.n_nodes = n_nodes;
+  a.n_pass = n_pass;
+  if (sv::launch_tree_prune(a, stream) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_gamma_update(uint32_t* history, const int32_t* num_accepted,
+                             const int32_t* draft_offsets, const float* temp_target,
+                             int couple_temperature, int B, int32_t* gamma_next,
+                             int32_t* draft_offsets_next, hipStream_t stream) {
+  if (B < 0) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!history || !num_accepted || !draft_offsets || !gamma_next) return SV_ERR_INVALID_ARG;
+  if (couple_temperature && !temp_target) return SV_ERR_INVALID_ARG;
+  if ((long long)B * 8 >= (1LL << 31)) return SV_ERR_INVALID_ARG;   // offsets stay in int32
+  if (sv::launch_gamma_update(history, num_accepted, draft_offsets, temp_target,
+                              couple_temperature ? 1 : 0, B, gamma_next, draft_offsets_next,
+                              stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
 int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids, int n_rows,
                              int n_slots, uint32_t* out_words, hipStream_t stream) {
   if (n_rows < 0 || n_slots < 0) return SV_ERR_INVALID_ARG;

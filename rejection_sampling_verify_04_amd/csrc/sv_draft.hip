@@ -1,0 +1,311 @@
+// Drafting helpers on the device, gfx950: the top-k candidates of draft
+// rows and the pruning of a drafted candidate forest into the round's tree
+// (blog.lonae.com/posts/2026-draft-model-kv-jDwzYp, tree-attention
+// paragraphs: every draft position branches into the draft's top-k
+// candidates; the tree is pruned by cumulative draft probability up to a
+// node budget rather than fully expanded).
+//
+// draft_topk_kernel: one work item of 1024 threads per row.  Each thread
+// owns a contiguous range of the row.  A radix select on order-preserving
+// keys (2 passes of 8 bits for bf16, 4 for fp32) finds the k-th largest
+// key; the keys above it and, in index order, enough keys equal to it are
+// gathered and ranked (larger logit first, lower id on ties).  The softmax
+// normaliser at the row's temperature is formed in the first pass.
+//
+// tree_prune_kernel: one work item per batch row; every candidate's depth,
+// cumulative log q and sibling rank, its place in the keep order (larger
+// cumulative log q, then shallower, earlier parent, lower rank), then a
+// breadth-first renumbering of the kept set, level by level.  With log q
+// <= 0 the cumulative value never grows along a path, so the first
+// n_max - 1 finite candidates of the keep order are closed under parents.
+#include <hip/hip_runtime.h>
+
+#include "sv_common.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kTopkMax = 64;
+
+template <int DT>
+__device__ __forceinline__ uint32_t logit_key(const void* row, int v) {
+  if (DT == 1) {
+    const uint32_t b = ((const uint16_t*)row)[v];
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  }
+  return float_order_key(((const float*)row)[v]);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* logits, int V, int k,
+                                                                 const float* temp, int* tokens,
+                                                                 float* logprob) {
+  constexpr int kBits = DT == 1 ? 16 : 32;
+  __shared__ uint32_t s_hist[256];
+  __shared__ double s_scan[kFinWaves];
+  __shared__ float s_wm[kFinWaves];
+  __shared__ double s_ws[kFinWaves];
+  __shared__ uint32_t s_key[kTopkMax];
+  __shared__ int s_idx[kTopkMax];
+  __shared__ uint32_t s_sel[2];   // digit chosen, count above it
+
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const char* row = (const char*)logits + (long long)r * V * (DT == 1 ? 2 : 4);
+  const int E = (V + kFinThreads - 1) / kFinThreads;
+  const int v0 = min(tid * E, V), v1 = min(v0 + E, V);
+  const float T = temp ? temp[r] : 1.0f;
+  if (!temp_ok(T)) {   // reported as token -1 and a NaN log-probability
+    if (tid < k) {
+      tokens[(long long)r * k + tid] = -1;
+      logprob[(long long)r * k + tid] = __builtin_nanf("");
+    }
+    return;
+  }
+  const bool greedy = T == 0.0f;
+  const float k2 = greedy ? 0.0f : log2e_over_t(T);
+
+  // softmax normaliser: block maximum, then the sum of 2^((x - m) k2)
+  float m = -__builtin_huge_valf();
+  for (int v = v0; v < v1; ++v) m = fmaxf(m, load_logit<DT>(row, v));
+  m = wave_max(m);
+  if (lane == 0) s_wm[wave] = m;
+  __syncthreads();
+  m = s_wm[0];
+  for (int w = 1; w < kFinWaves; ++w) m = fmaxf(m, s_wm[w]);
+  double s = 0.0;
+  if (!greedy)
+    for (int v = v0; v < v1; ++v) s += (double)exp2_hw((load_logit<DT>(row, v) - m) * k2);
+  s = wave_sum(s);
+  if (lane == 0) s_ws[wave] = s;
+
+  // radix select of the k-th largest key, 8 bits at a time from the top
+  uint32_t prefix = 0u, need = (uint32_t)k;
+  for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kFinThreads) s_hist[i] = 0u;
+    __syncthreads();
+    const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int v = v0; v < v1; ++v) {
+      const uint32_t key = logit_key<DT>(row, v);
+      if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&s_hist[(key >> shift) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // digit d with count(> d) < need <= count(>= d), scanning from the top
+      uint32_t c[4], tot = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = s_hist[255 - (lane * 4 + j)];
+        tot += c[j];
+      }
+      const double incl = wave_inclusive_scan((double)tot);
+      uint32_t above = (uint32_t)(incl - (double)tot);
+      int found = -1;
+      uint32_t above_found = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (found < 0 && above < need && above + c[j] >= need) {
+          found = 255 - (lane * 4 + j);
+          above_found = above;
+        }
+        above += c[j];
+      }
+      const unsigned long long hit = __ballot(found >= 0);
+      const int src = hit ? __ffsll((long long)hit) - 1 : 0;
+      const int d = __shfl(found, src);
+      const uint32_t ab = __shfl(above_found, src);
+      if (lane == 0) {
+        s_sel[0] = (uint32_t)max(d, 0);
+        s_sel[1] = ab;
+      }
+    }
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    need -= s_sel[1];
+  }
+  const uint32_t thr = prefix;   // the k-th largest key; `need` equal keys are taken
+  // keys above the threshold (fewer than k), and equal keys in index order
+  uint32_t n_above = 0u, n_eq = 0u;
+  for (int v = v0; v < v1; ++v) {
+    const uint32_t key = logit_key<DT>(row, v);
+    n_above += key > thr;
+    n_eq += key == thr;
+  }
+  double tot_above;
+  const uint32_t pos_above =
+      (uint32_t)block_exclusive_scan<kFinWaves>((double)n_above, s_scan, &tot_above);
+  double tot_eq;
+  const uint32_t pos_eq = (uint32_t)block_exclusive_scan<kFinWaves>((double)n_eq, s_scan, &tot_eq);
+  uint32_t pa = pos_above, pe = pos_eq;
+  for (int v = v0; v < v1; ++v) {
+    const uint32_t key = logit_key<DT>(row, v);
+    if (key > thr) {
+      s_key[pa] = key;
+      s_idx[pa] = v;
+      ++pa;
+    } else if (key == thr) {
+      if (pe < need) {
+        const uint32_t at = (uint32_t)tot_above + pe;
+        s_key[at] = key;
+        s_idx[at] = v;
+      }
+      ++pe;
+    }
+  }
+  __syncthreads();
+  // rank the k entries: larger key first, lower index on ties
+  if (tid < k) {
+    const uint32_t key = s_key[tid];
+    const int idx = s_idx[tid];
+    int rank = 0;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t kj = s_key[j];
+      rank += kj > key || (kj == key && s_idx[j] < idx);
+    }
+    double S = 0.0;
+    for (int w = 0; w < kFinWaves; ++w) S += s_ws[w];
+    const float x = load_logit<DT>(row, idx);
+    double lp;
+    if (greedy) lp = rank == 0 ? 0.0 : -__builtin_huge_val();
+    else lp = ((double)x - (double)m) * ((double)k2 / kLog2e) - log(S);
+    tokens[(long long)r * k + rank] = idx;
+    logprob[(long long)r * k + rank] = (float)lp;
+  }
+}
+
+constexpr int kPruneMax = 1024;   // candidates per batch row
+
+__global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a) {
+  __shared__ int s_par[kPruneMax], s_depth[kPruneMax], s_rank[kPruneMax], s_new[kPruneMax];
+  __shared__ double s_cum[kPruneMax];
+  __shared__ int s_keep[kPruneMax];
+  __shared__ int s_bad, s_maxd, s_count, s_pass;
+
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int C = min(a.n_cand ? a.n_cand[b] : a.C, a.C);
+  const long long cb = (long long)b * a.C;
+  if (tid == 0) {
+    s_bad = C < 0;
+    s_maxd = 0;
+    s_pass = 0;
+  }
+  __syncthreads();
+  const int i = tid;
+  const bool mine = i < C;
+  int par = -1;
+  double lq = 0.0;
+  if (mine) {
+    par = a.cand_parent[cb + i];
+    lq = (double)a.cand_logq[cb + i];
+    if (par < -1 || par >= i) s_bad = 1;
+    s_par[i] = par;
+  }
+  __syncthreads();
+  const bool bad = s_bad != 0;
+  // depth (walk to the root) and rank among the siblings
+  int depth = 0, rank = 0;
+  if (mine && !bad) {
+    for (int x = i; x >= 0; x = s_par[x]) ++depth;
+    for (int j = 0; j < i; ++j) rank += s_par[j] == par;
+    s_depth[i] = depth;
+    s_rank[i] = rank;
+    atomicMax(&s_maxd, depth);
+  }
+  __syncthreads();
+  const int maxd = bad ? 0 : min(s_maxd, kPruneMax);
+  // cumulative log q, one level at a time: parent's value plus the node's
+  double cum = 0.0;
+  for (int d = 1; d <= maxd; ++d) {
+    if (mine && !bad && depth == d) {
+      cum = (par < 0 ? 0.0 : s_cum[par]) + lq;
+      s_cum[i] = cum;
+    }
+    __syncthreads();
+  }
+  // place in the keep order; kept if finite and among the first n_max - 1
+  int keep = 0;
+  if (mine && !bad) {
+    int before = 0;
+    for (int j = 0; j < C; ++j) {
+      const double cj = s_cum[j];
+      const bool first =
+          cj > cum ||
+          (cj == cum && (s_depth[j] < depth ||
+                         (s_depth[j] == depth && (s_par[j] < par ||
+                                                  (s_par[j] == par && s_rank[j] < rank)))));
+      before += first;
+    }
+    keep = cum > -__builtin_huge_val() && before < a.n_max - 1;
+    s_keep[i] = keep;
+    s_new[i] = -1;
+  }
+  __syncthreads();
+  // breadth-first numbering, level by level: (depth, new parent index, rank)
+  int base = 1;
+  for (int d = 1; d <= maxd; ++d) {
+    int pos = 0;
+    const bool here = mine && !bad && keep && depth == d;
+    if (here) {
+      const int np = par < 0 ? 0 : s_new[par];
+      for (int j = 0; j < C; ++j) {
+        if (s_keep[j] && s_depth[j] == d) {
+          const int pj = s_par[j];
+          const int npj = pj < 0 ? 0 : s_new[pj];
+          pos += npj < np || (npj == np && s_rank[j] < rank);
+        }
+      }
+    }
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+    if (here) {
+      s_new[i] = base + pos;
+      atomicAdd(&s_count, 1);
+    }
+    __syncthreads();
+    base += s_count;
+    __syncthreads();
+  }
+  const int n = bad ? 0 : base;
+  const long long ob = (long long)b * a.n_max;
+  if (mine && !bad && keep) {
+    const int ni = s_new[i];
+    a.parents[ob + ni] = par < 0 ? 0 : s_new[par];
+    a.tokens[ob + ni] = a.cand_token[cb + i];
+    a.cum_logprob[ob + ni] = (float)cum;
+    if (exp(cum) >= a.tau) atomicAdd(&s_pass, 1);
+  }
+  if (tid == 0 && !bad) {
+    a.parents[ob] = -1;
+    a.tokens[ob] = -1;
+    a.cum_logprob[ob] = 0.0f;
+  }
+  for (int j = tid; j < a.n_max; j += kFinThreads) {
+    if (j >= n && (j > 0 || bad)) {
+      a.parents[ob + j] = -1;
+      a.tokens[ob + j] = -1;
+      a.cum_logprob[ob + j] = -__builtin_huge_valf();
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    a.n_nodes[b] = n;
+    if (a.n_pass) a.n_pass[b] = bad ? 0 : s_pass;
+  }
+}
+
+hipError_t launch_draft_topk(int dtype, const void* logits, int R, int V, int k, const float* temp,
+                             int* tokens, float* logprob, hipStream_t st) {
+  if (dtype == 1)
+    draft_topk_kernel<1><<<dim3((unsigned)R), dim3(kFinThreads), 0, st>>>(logits, V, k, temp,
+                                                                         tokens, logprob);
+  else
+    draft_topk_kernel<0><<<dim3((unsigned)R), dim3(kFinThreads), 0, st>>>(logits, V, k, temp,
+                                                                         tokens, logprob);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_prune(const TreePruneArgs& a, hipStream_t st) {
+  tree_prune_kernel<<<dim3((unsigned)a.B), dim3(kFinThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -116,6 +116,20 @@ struct KvArgs {
   int* new_len;
 };
 
+struct TreePruneArgs {
+  const int* cand_parent;    // [B][C]: -1 (a child of the root) or an earlier candidate
+  const int* cand_token;     // [B][C]
+  const float* cand_logq;    // [B][C] log q of the token under its parent's draft row
+  const int* n_cand;         // [B] or null (C)
+  int B, C, n_max;
+  double tau;
+  int* parents;              // [B][n_max] out
+  int* tokens;
+  float* cum_logprob;
+  int* n_nodes;              // [B] out (0: a malformed forest)
+  int* n_pass;               // [B] out or null: kept nodes with cumulative probability >= tau
+};
+
 // Workgroups of a kernel that fit on the current device at once (cached per
 // kernel slot and device; slots are unique across the library).
 template <typename K>
@@ -151,5 +165,11 @@ hipError_t launch_telemetry_tree(const int* num_accepted, const int* path, const
                                  const int* n_nodes, int B, int N, sv_telemetry* acc,
                                  hipStream_t st);
 hipError_t launch_telemetry_summary(const sv_telemetry* acc, double* out, hipStream_t st);
+hipError_t launch_draft_topk(int dtype, const void* logits, int R, int V, int k, const float* temp,
+                             int* tokens, float* logprob, hipStream_t st);
+hipError_t launch_tree_prune(const TreePruneArgs& a, hipStream_t st);
+hipError_t launch_gamma_update(uint32_t* history, const int* num_accepted, const int* off,
+                               const float* temp, int couple, int B, int* gamma_next,
+                               int* off_next, hipStream_t st);
 
 }  // namespace sv

@@ -124,6 +124,18 @@ def test_tree_and_attn_host_validation(lib):
     assert lib.spec_verify_telemetry_tree(p, p, p, None, 4, 65, p, None) == -1     # N > 64
     assert lib.spec_verify_telemetry_tree(p, None, p, None, 4, 8, p, None) == -1   # no paths
     assert lib.spec_verify_telemetry_summary(None, p, None) == -1
+    assert lib.spec_verify_draft_topk(p, 1, 0, 100, 4, None, p, p, None) == 0        # empty
+    assert lib.spec_verify_draft_topk(p, 1, 2, 100, 65, None, p, p, None) == -1      # k > 64
+    assert lib.spec_verify_draft_topk(p, 1, 2, 3, 4, None, p, p, None) == -1         # k > V
+    assert lib.spec_verify_draft_topk(p, 5, 2, 100, 4, None, p, p, None) == -1       # dtype
+    prune = lib.spec_verify_tree_prune
+    assert prune(p, p, p, None, 2, 1025, 64, ctypes.c_double(0.1), p, p, p, p, None, None) == -1
+    assert prune(p, p, p, None, 2, 10, 65, ctypes.c_double(0.1), p, p, p, p, None, None) == -1
+    assert prune(p, p, p, None, 2, 10, 64, ctypes.c_double(-1.0), p, p, p, p, None, None) == -1
+    assert prune(p, p, p, None, 0, 10, 64, ctypes.c_double(0.1), p, p, p, p, None, None) == 0
+    gu = lib.spec_verify_gamma_update
+    assert gu(p, p, p, None, 1, 4, p, None, None) == -1     # coupling without temperatures
+    assert gu(p, p, p, None, 0, 0, p, None, None) == 0      # empty
     assert lib.spec_verify_philox_words(0, 0, None, 0, 5, None, None) == 0
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, None, None) == -1
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, ctypes.c_void_p(8), None) == -1

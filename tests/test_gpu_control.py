@@ -1,0 +1,150 @@
+"""GPU parity of the drafting and control helpers against the oracle.
+
+* spec_verify_gamma_update: histories, next gammas and offsets bit-exact,
+  batches wider than one work item, temperature coupling, and a short
+  closed loop (draft with the controller's gammas, verify on the GPU,
+  update on the GPU) checked round by round;
+* spec_verify_draft_topk: tokens exact (ties to the lower id), log-
+  probabilities within 1e-5, bf16 and fp32, k = 1..64, V up to 152064,
+  greedy rows;
+* spec_verify_tree_prune: kept trees exact on full 4-wide, 4-deep forests
+  from the GPU's own top-k, budgets from 1 to beyond the forest, ragged
+  candidate counts and malformed forests.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import control as OC, draft as OD
+import synth
+from gpu_util import f32, i32, logits_to_dev, run_linear, say, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def test_gamma_update_matches_oracle():
+    import rejection_sampling_verify_04_amd as sv
+    torch = torch_mod()
+    rng = np.random.default_rng(100)
+    B = 2500
+    count = rng.integers(0, 17, size=B)
+    hist = (rng.integers(0, 1 << 16, size=B) & ((1 << count) - 1)) | (count << 16)
+    g = rng.choice([2, 4, 8], size=B)
+    off = np.concatenate([[0], np.cumsum(g)]).astype(np.int32)
+    n = np.array([rng.integers(-1, gi + 1) for gi in g], dtype=np.int32)
+    temp = rng.choice([0.5, 0.8, 0.9, 1.2], size=B).astype(np.float32)
+    for couple in (False, True):
+        h_dev = torch.from_numpy(hist.astype(np.int32)).cuda()
+        gn, on = sv.gamma_update(h_dev, i32(n), i32(off), temp_target=f32(temp),
+                                 couple_temperature=couple)
+        h_ref, g_ref, o_ref = OC.gamma_update(hist, n, g, temp, couple)
+        assert np.array_equal(h_dev.cpu().numpy(), h_ref)
+        assert np.array_equal(gn.cpu().numpy(), g_ref)
+        assert np.array_equal(on.cpu().numpy(), o_ref)
+    say("[control] gamma update: B=%d ok, gamma histogram %s" % (B, np.bincount(g_ref).tolist()))
+
+
+def test_gamma_closed_loop():
+    """Five rounds: draft with the controller's gammas, verify and update on the GPU."""
+    import rejection_sampling_verify_04_amd as sv
+    torch = torch_mod()
+    rng = np.random.default_rng(101)
+    B, V = 64, 512
+    sigma = np.where(np.arange(B) % 2 == 0, 3.0, 0.3)
+    h_dev = torch.zeros(B, dtype=torch.int32, device="cuda")
+    h_ref = np.zeros(B, dtype=np.int64)
+    gam = np.full(B, 4)
+    T = np.ones(B, dtype=np.float32)
+    for rnd in range(5):
+        d = synth._linear_batch(rng, gam, V, 3.0, sigma, T, T.copy(), synth.BF16)
+        gv = run_linear(d, step=rnd)
+        gn, on = sv.gamma_update(h_dev, i32(gv["num_accepted"]), i32(d["offsets"]))
+        h_ref, g_ref, o_ref = OC.gamma_update(h_ref, gv["num_accepted"], gam)
+        assert np.array_equal(h_dev.cpu().numpy(), h_ref)
+        assert np.array_equal(gn.cpu().numpy(), g_ref)
+        gam = g_ref
+    low = gam[sigma > 1].mean()
+    high = gam[sigma < 1].mean()
+    say("[control] closed loop: mean gamma sigma=3.0 rows %.2f, sigma=0.3 rows %.2f" % (low, high))
+    assert high > low
+
+
+@pytest.mark.parametrize("dtype,V,R,k", [(1, 1000, 40, 16), (1, 32000, 16, 4), (0, 5000, 8, 64),
+                                         (1, 152064, 3, 8), (0, 777, 5, 1)])
+def test_draft_topk_matches_oracle(dtype, V, R, k):
+    import rejection_sampling_verify_04_amd as sv
+    rng = np.random.default_rng(102 + V)
+    x = rng.normal(0, 2, size=(R, V)).astype(np.float32)
+    x[:, rng.integers(0, V, size=V // 10)] = x[:, :1]          # ties
+    if dtype == 1:
+        bits = synth.bf16_bits(x)
+        vals = synth.bf16_values(bits).astype(np.float64)
+        dev = logits_to_dev(bits, 1)
+    else:
+        vals = x.astype(np.float64)
+        dev = logits_to_dev(x, 0)
+    T = rng.choice([1.0, 0.7, 0.0], size=R).astype(np.float32)
+    tok, lp = sv.draft_topk(dev, k, temp=f32(T))
+    tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
+    for r in range(R):
+        rt, rl = OD.topk_candidates(vals[r], k, float(T[r]))
+        assert np.array_equal(tok[r], rt), (r, tok[r], rt)
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(lp[r]), fin)
+        assert np.all(np.abs(lp[r][fin] - rl[fin]) <= 1e-5 * np.maximum(1.0, np.abs(rl[fin])))
+    say("[control] draft top-k dtype=%d V=%d R=%d k=%d ok" % (dtype, V, R, k))
+
+
+def gpu_forest(rng, V, width, depth, B):
+    """Full forests from the GPU's own top-k of random draft rows."""
+    import rejection_sampling_verify_04_amd as sv
+    par, tok, lq = [], [], []
+    for b in range(B):
+        p_b, t_b, l_b = [], [], []
+        frontier = [-1]
+        for _ in range(depth):
+            rows = rng.normal(0, 2, size=(len(frontier), V)).astype(np.float32)
+            t, l = sv.draft_topk(logits_to_dev(rows, 0), width)
+            t, l = t.cpu().numpy(), l.cpu().numpy()
+            nxt = []
+            for j, p in enumerate(frontier):
+                for c in range(width):
+                    p_b.append(p)
+                    t_b.append(int(t[j, c]))
+                    l_b.append(float(l[j, c]))
+                    nxt.append(len(p_b) - 1)
+            frontier = nxt
+        par.append(p_b)
+        tok.append(t_b)
+        lq.append(l_b)
+    return (np.array(par, dtype=np.int32), np.array(tok, dtype=np.int32),
+            np.array(lq, dtype=np.float32))
+
+
+def test_tree_prune_matches_oracle():
+    import rejection_sampling_verify_04_amd as sv
+    rng = np.random.default_rng(103)
+    B = 6
+    par, tok, lq = gpu_forest(rng, 300, 4, 4, B)
+    C = par.shape[1]
+    n_cand = np.array([C, C, 200, 84, 20, 4], dtype=np.int32)
+    for n_max in (1, 16, 64):
+        out = sv.tree_prune(i32(par), i32(tok), f32(lq), n_max, tau=0.01, n_cand=i32(n_cand))
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+        for b in range(B):
+            c = int(n_cand[b])
+            rp, rt, rc, rpass = OD.prune_tree(par[b, :c], tok[b, :c], lq[b, :c].astype(np.float64),
+                                              n_max, 0.01)
+            n = len(rp)
+            assert got["n_nodes"][b] == n
+            assert np.array_equal(got["parents"][b, :n], rp)
+            assert np.array_equal(got["tokens"][b, :n], rt)
+            assert np.array_equal(got["cum_logprob"][b, :n], rc.astype(np.float32))
+            assert got["n_pass"][b] == rpass
+            assert np.all(got["parents"][b, n:] == -1)
+        say("[control] prune n_max=%d ok: nodes %s" % (n_max, got["n_nodes"].tolist()))
+    bad = par.copy()
+    bad[2, 10] = 50                     # a parent after its child
+    out = sv.tree_prune(i32(bad), i32(tok), f32(lq), 64)
+    assert out["n_nodes"].cpu().numpy()[2] == 0
