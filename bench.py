@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear_v32k",
                     choices=["linear_v1000", "linear_v32k", "linear_v128k", "bimodal_v152k",
-                             "tree_v32k", "tree_wor_v32k", "attn_tree", "kv_commit"])
+                             "tree_v32k", "tree_wor_v32k", "attn_tree", "kv_commit",
+                             "draft_topk", "tree_prune"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying one HIP graph")
@@ -172,6 +173,34 @@ def cpu_baseline_kv(kc, vc, L0, n_acc, path, N, seconds):
                        % (rows, toks, layers, N, t_total))
 
 
+def cpu_baseline_topk(rows, k, seconds):
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        x = oracle.bf16_bits_to_f64(rows[n % rows.shape[0]])
+        oracle.draft.topk_candidates(x, k, 1.0)
+        n += 1
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="draft rows/s", cores=1, kind="oracle",
+                sample="%d rows of the same workload in %.1f s, single-threaded Python/NumPy"
+                       % (n, dt))
+
+
+def cpu_baseline_prune(par, tok, logq, n_max, seconds):
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        b = n % par.shape[0]
+        oracle.draft.prune_tree(par[b], tok[b], logq[b].astype(np.float64), n_max)
+        n += 1
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="pruned trees/s", cores=1, kind="oracle",
+                sample="%d forests of the same workload in %.1f s, single-threaded Python"
+                       % (n, dt))
+
+
 def load_traffic(path, workload, kernel_sig):
     """HBM bytes per launch of the dominant kernel, from counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size); None when
@@ -191,7 +220,8 @@ def kernel_source_sig(wl):
     own file and the headers that file includes)."""
     import hashlib
     csrc = os.path.join(ROOT, "rejection_sampling_verify_04_amd", "csrc")
-    own = {"attn_tree": "sv_attn.hip", "kv_commit": "sv_kv.hip"}.get(wl, "sv_stats.hip")
+    own = {"attn_tree": "sv_attn.hip", "kv_commit": "sv_kv.hip", "draft_topk": "sv_draft.hip",
+           "tree_prune": "sv_draft.hip"}.get(wl, "sv_stats.hip")
     names = [own, "sv_common.h", "sv_internal.h"]
     h = hashlib.sha1()
     for name in names:
@@ -218,7 +248,48 @@ def main():
     stream = torch.cuda.current_stream()
     dev = torch.device("cuda", 0)
 
-    if wl == "kv_commit":
+    if wl in ("draft_topk", "tree_prune"):
+        # One level of tree drafting: top-4 candidates of 1024 draft rows
+        # (64 trees x 16 frontier nodes) over V=32000 bf16; and the pruning of
+        # 64 full 4-wide, 4-deep candidate forests (340 candidates) to 64 nodes.
+        rng = np.random.default_rng(11)
+        R, V, kk = 1024, 32000, 4
+        rows = synth.bf16_bits(rng.standard_normal((R, V), dtype=np.float32) * np.float32(2.0))
+        nrc = copies_for(R * V * 2)
+        lsets = [to_dev_logits(torch, rows, 1) for _ in range(nrc)]
+        Bp, C, n_max = 64, 340, 64
+        par = np.zeros((Bp, C), dtype=np.int32)
+        lvl = [list(range(0, 4)), list(range(4, 20)), list(range(20, 84)), list(range(84, 340))]
+        for d in range(4):
+            for j, c in enumerate(lvl[d]):
+                par[:, c] = -1 if d == 0 else lvl[d - 1][j // 4]
+        cl = torch.from_numpy(rng.standard_normal((Bp * 85, V // 8), dtype=np.float32)).cuda()
+        ct, clq = sv.draft_topk(cl, 4)
+        cpar = torch.from_numpy(par).cuda()
+        ctok = ct.reshape(Bp, C).contiguous()
+        clog = clq.reshape(Bp, C).contiguous()
+        torch.cuda.synchronize()
+        if wl == "draft_topk":
+            alg_bytes = R * V * 2
+            units = R
+
+            def step(i, ev=None):
+                sv.draft_topk(lsets[i % nrc], kk)
+            config = dict(workload=wl, rows=R, V=V, k=kk, input_dtype="bf16", input_copies=nrc)
+            unit = "draft rows/s"
+            metric = "draft top-k: rows/sec + achieved HBM GB/s (% of peak)"
+        else:
+            alg_bytes = Bp * C * 12 + Bp * n_max * 12
+            units = Bp
+
+            def step(i, ev=None):
+                sv.tree_prune(cpar, ctok, clog, n_max, tau=0.1)
+            config = dict(workload=wl, B=Bp, candidates=C, n_max=n_max,
+                          forest="4-wide, 4-deep, top-4 log q of random draft rows")
+            unit = "pruned trees/s"
+            metric = "tree pruning: trees/sec"
+        flops = 0
+    elif wl == "kv_commit":
         # The commit after a SAMPLED_WOR tree round: paths from the library's
         # own verify of the tree_wor_v32k trees, caches of 4 layers.
         B, H, N, dd, L0, layers = 64, 32, 64, 128, 4096, 4
@@ -386,8 +457,15 @@ def main():
     # HIP events attached to that kernel's dispatch on the call's stream.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    hooked = wl not in ("draft_topk", "tree_prune")
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        if hooked:
+            step(args.warmup + i, evs[i])
+        else:
+            # one kernel per step: events around the call on the current stream
+            evs[i][0].record()
+            step(args.warmup + i)
+            evs[i][1].record()
     torch.cuda.synchronize()
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     avg_kern_s = float(np.mean(kern_ms)) / 1e3
@@ -398,8 +476,9 @@ def main():
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=traffic,
-                kernel={"attn_tree": "attn_kernel", "kv_commit": "kv_commit_kernel"}.get(
-                    wl, "stats_kernel"),
+                kernel={"attn_tree": "attn_kernel", "kv_commit": "kv_commit_kernel",
+                        "draft_topk": "draft_topk_kernel",
+                        "tree_prune": "tree_prune_kernel"}.get(wl, "stats_kernel"),
                 algorithmic_bytes_per_launch=int(alg_bytes),
                 avg_kernel_us=round(avg_kern_s * 1e6, 2))
     if flops:
@@ -414,6 +493,11 @@ def main():
     if not args.no_cpu_baseline:
         if wl == "kv_commit":
             out["cpu_baseline"] = cpu_baseline_kv(kc, vc, L0, na, pa, N, args.cpu_seconds)
+        elif wl == "draft_topk":
+            out["cpu_baseline"] = cpu_baseline_topk(rows, kk, args.cpu_seconds)
+        elif wl == "tree_prune":
+            out["cpu_baseline"] = cpu_baseline_prune(par, ctok.cpu().numpy(), clog.cpu().numpy(),
+                                                     n_max, args.cpu_seconds)
         elif wl == "attn_tree":
             out["cpu_baseline"] = cpu_baseline_attn(q, k, v, pl, tree["parents"], args.cpu_seconds)
         elif d["kind"] == "linear":
