@@ -5,12 +5,14 @@
 // candidates; the tree is pruned by cumulative draft probability up to a
 // node budget rather than fully expanded).
 //
-// draft_topk_kernel: one work item of 1024 threads per row.  Each thread
-// owns a contiguous range of the row.  A radix select on order-preserving
-// keys (2 passes of 8 bits for bf16, 4 for fp32) finds the k-th largest
-// key; the keys above it and, in index order, enough keys equal to it are
-// gathered and ranked (larger logit first, lower id on ties).  The softmax
-// normaliser at the row's temperature is formed in the first pass.
+// draft_topk_kernel: one work item of 1024 threads per row.  A row of up to
+// 64 KB is read once from HBM with coalesced 16-byte loads and kept in LDS
+// as order-preserving keys (larger rows are re-read by every pass).  A
+// radix select on the keys (2 passes of 8 bits for bf16, 4 for fp32) finds
+// the k-th largest; the keys above it and, in index order (each thread owns
+// a contiguous range), enough keys equal to it are gathered and ranked
+// (larger logit first, lower id on ties).  The softmax normaliser at the
+// row's temperature is formed from the keys before the selection.
 //
 // tree_prune_kernel: one work item per batch row; every candidate's depth,
 // cumulative log q and sibling rank, its place in the keep order (larger
@@ -28,19 +30,49 @@ namespace sv {
 constexpr int kTopkMax = 64;
 
 template <int DT>
-__device__ __forceinline__ uint32_t logit_key(const void* row, int v) {
+__device__ __forceinline__ uint32_t key_of_bits(uint32_t b) {
+  if (DT == 1) return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+template <int DT>
+__device__ __forceinline__ float value_of_key(uint32_t key) {
   if (DT == 1) {
-    const uint32_t b = ((const uint16_t*)row)[v];
-    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+    const uint32_t b = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+    return __uint_as_float(b << 16);
   }
-  return float_order_key(((const float*)row)[v]);
+  return float_from_order_key(key);
 }
 
-template <int DT>
+// Keys of one row, either cached in LDS (the row read once from HBM with
+// coalesced loads) or re-read from global memory by every pass.
+template <int DT, bool CACHED>
+struct RowKeys {
+  const char* row;
+  const uint32_t* lds;   // CACHED: 16-bit keys (bf16) or 32-bit keys (fp32)
+  __device__ __forceinline__ uint32_t operator()(int v) const {
+    if (CACHED) {
+      if (DT == 1) return ((const uint16_t*)lds)[v];
+      return lds[v];
+    }
+    const uint32_t b = DT == 1 ? (uint32_t)((const uint16_t*)row)[v] : ((const uint32_t*)row)[v];
+    return key_of_bits<DT>(b);
+  }
+};
+
+constexpr int kTopkCacheWords = 16384;   // 64 KB: 32768 bf16 or 16384 fp32 keys
+constexpr int kTopkCand = 1024;          // candidates ranked directly
+
+template <int DT, bool CACHED>
 __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* logits, int V, int k,
-                                                                 const float* temp, int* tokens,
-                                                                 float* logprob) {
+                                                                 const float* temp, int vec_ok,
+                                                                 int* tokens, float* logprob) {
   constexpr int kBits = DT == 1 ? 16 : 32;
+  constexpr int ES = DT == 1 ? 2 : 4;
+  __shared__ uint32_t s_keys[CACHED ? kTopkCacheWords : 1];
+  // digit histograms, one per pair of waves (LDS atomics on a concentrated
+  // digit distribution contend within a pair only), and their sum
+  constexpr int kHists = kFinWaves / 2;
+  __shared__ uint32_t s_hists[kHists][256];
   __shared__ uint32_t s_hist[256];
   __shared__ double s_scan[kFinWaves];
   __shared__ float s_wm[kFinWaves];
@@ -48,11 +80,12 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
   __shared__ uint32_t s_key[kTopkMax];
   __shared__ int s_idx[kTopkMax];
   __shared__ uint32_t s_sel[2];   // digit chosen, count above it
+  __shared__ uint32_t s_tmax[kFinThreads];               // each thread's largest key
+  __shared__ uint32_t s_ckey[kTopkCand];                 // candidates: keys >= L
+  __shared__ int s_cidx[kTopkCand];
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const char* row = (const char*)logits + (long long)r * V * (DT == 1 ? 2 : 4);
-  const int E = (V + kFinThreads - 1) / kFinThreads;
-  const int v0 = min(tid * E, V), v1 = min(v0 + E, V);
+  const char* row = (const char*)logits + (long long)r * V * ES;
   const float T = temp ? temp[r] : 1.0f;
   if (!temp_ok(T)) {   // reported as token -1 and a NaN log-probability
     if (tid < k) {
@@ -63,30 +96,97 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
   }
   const bool greedy = T == 0.0f;
   const float k2 = greedy ? 0.0f : log2e_over_t(T);
+  const RowKeys<DT, CACHED> key_at{row, s_keys};
 
-  // softmax normaliser: block maximum, then the sum of 2^((x - m) k2)
+  // the row maximum and each thread's largest key (and, cached, the keys into
+  // LDS: 16-byte loads, interleaved)
   float m = -__builtin_huge_valf();
-  for (int v = v0; v < v1; ++v) m = fmaxf(m, load_logit<DT>(row, v));
+  uint32_t tmax = 0u;
+  if (CACHED) {
+    if (vec_ok) {
+      constexpr int EPV = 16 / ES;
+      for (int j = tid; j * EPV < V; j += kFinThreads) {
+        const uint4 w = *(const uint4*)(row + (long long)j * 16);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        uint32_t kk[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if (DT == 1) {
+            const uint32_t lo = key_of_bits<1>(ws[h] & 0xFFFFu), hi = key_of_bits<1>(ws[h] >> 16);
+            m = fmaxf(m, fmaxf(bf16_lo(ws[h]), bf16_hi(ws[h])));
+            tmax = max(tmax, max(lo, hi));
+            kk[h] = lo | (hi << 16);
+          } else {
+            kk[h] = key_of_bits<0>(ws[h]);
+            tmax = max(tmax, kk[h]);
+            m = fmaxf(m, __uint_as_float(ws[h]));
+          }
+        }
+        *(uint4*)&s_keys[j * 4] = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+      }
+    } else {
+      for (int v = tid; v < V; v += kFinThreads) {
+        const uint32_t b = DT == 1 ? (uint32_t)((const uint16_t*)row)[v] : ((const uint32_t*)row)[v];
+        const uint32_t key = key_of_bits<DT>(b);
+        if (DT == 1) ((uint16_t*)s_keys)[v] = (uint16_t)key;
+        else s_keys[v] = key;
+        tmax = max(tmax, key);
+        m = fmaxf(m, value_of_key<DT>(key));
+      }
+    }
+  } else {
+    for (int v = tid; v < V; v += kFinThreads) {
+      const uint32_t key = key_at(v);
+      tmax = max(tmax, key);
+      m = fmaxf(m, value_of_key<DT>(key));
+    }
+  }
+  s_tmax[tid] = tmax;
   m = wave_max(m);
   if (lane == 0) s_wm[wave] = m;
   __syncthreads();
   m = s_wm[0];
   for (int w = 1; w < kFinWaves; ++w) m = fmaxf(m, s_wm[w]);
+  // softmax normaliser: the sum of 2^((x - m) k2)
   double s = 0.0;
   if (!greedy)
-    for (int v = v0; v < v1; ++v) s += (double)exp2_hw((load_logit<DT>(row, v) - m) * k2);
+    for (int v = tid; v < V; v += kFinThreads)
+      s += (double)exp2_hw((value_of_key<DT>(key_at(v)) - m) * k2);
   s = wave_sum(s);
   if (lane == 0) s_ws[wave] = s;
+  // the rank-th output: token and log softmax(x / T) (s_ws is read after a
+  // barrier on every path)
+  auto write_out = [&](int rank, uint32_t key, int idx) {
+    double S = 0.0;
+    for (int w = 0; w < kFinWaves; ++w) S += s_ws[w];
+    const float x = value_of_key<DT>(key);
+    double lp;
+    if (greedy) lp = rank == 0 ? 0.0 : -__builtin_huge_val();
+    else lp = ((double)x - (double)m) * ((double)k2 / kLog2e) - log(S);
+    tokens[(long long)r * k + rank] = idx;
+    logprob[(long long)r * k + rank] = (float)lp;
+  };
 
-  // radix select of the k-th largest key, 8 bits at a time from the top
+  // Radix select of the k-th largest of n keys, 8 bits at a time from the
+  // top: the key, and how many keys equal to it are needed beside the ones
+  // above it.
+  auto radix_kth = [&](auto key_of, int n, uint32_t* need_out) -> uint32_t {
   uint32_t prefix = 0u, need = (uint32_t)k;
   for (int shift = kBits - 8; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kFinThreads) s_hist[i] = 0u;
+    for (int i = tid; i < kHists * 256; i += kFinThreads) (&s_hists[0][0])[i] = 0u;
     __syncthreads();
     const uint32_t hi_mask = shift + 8 >= 32 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int v = v0; v < v1; ++v) {
-      const uint32_t key = logit_key<DT>(row, v);
-      if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&s_hist[(key >> shift) & 0xFFu], 1u);
+    uint32_t* hist = s_hists[wave >> 1];
+    for (int v = tid; v < n; v += kFinThreads) {
+      const uint32_t key = key_of(v);
+      if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t t = 0u;
+#pragma unroll
+      for (int h = 0; h < kHists; ++h) t += s_hists[h][tid];
+      s_hist[tid] = t;
     }
     __syncthreads();
     if (wave == 0) {
@@ -122,11 +222,58 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
     prefix |= s_sel[0] << shift;
     need -= s_sel[1];
   }
-  const uint32_t thr = prefix;   // the k-th largest key; `need` equal keys are taken
-  // keys above the threshold (fewer than k), and equal keys in index order
+  *need_out = need;
+  return prefix;
+  };
+
+  // L = the k-th largest of the threads' largest keys: at least k keys are
+  // >= L, so the top k are among them.  When they are few, rank them all.
+  uint32_t need_l;
+  const uint32_t L = radix_kth([&](int v) { return s_tmax[v]; }, kFinThreads, &need_l);
+  uint32_t n_cand = 0u;
+  for (int v = tid; v < V; v += kFinThreads) n_cand += key_at(v) >= L;
+  double c_tot;
+  const uint32_t c_pos = (uint32_t)block_exclusive_scan<kFinWaves>((double)n_cand, s_scan, &c_tot);
+  const int C = (int)c_tot;
+  if (C <= kTopkCand) {
+    uint32_t at = c_pos;
+    for (int v = tid; v < V; v += kFinThreads) {
+      const uint32_t key = key_at(v);
+      if (key >= L) {
+        s_ckey[at] = key;
+        s_cidx[at] = v;
+        ++at;
+      }
+    }
+    __syncthreads();
+    if (tid < C) {
+      const uint32_t key = s_ckey[tid];
+      const int idx = s_cidx[tid];
+      int rank = 0;
+      for (int j = 0; j < C; ++j) {
+        const uint32_t kj = s_ckey[j];
+        rank += kj > key || (kj == key && s_cidx[j] < idx);
+      }
+      if (rank < k) {
+        s_key[rank] = key;
+        s_idx[rank] = idx;
+      }
+    }
+    __syncthreads();
+    if (tid < k) write_out(tid, s_key[tid], s_idx[tid]);
+    return;
+  }
+
+  // Many keys tie at the top: radix select over the whole row.
+  uint32_t need;
+  const uint32_t thr = radix_kth(key_at, V, &need);   // the k-th largest; `need` equal keys
+  // keys above the threshold (fewer than k, any order), and the equal keys of
+  // lowest index: each thread owns a contiguous range for the latter
+  const int E = (V + kFinThreads - 1) / kFinThreads;
+  const int v0 = min(tid * E, V), v1 = min(v0 + E, V);
   uint32_t n_above = 0u, n_eq = 0u;
   for (int v = v0; v < v1; ++v) {
-    const uint32_t key = logit_key<DT>(row, v);
+    const uint32_t key = key_at(v);
     n_above += key > thr;
     n_eq += key == thr;
   }
@@ -137,7 +284,7 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
   const uint32_t pos_eq = (uint32_t)block_exclusive_scan<kFinWaves>((double)n_eq, s_scan, &tot_eq);
   uint32_t pa = pos_above, pe = pos_eq;
   for (int v = v0; v < v1; ++v) {
-    const uint32_t key = logit_key<DT>(row, v);
+    const uint32_t key = key_at(v);
     if (key > thr) {
       s_key[pa] = key;
       s_idx[pa] = v;
@@ -161,14 +308,7 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
       const uint32_t kj = s_key[j];
       rank += kj > key || (kj == key && s_idx[j] < idx);
     }
-    double S = 0.0;
-    for (int w = 0; w < kFinWaves; ++w) S += s_ws[w];
-    const float x = load_logit<DT>(row, idx);
-    double lp;
-    if (greedy) lp = rank == 0 ? 0.0 : -__builtin_huge_val();
-    else lp = ((double)x - (double)m) * ((double)k2 / kLog2e) - log(S);
-    tokens[(long long)r * k + rank] = idx;
-    logprob[(long long)r * k + rank] = (float)lp;
+    write_out(rank, key, idx);
   }
 }
 
@@ -294,12 +434,17 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
 
 hipError_t launch_draft_topk(int dtype, const void* logits, int R, int V, int k, const float* temp,
                              int* tokens, float* logprob, hipStream_t st) {
-  if (dtype == 1)
-    draft_topk_kernel<1><<<dim3((unsigned)R), dim3(kFinThreads), 0, st>>>(logits, V, k, temp,
-                                                                         tokens, logprob);
-  else
-    draft_topk_kernel<0><<<dim3((unsigned)R), dim3(kFinThreads), 0, st>>>(logits, V, k, temp,
-                                                                         tokens, logprob);
+  const int es = dtype == 1 ? 2 : 4;
+  const int vec_ok = ((long long)V * es) % 16 == 0 && ((uintptr_t)logits & 15u) == 0;
+  const bool cached = (long long)V * es <= (long long)kTopkCacheWords * 4;
+  const dim3 grid((unsigned)R), block(kFinThreads);
+  if (dtype == 1) {
+    if (cached) draft_topk_kernel<1, true><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
+    else draft_topk_kernel<1, false><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
+  } else {
+    if (cached) draft_topk_kernel<0, true><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
+    else draft_topk_kernel<0, false><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
+  }
   return hipGetLastError();
 }
 

@@ -96,6 +96,29 @@ def test_draft_topk_matches_oracle(dtype, V, R, k):
     say("[control] draft top-k dtype=%d V=%d R=%d k=%d ok" % (dtype, V, R, k))
 
 
+def test_draft_topk_heavy_ties():
+    """Rows whose top values repeat far more often than k (the whole-row path)."""
+    import rejection_sampling_verify_04_amd as sv
+    rng = np.random.default_rng(104)
+    R, V, k = 6, 20000, 8
+    x = rng.normal(0, 1, size=(R, V)).astype(np.float32)
+    x[0] = 0.5                                  # every logit equal
+    x[1, rng.choice(V, 3000, replace=False)] = 9.0   # 3000 copies of the maximum
+    x[2, :] = -np.inf
+    x[2, 5] = 1.0                               # one finite logit among -inf
+    bits = synth.bf16_bits(x)
+    vals = synth.bf16_values(bits).astype(np.float64)
+    tok, lp = sv.draft_topk(logits_to_dev(bits, 1), k)
+    tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
+    for r in range(R):
+        rt, rl = OD.topk_candidates(vals[r], k, 1.0)
+        assert np.array_equal(tok[r], rt), (r, tok[r], rt)
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(lp[r]), fin)
+        assert np.all(np.abs(lp[r][fin] - rl[fin]) <= 1e-5 * np.maximum(1.0, np.abs(rl[fin])))
+    say("[control] draft top-k with heavy ties ok")
+
+
 def gpu_forest(rng, V, width, depth, B):
     """Full forests from the GPU's own top-k of random draft rows."""
     import rejection_sampling_verify_04_amd as sv
