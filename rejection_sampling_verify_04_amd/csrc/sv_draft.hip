@@ -17,7 +17,8 @@
 // tree_prune_kernel: one work item per batch row; every candidate's depth,
 // cumulative log q and sibling rank, its place in the keep order (larger
 // cumulative log q, then shallower, earlier parent, lower rank), then a
-// breadth-first renumbering of the kept set, level by level.  With log q
+// breadth-first renumbering of the kept set (at most 63 nodes, one wave),
+// level by level.  With log q
 // <= 0 the cumulative value never grows along a path, so the first
 // n_max - 1 finite candidates of the keep order are closed under parents.
 #include <hip/hip_runtime.h>
@@ -315,10 +316,14 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
 constexpr int kPruneMax = 1024;   // candidates per batch row
 
 __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a) {
-  __shared__ int s_par[kPruneMax], s_depth[kPruneMax], s_rank[kPruneMax], s_new[kPruneMax];
-  __shared__ double s_cum[kPruneMax];
+  __shared__ __align__(16) int s_par[kPruneMax];
+  __shared__ int s_depth[kPruneMax], s_rank[kPruneMax], s_new[kPruneMax];
+  __shared__ __align__(16) double s_cum[kPruneMax];
   __shared__ int s_keep[kPruneMax];
-  __shared__ int s_bad, s_maxd, s_count, s_pass;
+  __shared__ int s_klist[64];
+  __shared__ __align__(16) uint32_t s_tie[kPruneMax];
+  __shared__ double s_scan[kFinWaves];
+  __shared__ int s_bad, s_maxd, s_pass;
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const int C = min(a.n_cand ? a.n_cand[b] : a.C, a.C);
@@ -345,7 +350,20 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
   int depth = 0, rank = 0;
   if (mine && !bad) {
     for (int x = i; x >= 0; x = s_par[x]) ++depth;
-    for (int j = 0; j < i; ++j) rank += s_par[j] == par;
+    // earlier siblings: sixteen parents per step in four 16-byte LDS reads,
+    // branch-free (entries at or past i never count)
+    const int4* p4 = (const int4*)s_par;
+    for (int j = 0; j < i; j += 16) {
+      int4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = p4[(j >> 2) + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jj = j + 4 * u;
+        rank += (jj < i && q[u].x == par) + (jj + 1 < i && q[u].y == par) +
+                (jj + 2 < i && q[u].z == par) + (jj + 3 < i && q[u].w == par);
+      }
+    }
     s_depth[i] = depth;
     s_rank[i] = rank;
     atomicMax(&s_maxd, depth);
@@ -361,49 +379,69 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
     }
     __syncthreads();
   }
-  // place in the keep order; kept if finite and among the first n_max - 1
+  // place in the keep order; kept if finite and among the first n_max - 1.
+  // The tie order (depth, parent, rank) packs into one word: 11, 11, 10 bits.
+  if (mine && !bad) s_tie[i] = ((uint32_t)depth << 21) | ((uint32_t)(par + 1) << 10) | (uint32_t)rank;
+  if (i >= C && i < ((C + 7) & ~7)) {   // the pad entries read by the eight-wide loop
+    s_cum[i] = -__builtin_huge_val();
+    s_tie[i] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
   int keep = 0;
   if (mine && !bad) {
+    const uint32_t tie = s_tie[i];
     int before = 0;
-    for (int j = 0; j < C; ++j) {
-      const double cj = s_cum[j];
-      const bool first =
-          cj > cum ||
-          (cj == cum && (s_depth[j] < depth ||
-                         (s_depth[j] == depth && (s_par[j] < par ||
-                                                  (s_par[j] == par && s_rank[j] < rank)))));
-      before += first;
+    // eight candidates per step, all loads unconditional (the arrays are
+    // padded past C with entries that never count: -inf and the largest tie)
+    for (int j = 0; j < C; j += 8) {
+      double2 c2[4];
+      uint2 t2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        c2[u] = ((const double2*)s_cum)[(j >> 1) + u];
+        t2[u] = ((const uint2*)s_tie)[(j >> 1) + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        before += (c2[u].x > cum) | ((c2[u].x == cum) & (t2[u].x < tie));
+        before += (c2[u].y > cum) | ((c2[u].y == cum) & (t2[u].y < tie));
+      }
     }
     keep = cum > -__builtin_huge_val() && before < a.n_max - 1;
     s_keep[i] = keep;
     s_new[i] = -1;
   }
   __syncthreads();
-  // breadth-first numbering, level by level: (depth, new parent index, rank)
-  int base = 1;
-  for (int d = 1; d <= maxd; ++d) {
-    int pos = 0;
-    const bool here = mine && !bad && keep && depth == d;
-    if (here) {
-      const int np = par < 0 ? 0 : s_new[par];
-      for (int j = 0; j < C; ++j) {
-        if (s_keep[j] && s_depth[j] == d) {
-          const int pj = s_par[j];
-          const int npj = pj < 0 ? 0 : s_new[pj];
-          pos += npj < np || (npj == np && s_rank[j] < rank);
-        }
-      }
+  // breadth-first numbering of the kept nodes (at most 63), gathered in keep
+  // order, by one wave, level by level: (depth, new parent index, rank)
+  double k_tot;
+  const int kpos = (int)block_exclusive_scan<kFinWaves>((double)(keep ? 1 : 0), s_scan, &k_tot);
+  const int K = (int)k_tot;
+  if (keep) s_klist[kpos] = i;
+  __syncthreads();
+  if (tid < 64) {
+    const int q = tid;
+    const int ci = q < K ? s_klist[q] : 0;
+    const int dq = q < K ? s_depth[ci] : 0;
+    const int pq = q < K ? s_par[ci] : -1;
+    const int rq = q < K ? s_rank[ci] : 0;
+    int base = 1;
+    for (int d = 1; d <= maxd; ++d) {
+      const bool here = q < K && dq == d;
+      // this level's order key: the parent's new index (numbered at the level
+      // above), then the sibling rank; the other lanes get a key that never
+      // counts
+      const int np = pq < 0 ? 0 : (here ? s_new[pq] : 0);
+      const uint32_t key = here ? ((uint32_t)np << 10) | (uint32_t)rq : 0xFFFFFFFFu;
+      int pos = 0;
+      for (int j = 0; j < K; ++j) pos += __builtin_amdgcn_readlane(key, j) < key;
+      const int n_here = __popcll(__ballot(here));
+      if (here) s_new[ci] = base + pos;
+      base += n_here;
     }
-    if (tid == 0) s_count = 0;
-    __syncthreads();
-    if (here) {
-      s_new[i] = base + pos;
-      atomicAdd(&s_count, 1);
-    }
-    __syncthreads();
-    base += s_count;
-    __syncthreads();
   }
+  __syncthreads();
+  const int base = 1 + K;
   const int n = bad ? 0 : base;
   const long long ob = (long long)b * a.n_max;
   if (mine && !bad && keep) {
