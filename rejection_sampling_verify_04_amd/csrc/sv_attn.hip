@@ -1,9 +1,9 @@
 // Tree- or causal-masked verify attention on MFMA (gfx950).
 //
 // One workgroup per (batch row, head); wave w owns query rows 16w..16w+15.
-// Keys stream in tiles of 64 from the cache into LDS (K and V row-major),
-// with the next tile's global loads in flight while the current tile is
-// multiplied.  The V^T operand is formed on the way out of LDS by the
+// Keys stream in tiles of 64 from the cache into two LDS buffers (K and V
+// row-major), with the next two tiles' global loads in flight while the
+// current tile is multiplied, and one barrier per tile.  The V^T operand is formed on the way out of LDS by the
 // transposing read ds_read_b64_tr_b16.  Per tile and wave:
 //
 //   S^T[64 keys x 16 queries] = K_tile . Q^T    4 key blocks x 4 d-steps of
@@ -65,9 +65,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kKT * kVsStride];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kKT * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * kKT * kVsStride];
   __shared__ unsigned long long s_anc[kMaxNodes];
   __shared__ int s_L, s_ok;
 
@@ -128,43 +128,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 
   const int total = L + N;
   const int n_tiles = (total + kKT - 1) / kKT;
-  // The next tile's loads are in flight while this tile is multiplied.  Keys
-  // past the end load the last key (finite, masked to weight 0), so that no
-  // load sits behind a branch: a load whose value crosses a branch join is
+  // Two tiles' loads are in flight in registers (buffers A and B) while the
+  // current tile is multiplied out of one of the two LDS buffers.  Keys past
+  // the end load the last key (finite, masked to weight 0), so that no load
+  // sits behind a branch: a load whose value crosses a branch join is
   // waited for there, which would drain the prefetch.
-  uint4 kr[4], vr[4];
-  auto load_tile = [&](int t) {
+  u32x4_t kA[4], vA[4], kB[4], vB[4];
+  auto load_tile = [&](u32x4_t (&kr)[4], u32x4_t (&vr)[4], int t) {
+    t = min(t, n_tiles - 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ci = j * kThreads + tid;
       const int key = ci >> 4, d0 = (ci & 15) * 8;
       const int gk = min(t * kKT + key, total - 1);
-      kr[j] = *(const uint4*)(a.k + headKV + (long long)gk * kD + d0);
-      vr[j] = *(const uint4*)(a.v + headKV + (long long)gk * kD + d0);
+      kr[j] = *(const u32x4_t*)(a.k + headKV + (long long)gk * kD + d0);
+      vr[j] = *(const u32x4_t*)(a.v + headKV + (long long)gk * kD + d0);
     }
   };
-  load_tile(0);
-
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();
+  auto store_tile = [&](const u32x4_t (&kr)[4], const u32x4_t (&vr)[4], int buf) {
+    uint16_t* ks = Ks + buf * (kKT * kKsStride);
+    uint16_t* vs = Vs + buf * (kKT * kVsStride);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ci = j * kThreads + tid;
       const int key = ci >> 4, d0 = (ci & 15) * 8;
-      *(uint4*)&Ks[key * kKsStride + d0] = kr[j];
-      *(uint4*)&Vs[key * kVsStride + d0] = vr[j];
+      *(u32x4_t*)&ks[key * kKsStride + d0] = kr[j];
+      *(u32x4_t*)&vs[key * kVsStride + d0] = vr[j];
     }
-    __syncthreads();
-    load_tile(min(t + 1, n_tiles - 1));
+  };
 
+  // One tile out of LDS buffer `buf`.
+  auto compute_tile = [&](int t, int buf) {
+    const uint16_t* ks = Ks + buf * (kKT * kKsStride);
+    const uint16_t* vs = Vs + buf * (kKT * kVsStride);
     f32x4_t s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 ku = *(const uint4*)&Ks[(kb * 16 + col) * kKsStride + ks * 32 + 8 * g];
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ku), qop[ks], s[kb], 0, 0, 0);
+      for (int ks_ = 0; ks_ < 4; ++ks_) {
+        const uint4 ku = *(const uint4*)&ks[(kb * 16 + col) * kKsStride + ks_ * 32 + 8 * g];
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ku), qop[ks_], s[kb], 0, 0, 0);
       }
     }
 
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
                                   pack_bf16x2(s[2 * ks2 + 1][2], s[2 * ks2 + 1][3]));
       const bf16x8_t pop = as_bf16x8(pu);
       // V rows of the keys 32 ks2 + 4 g + {0..3} and 32 ks2 + 16 + 4 g + {0..3}
-      const uint16_t* vlo = &Vs[(ks2 * 32 + 4 * g + (col >> 2)) * kVsStride + 4 * (col & 3)];
+      const uint16_t* vlo = &vs[(ks2 * 32 + 4 * g + (col >> 2)) * kVsStride + 4 * (col & 3)];
       const uint16_t* vhi = vlo + 16 * kVsStride;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
@@ -226,6 +230,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vu), pop, o[mb], 0, 0, 0);
       }
     }
+  };
+
+  // Tile t sits in LDS buffer t & 1; tile t + 1 in registers (A for odd
+  // t + 1, B for even), tile t + 2 in the other register buffer.  After tile
+  // t is multiplied, tile t + 1 goes to the other LDS buffer (last read for
+  // tile t - 1, which every wave finished before the previous barrier), its
+  // register buffer takes tile t + 3, and one barrier publishes it.
+  load_tile(kA, vA, 0);
+  load_tile(kB, vB, 1);
+  store_tile(kA, vA, 0);
+  load_tile(kA, vA, 2);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    compute_tile(t, 0);
+    if (t + 1 >= n_tiles) break;
+    store_tile(kB, vB, 1);
+    load_tile(kB, vB, t + 3);
+    __syncthreads();
+    compute_tile(t + 1, 1);
+    if (t + 2 >= n_tiles) break;
+    store_tile(kA, vA, 0);
+    load_tile(kA, vA, t + 4);
+    __syncthreads();
   }
 
   float l = l_run + __shfl_xor(l_run, 16, 64);

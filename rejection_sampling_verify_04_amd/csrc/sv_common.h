@@ -224,6 +224,18 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* scratch
   return base + excl_lane;
 }
 
+// A value that is the same in every lane, kept in scalar registers.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ __forceinline__ double uni(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const unsigned long long lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const unsigned long long hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
 // Order-preserving map of a float to uint32 (for max-with-lowest-index keys).
 __device__ __forceinline__ uint32_t float_order_key(float f) {
   uint32_t u = __float_as_uint(f);

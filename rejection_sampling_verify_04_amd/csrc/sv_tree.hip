@@ -279,17 +279,6 @@ struct WorDist {
   int onehot;            // a greedy row is present (one-hot terms to add)
 };
 
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ float uni(float v) {
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
-}
-__device__ __forceinline__ double uni(double v) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-  const unsigned long long lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  const unsigned long long hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  return __longlong_as_double((long long)((hi << 32) | lo));
-}
-
 // lambda as the float32 weights use it (finite: -lambda * 0 must stay 0).
 __device__ __forceinline__ float lam_f32(double lam) { return uni((float)fmin(lam, 3.0e38)); }
 

@@ -107,6 +107,25 @@ def test_error_rows_do_not_stop_the_batch():
     assert gpu["num_accepted"][0] >= 0 and gpu["num_accepted"][4] >= 0
 
 
+def test_error_rows_multichunk():
+    # V of three chunks: rows with nothing to draw are finished by their
+    # first chunk's work item, the others by whichever chunk completes them
+    d = ragged(18, [3, 4, 2, 5, 3, 6], 20000, synth.BF16)
+    d["tokens"] = d["tokens"].copy()
+    d["tokens"][d["offsets"][1] + 2] = -3             # row 1: token out of range
+    d["temp_target"] = d["temp_target"].copy()
+    d["temp_target"][2] = np.nan                      # row 2: bad temperature
+    d["temp_target"][5] = 0.0                         # row 5: greedy (no draw)
+    tv = d["target"].copy()
+    o3 = d["offsets"][3] + 3
+    tv[o3] = 0xFF80                                   # row 3: an all -inf target row
+    d["target"] = tv
+    gpu, ref, _ = check(d, "error rows, 3 chunks")
+    assert list(gpu["num_accepted"][[1, 2, 3]]) == [-1, -1, -1]
+    assert gpu["num_accepted"][0] >= 0 and gpu["num_accepted"][4] >= 0
+    assert gpu["num_accepted"][5] >= 0
+
+
 def test_row_ids_make_packing_irrelevant():
     d = ragged(17, [4, 4, 4, 4], 6000, synth.BF16)
     ids = np.array([7, 1000003, 5, 2 ** 31 + 9], dtype=np.uint32)
