@@ -2,7 +2,7 @@
 //
 // One workgroup per (batch row, head); wave w owns query rows 16w..16w+15.
 // Keys stream in tiles of 64 from the cache into two LDS buffers (K and V
-// row-major), with the next two tiles' global loads in flight while the
+// row-major), with the next three tiles' global loads in flight while the
 // current tile is multiplied, and one barrier per tile.  The V^T operand is formed on the way out of LDS by the
 // transposing read ds_read_b64_tr_b16.  Per tile and wave:
 //
@@ -55,14 +55,13 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Two floats to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnArgs a) {
@@ -128,12 +127,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int total = L + N;
   const int n_tiles = (total + kKT - 1) / kKT;
-  // Two tiles' loads are in flight in registers (buffers A and B) while the
-  // current tile is multiplied out of one of the two LDS buffers.  Keys past
+  // Three tiles' loads are in flight in registers (buffers A, B and C) while
+  // the current tile is multiplied out of one of the two LDS buffers.  Keys past
   // the end load the last key (finite, masked to weight 0), so that no load
   // sits behind a branch: a load whose value crosses a branch join is
   // waited for there, which would drain the prefetch.
-  u32x4_t kA[4], vA[4], kB[4], vB[4];
+  u32x4_t kA[4], vA[4], kB[4], vB[4], kC[4], vC[4];
   auto load_tile = [&](u32x4_t (&kr)[4], u32x4_t (&vr)[4], int t) {
     t = min(t, n_tiles - 1);
 #pragma unroll
@@ -207,8 +206,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    // the running maxima rarely move once the first tiles are in
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+    }
 
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -232,28 +234,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // Tile t sits in LDS buffer t & 1; tile t + 1 in registers (A for odd
-  // t + 1, B for even), tile t + 2 in the other register buffer.  After tile
-  // t is multiplied, tile t + 1 goes to the other LDS buffer (last read for
-  // tile t - 1, which every wave finished before the previous barrier), its
-  // register buffer takes tile t + 3, and one barrier publishes it.
+  // Tile t is loaded into register buffer t mod 3 and multiplied out of LDS
+  // buffer t mod 2.  After tile t is multiplied, tile t + 1 goes from its
+  // registers to the other LDS buffer (last read for tile t - 1, which every
+  // wave finished before the previous barrier), those registers take tile
+  // t + 4, and one barrier publishes tile t + 1: three tiles' loads stay in
+  // flight behind the one being multiplied.
   load_tile(kA, vA, 0);
   load_tile(kB, vB, 1);
+  load_tile(kC, vC, 2);
   store_tile(kA, vA, 0);
-  load_tile(kA, vA, 2);
+  load_tile(kA, vA, 3);
   __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    compute_tile(t, 0);
-    if (t + 1 >= n_tiles) break;
-    store_tile(kB, vB, 1);
-    load_tile(kB, vB, t + 3);
-    __syncthreads();
-    compute_tile(t + 1, 1);
-    if (t + 2 >= n_tiles) break;
-    store_tile(kA, vA, 0);
-    load_tile(kA, vA, t + 4);
-    __syncthreads();
+#define SV_ATTN_STEP(T, KR, VR, BUF)    \
+  compute_tile((T), 1 - (BUF));          \
+  if ((T) + 1 >= n_tiles) break;         \
+  store_tile(KR, VR, (BUF));             \
+  load_tile(KR, VR, (T) + 4);            \
+  __syncthreads();
+  for (int t = 0;; t += 6) {
+    SV_ATTN_STEP(t, kB, vB, 1)
+    SV_ATTN_STEP(t + 1, kC, vC, 0)
+    SV_ATTN_STEP(t + 2, kA, vA, 1)
+    SV_ATTN_STEP(t + 3, kB, vB, 0)
+    SV_ATTN_STEP(t + 4, kC, vC, 1)
+    SV_ATTN_STEP(t + 5, kA, vA, 0)
   }
+#undef SV_ATTN_STEP
 
   float l = l_run + __shfl_xor(l_run, 16, 64);
   l += __shfl_xor(l, 32, 64);
