@@ -463,19 +463,194 @@ __device__ double wor_pass(const WorDist& d, int V, int nc, float lam,
   return G;
 }
 
-template <int DT, bool VEC>
+// With the vocabulary in at most NC_MAX chunks, a node's target term
+// a(v) = p(v) is kept in LDS as float32 from the node's first pass on:
+// between the passes of one node only lambda changes, so the later passes
+// read the draft row alone and form one exponential per element.  a is
+// formed by the same expression as in wor_weights, so every weight is the
+// same value either way.
+constexpr int kWorCacheChunks = 4;   // V <= 32768
+
+// threadIdx.x as a value the compiler cannot prove invariant: what a pass
+// derives from it (addresses, element indices) is formed inside the pass
+// instead of being hoisted out of the walk and held in registers throughout.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// a(v) of this thread's elements of every chunk into s_a (each thread later
+// reads back only what it wrote, so no barrier is needed).  All loads are
+// in flight together; addresses past V are clamped into the row.
+template <int DT, int NC>
+__device__ __forceinline__ void wor_fill(const WorDist& d, int V, float* s_a) {
+  constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV, NV = StopVec<DT>::NV;
+  const int tix = opaque_tid();
+  uint4 raw[NC][NV];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e0 = c * kChunk + tix * kPerThread;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int ej = e0 + j * EPV;
+      raw[c][j] = *(const uint4*)(d.xrow + (ej < V ? (long long)ej * ES : 0));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e0 = c * kChunk + tix * kPerThread;
+    float xp[kPerThread], av[kPerThread];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const uint32_t rw[4] = {raw[c][j].x, raw[c][j].y, raw[c][j].z, raw[c][j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (DT == 1) {
+          xp[j * 8 + 2 * h] = bf16_lo(rw[h]);
+          xp[j * 8 + 2 * h + 1] = bf16_hi(rw[h]);
+        } else {
+          xp[j * EPV + h] = __uint_as_float(rw[h]);
+        }
+      }
+    }
+    // the expression of wor_weights (fmaf with a zero addend rounds as the
+    // plain product does)
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      av[e] = fmaf(exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)), d.p_inv_s,
+                   e0 + e == d.p_amax ? 1.0f : 0.0f);
+    float4* ca = (float4*)(s_a + e0);
+    ca[0] = make_float4(av[0], av[1], av[2], av[3]);
+    ca[1] = make_float4(av[4], av[5], av[6], av[7]);
+  }
+}
+
+// As wor_weights (vector path), with a(v) read from the node's cache s_a
+// and the draft row's values from `r`.
+template <int DT, bool WANT_E>
+__device__ __forceinline__ void wor_weights_c(const WorDist& d, int V, int chunk, int tix,
+                                              const StopVec<DT>& r, const float* s_a, float lam,
+                                              const int* ex_tok, const float* ex_lam, int nex,
+                                              int t_cur, float w[kPerThread],
+                                              float be[kPerThread]) {
+  constexpr int EPV = StopVec<DT>::EPV;
+  const int e0 = chunk * kChunk + tix * kPerThread;
+  float xq[kPerThread], av[kPerThread];
+#pragma unroll
+  for (int j = 0; j < StopVec<DT>::NV; ++j) {
+    const uint32_t sw[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (DT == 1) {
+        xq[j * 8 + 2 * h] = bf16_lo(sw[h]);
+        xq[j * 8 + 2 * h + 1] = bf16_hi(sw[h]);
+      } else {
+        xq[j * EPV + h] = __uint_as_float(sw[h]);
+      }
+    }
+  }
+  const float4* ca = (const float4*)(s_a + e0);
+  const float4 lo = ca[0], hi = ca[1];
+  av[0] = lo.x; av[1] = lo.y; av[2] = lo.z; av[3] = lo.w;
+  av[4] = hi.x; av[5] = hi.y; av[6] = hi.z; av[7] = hi.w;
+  float lv[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) lv[e] = lam;
+  uint32_t exm = 0u;
+  for (int k = 0; k < nex; ++k) {
+    const int off = ex_tok[k] - e0;
+    if ((unsigned)off < (unsigned)kPerThread) {
+      const float l = ex_lam[k];
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        if (e == off) {
+          lv[e] = l;
+          exm |= 1u << e;
+        }
+      }
+    }
+  }
+  if (WANT_E && (unsigned)(t_cur - e0) < (unsigned)kPerThread) exm |= 1u << (t_cur - e0);
+  if (!d.onehot && e0 + kPerThread <= V) {
+    // sampled rows, elements all inside the row (the same values as below)
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const float b = exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
+      w[e] = fmaxf(fmaf(-lv[e], b, av[e]), 0.0f);
+      if (WANT_E) be[e] = ((exm >> e) & 1u) ? 0.0f : b;
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int idx = e0 + e;
+    const float b = fmaf(exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)), d.q_inv_s,
+                         idx == d.q_amax ? 1.0f : 0.0f);
+    const float wv = fmaxf(fmaf(-lv[e], b, av[e]), 0.0f);
+    const bool in = idx < V;
+    w[e] = in ? wv : 0.0f;
+    if (WANT_E) be[e] = (in && !((exm >> e) & 1u)) ? b : 0.0f;
+  }
+}
+
+// wor_pass over NC chunks with the node's cache: the draft row's loads of
+// every chunk are in flight together, and one block reduction serves the
+// pass.  The totals are formed as in wor_pass, so the results are the same
+// values.
+template <int DT, int NC, bool WANT_E>
+__device__ double wor_pass_c(const WorDist& d, int V, float lam, const int* ex_tok,
+                             const float* ex_lam, int nex, int t_cur, const float* s_a,
+                             double* s_mass, double* s_red, double* E) {
+  constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV;
+  const int tix = opaque_tid();
+  StopVec<DT> r[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e0 = c * kChunk + tix * kPerThread;
+#pragma unroll
+    for (int j = 0; j < StopVec<DT>::NV; ++j) {
+      const int ej = e0 + j * EPV;
+      r[c].q[j] = *(const uint4*)(d.yrow + (ej < V ? (long long)ej * ES : 0));
+    }
+  }
+  double v[NC + 1], e_acc = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float w[kPerThread], be[kPerThread];
+    wor_weights_c<DT, WANT_E>(d, V, c, tix, r[c], s_a, lam, ex_tok, ex_lam, nex, t_cur, w, be);
+    v[c] = thread_total(w);
+    if (WANT_E) e_acc += thread_total(be);
+    // one chunk's values live at a time
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  v[NC] = e_acc;
+  double t[NC + 1];
+  block_totals<NC + 1>(v, s_red, t);
+  double G = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    G += t[c];
+    if (threadIdx.x == 0) s_mass[c] = t[c];
+  }
+  if (WANT_E) *E = t[NC];
+  return G;
+}
+
+template <int DT, bool VEC, int NC>
 __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   __shared__ RowStats s_rows[kMaxNodes], s_qrows[kMaxNodes];
   __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes];
   __shared__ int s_rowok[kMaxNodes], s_qrowok[kMaxNodes];
   __shared__ double s_pa[kMaxNodes], s_qb[kMaxNodes], s_uacc[kMaxNodes];
-  __shared__ double s_cm[kMaxNodes * kMaxChunks];  // p's mass per (node, chunk)
+  __shared__ double s_cm[kMaxNodes * (NC ? NC : kMaxChunks)];  // p's mass per (node, chunk)
+  __shared__ __attribute__((aligned(16))) float s_a[NC ? NC * kChunk : 4];   // a(v) of cached_node
   __shared__ int s_ex_tok[kMaxNodes];              // tokens of the rejected siblings
   __shared__ float s_ex_lamf[kMaxNodes];           // their lambda (weights)
   __shared__ double s_ex_lam[kMaxNodes];           // their lambda (ratios)
   __shared__ unsigned long long s_inner;
   __shared__ int s_flags;
-  __shared__ double s_red[kFinWaves * (kWorGroup + 1)];
+  __shared__ double s_red[kFinWaves * ((NC > kWorGroup ? NC : kWorGroup) + 1)];
   __shared__ double s_scan[kFinWaves];
   __shared__ double s_mass[kMaxChunks];
   __shared__ int s_found[kFinWaves], s_last[kFinWaves];
@@ -483,7 +658,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   __shared__ double s_base, s_t;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nc = a.n_chunks;
+  const int nc = NC ? NC : a.n_chunks;
   const int n_parts = nc * kPartsPerChunk;
   const int b = blockIdx.x;
   const int V = a.V, N = a.N;
@@ -496,8 +671,8 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   if (nn < 1 || nn > N) err0 = kRowBadShape;
   else if (!temp_ok(Tt) || !temp_ok(Td)) err0 = kRowBadTemp;
   const bool gt = Tt == 0.0f, gd = Td == 0.0f;
-  const float kt = (gt || err0) ? 0.0f : log2e_over_t(Tt);
-  const float kd = (gd || err0) ? 0.0f : log2e_over_t(Td);
+  const float kt = uni((gt || err0) ? 0.0f : log2e_over_t(Tt));
+  const float kd = uni((gd || err0) ? 0.0f : log2e_over_t(Td));
   const uint32_t rid = uni((int)(a.row_ids ? a.row_ids[b] : (uint32_t)b));
 
   // Partials of the 2 nn rows (target rows of the nodes, then their draft
@@ -599,6 +774,26 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   double lam = 0.0;
   int nex = 0;
   bool have_masses = false;   // s_mass holds the masses of the current weights
+  int cached_node = -1;       // the node whose a(v) s_a holds (NC > 0)
+  // One pass at this node: wor_pass, or with the cache (filled at the
+  // node's first pass) wor_pass_c.
+  auto pass = [&](bool want_e, float lamf, int t_cur, double* E) -> double {
+    if constexpr (NC > 0) {
+      if (cached_node != node) {
+        wor_fill<DT, NC>(d, V, s_a);
+        cached_node = node;
+      }
+      return want_e ? wor_pass_c<DT, NC, true>(d, V, lamf, s_ex_tok, s_ex_lamf, nex, t_cur, s_a,
+                                               s_mass, s_red, E)
+                    : wor_pass_c<DT, NC, false>(d, V, lamf, s_ex_tok, s_ex_lamf, nex, t_cur, s_a,
+                                                s_mass, s_red, E);
+    } else {
+      return want_e ? wor_pass<DT, VEC, true>(d, V, nc, lamf, s_ex_tok, s_ex_lamf, nex, t_cur,
+                                              s_mass, s_red, E)
+                    : wor_pass<DT, VEC, false>(d, V, nc, lamf, s_ex_tok, s_ex_lamf, nex, t_cur,
+                                               s_mass, s_red, E);
+    }
+  };
   for (;;) {
     kids = __ballot(lane > node && lane < nn && s_par[lane] == node);
     d = wor_dist((const char*)a.target + (rb + node) * rowbytes,
@@ -644,12 +839,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
       double E = Q;
       double G;
       if (dupk < 0 && bv > 0.5 * Q) {
-        G = uni(wor_pass<DT, VEC, true>(d, V, nc, lam_f32(mu), s_ex_tok, s_ex_lamf, nex, t, s_mass,
-                                        s_red, &E));
+        G = uni(pass(true, lam_f32(mu), t, &E));
         E = uni(E);
       } else {
-        G = uni(wor_pass<DT, VEC, false>(d, V, nc, lam_f32(mu), s_ex_tok, s_ex_lamf, nex, -1,
-                                         s_mass, s_red, nullptr));
+        G = uni(pass(false, lam_f32(mu), -1, nullptr));
         if (dupk < 0) E = Q - bv;
       }
       if (G > 0.0) {
@@ -688,8 +881,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
       if (tid < nc) s_mass[tid] = s_cm[stop * nc + tid];
     } else if (!have_masses) {
       // the last rejection left p_j as it was: masses of its weights
-      wor_pass<DT, VEC, false>(d, V, nc, lam_f32(lam), s_ex_tok, s_ex_lamf, nex, -1, s_mass, s_red,
-                               nullptr);
+      pass(false, lam_f32(lam), -1, nullptr);
     }
     __syncthreads();
     double R = 0.0;
@@ -736,10 +928,22 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
 hipError_t launch_tree_finish(int dtype, const TreeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.B), block(kFinThreads);
   if (a.mode == 1) {
-    if (dtype == 1 && a.vec_ok) tree_wor_kernel<1, true><<<grid, block, 0, st>>>(a);
-    else if (dtype == 1) tree_wor_kernel<1, false><<<grid, block, 0, st>>>(a);
-    else if (a.vec_ok) tree_wor_kernel<0, true><<<grid, block, 0, st>>>(a);
-    else tree_wor_kernel<0, false><<<grid, block, 0, st>>>(a);
+    // vocabularies of up to kWorCacheChunks chunks keep a(v) in LDS
+#define SV_WOR_C(DT_, NC_)                                                   \
+  case NC_:                                                                  \
+    tree_wor_kernel<DT_, true, NC_><<<grid, block, 0, st>>>(a);              \
+    break;
+    if (a.vec_ok && a.n_chunks <= kWorCacheChunks) {
+      if (dtype == 1) {
+        switch (a.n_chunks) { SV_WOR_C(1, 1) SV_WOR_C(1, 2) SV_WOR_C(1, 3) SV_WOR_C(1, 4) }
+      } else {
+        switch (a.n_chunks) { SV_WOR_C(0, 1) SV_WOR_C(0, 2) SV_WOR_C(0, 3) SV_WOR_C(0, 4) }
+      }
+    } else if (dtype == 1 && a.vec_ok) tree_wor_kernel<1, true, 0><<<grid, block, 0, st>>>(a);
+    else if (dtype == 1) tree_wor_kernel<1, false, 0><<<grid, block, 0, st>>>(a);
+    else if (a.vec_ok) tree_wor_kernel<0, true, 0><<<grid, block, 0, st>>>(a);
+    else tree_wor_kernel<0, false, 0><<<grid, block, 0, st>>>(a);
+#undef SV_WOR_C
   } else {
     if (dtype == 1) tree_kernel<1><<<grid, block, 0, st>>>(a);
     else tree_kernel<0><<<grid, block, 0, st>>>(a);
