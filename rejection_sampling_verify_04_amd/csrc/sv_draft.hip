@@ -6,13 +6,16 @@
 // node budget rather than fully expanded).
 //
 // draft_topk_kernel: one work item of 1024 threads per row.  A row of up to
-// 64 KB is read once from HBM with coalesced 16-byte loads and kept in LDS
-// as order-preserving keys (larger rows are re-read by every pass).  A
-// radix select on the keys (2 passes of 8 bits for bf16, 4 for fp32) finds
-// the k-th largest; the keys above it and, in index order (each thread owns
-// a contiguous range), enough keys equal to it are gathered and ranked
-// (larger logit first, lower id on ties).  The softmax normaliser at the
-// row's temperature is formed from the keys before the selection.
+// 64 KB is read once from HBM, every thread's four 16-byte loads in flight
+// together, and kept in registers as order-preserving keys (larger or
+// unaligned rows are re-read from memory by every step).  The softmax
+// normaliser at the row's temperature comes first.  L, the k-th largest of
+// the threads' largest keys, bounds the top k from below (at least k keys
+// are >= L), so the keys >= L are gathered and ranked directly (larger logit
+// first, lower id on ties).  When too many keys tie at the top for that, a
+// radix select over the row (2 passes of 8 bits for bf16, 4 for fp32) finds
+// the k-th largest, and the keys above it and, in index order (each thread
+// owns a contiguous range), enough keys equal to it are ranked.
 //
 // tree_prune_kernel: one work item per batch row; every candidate's depth,
 // cumulative log q and sibling rank, its place in the keep order (larger
@@ -30,9 +33,15 @@ namespace sv {
 
 constexpr int kTopkMax = 64;
 
+// Order-preserving key of a logit's bits, with -0 and +0 one key (they
+// compare equal as values; ties go to the lower id).
 template <int DT>
 __device__ __forceinline__ uint32_t key_of_bits(uint32_t b) {
-  if (DT == 1) return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  if (DT == 1) {
+    b = (b & 0x7FFFu) ? b : 0u;
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  }
+  b = (b & 0x7FFFFFFFu) ? b : 0u;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 template <int DT>
@@ -44,32 +53,26 @@ __device__ __forceinline__ float value_of_key(uint32_t key) {
   return float_from_order_key(key);
 }
 
-// Keys of one row, either cached in LDS (the row read once from HBM with
-// coalesced loads) or re-read from global memory by every pass.
-template <int DT, bool CACHED>
+// Keys of one row, read from memory.
+template <int DT>
 struct RowKeys {
   const char* row;
-  const uint32_t* lds;   // CACHED: 16-bit keys (bf16) or 32-bit keys (fp32)
   __device__ __forceinline__ uint32_t operator()(int v) const {
-    if (CACHED) {
-      if (DT == 1) return ((const uint16_t*)lds)[v];
-      return lds[v];
-    }
     const uint32_t b = DT == 1 ? (uint32_t)((const uint16_t*)row)[v] : ((const uint32_t*)row)[v];
     return key_of_bits<DT>(b);
   }
 };
 
-constexpr int kTopkCacheWords = 16384;   // 64 KB: 32768 bf16 or 16384 fp32 keys
+constexpr int kTopkRegVecs = 4;   // 16-byte vectors per thread: rows of up to 64 KB
 constexpr int kTopkCand = 1024;          // candidates ranked directly
 
-template <int DT, bool CACHED>
+template <int DT, bool REG>
 __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* logits, int V, int k,
-                                                                 const float* temp, int vec_ok,
+                                                                 const float* temp,
                                                                  int* tokens, float* logprob) {
   constexpr int kBits = DT == 1 ? 16 : 32;
   constexpr int ES = DT == 1 ? 2 : 4;
-  __shared__ uint32_t s_keys[CACHED ? kTopkCacheWords : 1];
+  constexpr int EPV = 16 / ES;
   // digit histograms, one per pair of waves (LDS atomics on a concentrated
   // digit distribution contend within a pair only), and their sum
   constexpr int kHists = kFinWaves / 2;
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
   __shared__ int s_idx[kTopkMax];
   __shared__ uint32_t s_sel[2];   // digit chosen, count above it
   __shared__ uint32_t s_tmax[kFinThreads];               // each thread's largest key
-  __shared__ uint32_t s_ckey[kTopkCand];                 // candidates: keys >= L
+  __shared__ float s_cval[kTopkCand];                    // candidates: values >= L
   __shared__ int s_cidx[kTopkCand];
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -97,44 +100,51 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
   }
   const bool greedy = T == 0.0f;
   const float k2 = greedy ? 0.0f : log2e_over_t(T);
-  const RowKeys<DT, CACHED> key_at{row, s_keys};
+  const RowKeys<DT> key_at{row};
 
-  // the row maximum and each thread's largest key (and, cached, the keys into
-  // LDS: 16-byte loads, interleaved)
-  float m = -__builtin_huge_valf();
-  uint32_t tmax = 0u;
-  if (CACHED) {
-    if (vec_ok) {
-      constexpr int EPV = 16 / ES;
-      for (int j = tid; j * EPV < V; j += kFinThreads) {
-        const uint4 w = *(const uint4*)(row + (long long)j * 16);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        uint32_t kk[4];
+  // REG: this thread's vectors tid + 1024 j, all loads issued together
+  // (vectors past the row read vector 0 and are never used), unpacked once
+  constexpr int kRegElems = REG ? kTopkRegVecs * EPV : 1;
+  float xv[kRegElems];
+  bool okv[REG ? kTopkRegVecs : 1];
+  if (REG) {
+    u32x4_t raw[kTopkRegVecs];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          if (DT == 1) {
-            const uint32_t lo = key_of_bits<1>(ws[h] & 0xFFFFu), hi = key_of_bits<1>(ws[h] >> 16);
-            m = fmaxf(m, fmaxf(bf16_lo(ws[h]), bf16_hi(ws[h])));
-            tmax = max(tmax, max(lo, hi));
-            kk[h] = lo | (hi << 16);
-          } else {
-            kk[h] = key_of_bits<0>(ws[h]);
-            tmax = max(tmax, kk[h]);
-            m = fmaxf(m, __uint_as_float(ws[h]));
-          }
+    for (int j = 0; j < kTopkRegVecs; ++j) {
+      const int vj = tid + j * kFinThreads;
+      okv[j] = vj * EPV < V;
+      raw[j] = *(const u32x4_t*)(row + (long long)(okv[j] ? vj : 0) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkRegVecs; ++j) {
+      const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (DT == 1) {
+          xv[j * EPV + 2 * h] = bf16_lo(w[h]);
+          xv[j * EPV + 2 * h + 1] = bf16_hi(w[h]);
+        } else {
+          xv[j * EPV + h] = __uint_as_float(w[h]);
         }
-        *(uint4*)&s_keys[j * 4] = make_uint4(kk[0], kk[1], kk[2], kk[3]);
-      }
-    } else {
-      for (int v = tid; v < V; v += kFinThreads) {
-        const uint32_t b = DT == 1 ? (uint32_t)((const uint16_t*)row)[v] : ((const uint32_t*)row)[v];
-        const uint32_t key = key_of_bits<DT>(b);
-        if (DT == 1) ((uint16_t*)s_keys)[v] = (uint16_t)key;
-        else s_keys[v] = key;
-        tmax = max(tmax, key);
-        m = fmaxf(m, value_of_key<DT>(key));
       }
     }
+  }
+  // element e of this thread's registers is logit (tid + 1024 (e / EPV)) EPV + e % EPV
+  auto reg_index = [&](int e) { return (tid + (e / EPV) * kFinThreads) * EPV + e % EPV; };
+
+  // the row maximum and each thread's largest key
+  float m = -__builtin_huge_valf();
+  uint32_t tmax = 0u;
+  if (REG) {
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < kRegElems; ++e) {
+      if (okv[e / EPV]) {
+        m = fmaxf(m, xv[e]);
+        any = true;
+      }
+    }
+    tmax = any ? key_of_bits<DT>(DT == 1 ? __float_as_uint(m) >> 16 : __float_as_uint(m)) : 0u;
   } else {
     for (int v = tid; v < V; v += kFinThreads) {
       const uint32_t key = key_at(v);
@@ -146,21 +156,50 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
   m = wave_max(m);
   if (lane == 0) s_wm[wave] = m;
   __syncthreads();
+  // L = the k-th largest of the waves' largest values (k <= 16; each wave
+  // finds it from the 16 values itself) or of the threads' largest keys (a
+  // radix select): at least k logits are >= L, so the top k are among them.
+  float L;
+  if (k <= kFinWaves) {
+    const float mw = lane < kFinWaves ? s_wm[lane] : -__builtin_huge_valf();
+    int ge = 0;
+#pragma unroll
+    for (int j = 0; j < kFinWaves; ++j)
+      ge += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), j)) >= mw;
+    // the largest wave maximum with at least k wave maxima at or above it
+    L = wave_max((lane < kFinWaves && ge >= k) ? mw : -__builtin_huge_valf());
+  }
   m = s_wm[0];
   for (int w = 1; w < kFinWaves; ++w) m = fmaxf(m, s_wm[w]);
-  // softmax normaliser: the sum of 2^((x - m) k2)
+  // softmax normaliser: the sum of 2^((x - m) k2), eight terms at a time in
+  // float32 (pairwise), then in float64
   double s = 0.0;
-  if (!greedy)
-    for (int v = tid; v < V; v += kFinThreads)
-      s += (double)exp2_hw((value_of_key<DT>(key_at(v)) - m) * k2);
+  if (!greedy) {
+    if (REG) {
+#pragma unroll
+      for (int j = 0; j < kTopkRegVecs; ++j) {
+        float t[EPV];
+#pragma unroll
+        for (int h = 0; h < EPV; ++h) t[h] = exp2_hw((xv[j * EPV + h] - m) * k2);
+#pragma unroll
+        for (int w2 = EPV / 2; w2 >= 1; w2 >>= 1) {
+#pragma unroll
+          for (int h = 0; h < w2; ++h) t[h] = t[2 * h] + t[2 * h + 1];
+        }
+        if (okv[j]) s += (double)t[0];
+      }
+    } else {
+      for (int v = tid; v < V; v += kFinThreads)
+        s += (double)exp2_hw((value_of_key<DT>(key_at(v)) - m) * k2);
+    }
+  }
   s = wave_sum(s);
   if (lane == 0) s_ws[wave] = s;
   // the rank-th output: token and log softmax(x / T) (s_ws is read after a
   // barrier on every path)
-  auto write_out = [&](int rank, uint32_t key, int idx) {
+  auto write_out = [&](int rank, float x, int idx) {
     double S = 0.0;
     for (int w = 0; w < kFinWaves; ++w) S += s_ws[w];
-    const float x = value_of_key<DT>(key);
     double lp;
     if (greedy) lp = rank == 0 ? 0.0 : -__builtin_huge_val();
     else lp = ((double)x - (double)m) * ((double)k2 / kLog2e) - log(S);
@@ -227,45 +266,59 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
   return prefix;
   };
 
-  // L = the k-th largest of the threads' largest keys: at least k keys are
-  // >= L, so the top k are among them.  When they are few, rank them all.
-  uint32_t need_l;
-  const uint32_t L = radix_kth([&](int v) { return s_tmax[v]; }, kFinThreads, &need_l);
+  if (k > kFinWaves) {
+    uint32_t need_l;
+    L = value_of_key<DT>(radix_kth([&](int v) { return s_tmax[v]; }, kFinThreads, &need_l));
+  }
   uint32_t n_cand = 0u;
-  for (int v = tid; v < V; v += kFinThreads) n_cand += key_at(v) >= L;
+  if (REG) {
+#pragma unroll
+    for (int e = 0; e < kRegElems; ++e) n_cand += okv[e / EPV] && xv[e] >= L;
+  } else {
+    for (int v = tid; v < V; v += kFinThreads) n_cand += value_of_key<DT>(key_at(v)) >= L;
+  }
   double c_tot;
   const uint32_t c_pos = (uint32_t)block_exclusive_scan<kFinWaves>((double)n_cand, s_scan, &c_tot);
   const int C = (int)c_tot;
   if (C <= kTopkCand) {
     uint32_t at = c_pos;
-    for (int v = tid; v < V; v += kFinThreads) {
-      const uint32_t key = key_at(v);
-      if (key >= L) {
-        s_ckey[at] = key;
-        s_cidx[at] = v;
-        ++at;
+    auto put = [&](float x, int v) {
+      s_cval[at] = x;
+      s_cidx[at] = v;
+      ++at;
+    };
+    if (REG) {
+#pragma unroll
+      for (int e = 0; e < kRegElems; ++e)
+        if (okv[e / EPV] && xv[e] >= L) put(xv[e], reg_index(e));
+    } else {
+      for (int v = tid; v < V; v += kFinThreads) {
+        const float x = value_of_key<DT>(key_at(v));
+        if (x >= L) put(x, v);
       }
     }
     __syncthreads();
+    // rank: larger value first, lower id on ties
     if (tid < C) {
-      const uint32_t key = s_ckey[tid];
+      const float x = s_cval[tid];
       const int idx = s_cidx[tid];
       int rank = 0;
       for (int j = 0; j < C; ++j) {
-        const uint32_t kj = s_ckey[j];
-        rank += kj > key || (kj == key && s_cidx[j] < idx);
+        const float xj = s_cval[j];
+        rank += xj > x || (xj == x && s_cidx[j] < idx);
       }
       if (rank < k) {
-        s_key[rank] = key;
+        s_key[rank] = __float_as_uint(x);
         s_idx[rank] = idx;
       }
     }
     __syncthreads();
-    if (tid < k) write_out(tid, s_key[tid], s_idx[tid]);
+    if (tid < k) write_out(tid, __uint_as_float(s_key[tid]), s_idx[tid]);
     return;
   }
 
-  // Many keys tie at the top: radix select over the whole row.
+  // Many keys tie at the top: radix select over the whole row (read from
+  // memory again).
   uint32_t need;
   const uint32_t thr = radix_kth(key_at, V, &need);   // the k-th largest; `need` equal keys
   // keys above the threshold (fewer than k, any order), and the equal keys of
@@ -309,7 +362,7 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
       const uint32_t kj = s_key[j];
       rank += kj > key || (kj == key && s_idx[j] < idx);
     }
-    write_out(rank, key, idx);
+    write_out(rank, value_of_key<DT>(key), idx);
   }
 }
 
@@ -473,15 +526,16 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
 hipError_t launch_draft_topk(int dtype, const void* logits, int R, int V, int k, const float* temp,
                              int* tokens, float* logprob, hipStream_t st) {
   const int es = dtype == 1 ? 2 : 4;
-  const int vec_ok = ((long long)V * es) % 16 == 0 && ((uintptr_t)logits & 15u) == 0;
-  const bool cached = (long long)V * es <= (long long)kTopkCacheWords * 4;
+  const bool vec_ok = ((long long)V * es) % 16 == 0 && ((uintptr_t)logits & 15u) == 0;
+  // keys in registers: aligned rows of up to 4 vectors per thread
+  const bool reg = vec_ok && (long long)V * es <= (long long)kTopkRegVecs * kFinThreads * 16;
   const dim3 grid((unsigned)R), block(kFinThreads);
   if (dtype == 1) {
-    if (cached) draft_topk_kernel<1, true><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
-    else draft_topk_kernel<1, false><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
+    if (reg) draft_topk_kernel<1, true><<<grid, block, 0, st>>>(logits, V, k, temp, tokens, logprob);
+    else draft_topk_kernel<1, false><<<grid, block, 0, st>>>(logits, V, k, temp, tokens, logprob);
   } else {
-    if (cached) draft_topk_kernel<0, true><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
-    else draft_topk_kernel<0, false><<<grid, block, 0, st>>>(logits, V, k, temp, vec_ok, tokens, logprob);
+    if (reg) draft_topk_kernel<0, true><<<grid, block, 0, st>>>(logits, V, k, temp, tokens, logprob);
+    else draft_topk_kernel<0, false><<<grid, block, 0, st>>>(logits, V, k, temp, tokens, logprob);
   }
   return hipGetLastError();
 }

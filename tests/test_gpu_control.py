@@ -119,6 +119,34 @@ def test_draft_topk_heavy_ties():
     say("[control] draft top-k with heavy ties ok")
 
 
+def test_draft_topk_signed_zero_ties():
+    """-0 and +0 are equal logits: ties between them go to the lower id, in
+    the direct path (a few zeros at the top) and in the whole-row path (more
+    zeros at the top than candidates are ranked directly)."""
+    import rejection_sampling_verify_04_amd as sv
+    rng = np.random.default_rng(105)
+    R, V, k = 4, 32000, 8
+    x = -np.abs(rng.normal(1, 1, size=(R, V))).astype(np.float32) - 0.5
+    for r, n in enumerate([5, 12, 3000, 20000]):
+        pos = rng.choice(V, n, replace=False)
+        x[r, pos] = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0))
+    for dt in (1, 0):
+        if dt == 1:
+            bits = synth.bf16_bits(x)
+            vals = synth.bf16_values(bits).astype(np.float64)
+            dev = logits_to_dev(bits, 1)
+        else:
+            vals = x.astype(np.float64)
+            dev = logits_to_dev(x, 0)
+        tok, lp = sv.draft_topk(dev, k)
+        tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
+        for r in range(R):
+            rt, rl = OD.topk_candidates(vals[r], k, 1.0)
+            assert np.array_equal(tok[r], rt), (dt, r, tok[r], rt)
+            assert np.all(np.abs(lp[r] - rl) <= 1e-5 * np.maximum(1.0, np.abs(rl)))
+    say("[control] draft top-k signed-zero ties ok")
+
+
 def gpu_forest(rng, V, width, depth, B):
     """Full forests from the GPU's own top-k of random draft rows."""
     import rejection_sampling_verify_04_amd as sv

@@ -86,3 +86,12 @@ def test_prune_ties_and_impossible_candidates():
     par, tok, cum, _ = D.prune_tree(parent, token, logq, 10)
     assert 12 not in tok                      # zero probability: never kept
     assert list(tok) == [-1, 10, 11, 20, 21, 30]
+
+
+def test_topk_signed_zeros_are_one_value():
+    # -0 and +0 compare equal as logits, so the lower id ranks first and
+    # both carry the same log-probability
+    tok, lp = D.topk_candidates(np.array([-1.0, -0.0, 0.0, -2.0]), 3, 1.0)
+    assert tok.tolist() == [1, 2, 0]
+    assert lp[0] == lp[1]
+    assert abs(lp[0] - (0.0 - np.log(2.0 + np.exp(-1.0) + np.exp(-2.0)))) < 1e-15
