@@ -140,8 +140,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int ci = j * kThreads + tid;
       const int key = ci >> 4, d0 = (ci & 15) * 8;
       const int gk = min(t * kKT + key, total - 1);
-      kr[j] = *(const u32x4_t*)(a.k + headKV + (long long)gk * kD + d0);
-      vr[j] = *(const u32x4_t*)(a.v + headKV + (long long)gk * kD + d0);
+      // the cache rows are read once: non-temporal loads
+      kr[j] = __builtin_nontemporal_load((const u32x4_t*)(a.k + headKV + (long long)gk * kD + d0));
+      vr[j] = __builtin_nontemporal_load((const u32x4_t*)(a.v + headKV + (long long)gk * kD + d0));
     }
   };
   auto store_tile = [&](const u32x4_t (&kr)[4], const u32x4_t (&vr)[4], int buf) {

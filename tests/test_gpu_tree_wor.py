@@ -89,6 +89,18 @@ def test_wor_greedy_and_mixed_temperatures():
     check(d, "greedy and mixed temperatures")
 
 
+def test_wor_two_chunks_mixed_temperatures():
+    # V = 12000: two chunks with the target term kept in LDS across a node's
+    # passes, one-hot (greedy) terms included
+    d = synth.tree_wor(seed=19, B=24, N=21, V=12000, draft_sd=5.0, pert=1.0)
+    tt, td = d["temp_target"].copy(), d["temp_draft"].copy()
+    tt[0::4] = 0.0
+    td[1::4] = 0.0
+    tt[3::4], td[3::4] = 0.7, 1.3
+    d["temp_target"], d["temp_draft"] = tt, td
+    check(d, "V=12000 bf16, mixed temperatures")
+
+
 def test_wor_repeated_sibling_tokens():
     # duplicate children (a sampler with replacement): the zero-q path and warning
     d = synth.tree_wor(seed=17, B=24, N=21, V=64, draft_sd=6.0, pert=1.0, dtype=synth.F32)
