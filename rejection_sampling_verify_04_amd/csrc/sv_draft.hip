@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* log
     for (int j = 0; j < kTopkRegVecs; ++j) {
       const int vj = tid + j * kFinThreads;
       okv[j] = vj * EPV < V;
-      raw[j] = *(const u32x4_t*)(row + (long long)(okv[j] ? vj : 0) * 16);
+      raw[j] = __builtin_nontemporal_load((const u32x4_t*)(row + (long long)(okv[j] ? vj : 0) * 16));
     }
 #pragma unroll
     for (int j = 0; j < kTopkRegVecs; ++j) {

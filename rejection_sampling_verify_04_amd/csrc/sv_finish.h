@@ -220,8 +220,11 @@ __device__ __forceinline__ void stop_load(const StopDist& d, int V, int chunk, S
   for (int j = 0; j < StopVec<DT>::NV; ++j) {
     const int ej = e0 + j * EPV;
     const long long off = ej < V ? (long long)ej * ES : 0;
-    r.p[j] = *(const uint4*)(prow + off);
-    r.q[j] = *(const uint4*)(qrow + off);
+    // read once per pass: non-temporal loads
+    const u32x4_t pv = __builtin_nontemporal_load((const u32x4_t*)(prow + off));
+    const u32x4_t qv = __builtin_nontemporal_load((const u32x4_t*)(qrow + off));
+    r.p[j] = make_uint4(pv.x, pv.y, pv.z, pv.w);
+    r.q[j] = make_uint4(qv.x, qv.y, qv.z, qv.w);
   }
 }
 
