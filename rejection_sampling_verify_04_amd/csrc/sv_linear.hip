@@ -280,7 +280,6 @@ constexpr int kMassRecCache = 512;   // batch-row decisions staged in LDS by the
 template <int DT, bool CACHE>
 __global__ __launch_bounds__(kFinThreads) void linear_mass_kernel(LinearArgs a) {
   __shared__ LinRecord s_rec[CACHE ? kMassRecCache : 1];
-  __shared__ double s_scan[kFinWaves];
   const int nc = a.n_chunks, V = a.V;
   const long long total = (long long)a.B * nc;
   if (CACHE) {
@@ -305,13 +304,14 @@ __global__ __launch_bounds__(kFinThreads) void linear_mass_kernel(LinearArgs a) 
   };
   int b, c;
   bool live;
+  // each wave stores its own total (the wave scan's last lane, as the block
+  // scan forms it), so the waves never wait for one another
   auto reduce = [&](const StopDist& dd, int bb, int cc, const StopVec<DT>& cur, int vec) {
     float w[kPerThread];
     stop_weights_from<DT>(dd, V, cc, vec, 0u, cur, w);
-    const double acc = thread_total(w);
-    double m;
-    block_exclusive_scan<kFinWaves>(acc, s_scan, &m);
-    if (threadIdx.x < kFinWaves) a.wsum[((long long)bb * nc + cc) * kFinWaves + threadIdx.x] = s_scan[threadIdx.x];
+    const double incl = wave_inclusive_scan(thread_total(w));
+    if ((threadIdx.x & 63) == 63)
+      a.wsum[((long long)bb * nc + cc) * kFinWaves + (threadIdx.x >> 6)] = incl;
   };
   if (!a.vec_ok) {                        // unaligned rows: plain loads, no prefetch
     const StopVec<DT> none{};
@@ -356,7 +356,6 @@ __global__ __launch_bounds__(kFinThreads) void linear_mass_kernel(LinearArgs a) 
 template <int DT>
 __global__ __launch_bounds__(kFinThreads) void linear_decide_mass_kernel(LinearArgs a) {
   __shared__ LinShared sh;
-  __shared__ double s_scan[kFinWaves];
   const int n_chunks = a.n_chunks;
   const int b = blockIdx.x / n_chunks;
   const int c = blockIdx.x - b * n_chunks;
@@ -364,9 +363,12 @@ __global__ __launch_bounds__(kFinThreads) void linear_decide_mass_kernel(LinearA
   if (c == 0 && threadIdx.x == 0) a.rec[b] = r;
   if (r.kind != kKindReject && r.kind != kKindBonus) return;
   const StopDist d = record_dist<DT>(a, b, r);
-  chunk_mass<DT>(d, a.V, c, a.vec_ok, 0u, s_scan);
-  if (threadIdx.x < kFinWaves)
-    a.wsum[((long long)b * n_chunks + c) * kFinWaves + threadIdx.x] = s_scan[threadIdx.x];
+  float w[kPerThread];
+  stop_weights<DT>(d, a.V, c, a.vec_ok, 0u, w);
+  // each wave stores its own total (the wave scan's last lane)
+  const double incl = wave_inclusive_scan(thread_total(w));
+  if ((threadIdx.x & 63) == 63)
+    a.wsum[((long long)b * n_chunks + c) * kFinWaves + (threadIdx.x >> 6)] = incl;
 }
 
 // This wave's 64 lanes form the weights of threads 64 w + lane (of 1024) of
