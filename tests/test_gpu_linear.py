@@ -126,6 +126,25 @@ def test_error_rows_multichunk():
     assert gpu["num_accepted"][5] >= 0
 
 
+def test_longest_draft_runs():
+    # gamma = 64 (the largest): 129 logit rows per decision, and Philox slot
+    # 64 serves the 64th draft's test and the bonus draw after it
+    for V, dt in ((1000, synth.F32), (20000, synth.BF16)):
+        d = ragged(19, [64, 63, 40], V, dt, sigma=0.05)
+        tv = d["target"].copy()
+        o0 = d["offsets"][0]
+        tv[o0:o0 + 64] = d["draft"][o0:o0 + 64]     # row 0: every draft accepted
+        d["target"] = tv
+        gpu, ref, _ = check(d, "gamma 64, V=%d" % V)
+        assert gpu["num_accepted"][0] == 64
+
+
+def test_largest_vocabulary():
+    # V = 524288: the 64 chunks the finish passes support
+    d = ragged(20, [2, 3], 524288, synth.BF16, sigma=0.3)
+    check(d, "V=524288 bf16")
+
+
 def test_row_ids_make_packing_irrelevant():
     d = ragged(17, [4, 4, 4, 4], 6000, synth.BF16)
     ids = np.array([7, 1000003, 5, 2 ** 31 + 9], dtype=np.uint32)

@@ -42,6 +42,12 @@ def test_peaked_trees_bf16_multichunk():
     check(d, "peaked V=20000 bf16")
 
 
+def test_largest_vocabulary_trees():
+    # V = 524288 (64 chunks): the stop draw picks one chunk of 64
+    d = synth.tree_v32k(seed=24, B=2, N=8, V=524288, draft_sd=3.0, pert=0.5)
+    check(d, "V=524288 bf16")
+
+
 def test_greedy_and_mixed_temperature_trees():
     d = synth.peaked_tree(seed=22, B=24)
     d["temp_target"] = np.where(np.arange(24) % 3 == 0, 0.0, d["temp_target"]).astype(np.float32)
