@@ -107,6 +107,83 @@ def cpu_baseline_linear(d, seconds):
                        "single-threaded NumPy float64" % (rows, done_pos, dt))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+_POOL_DATA = None
+
+
+def _oracle_batch_row(d, bb):
+    """One batch row of the workload through the oracle; returns its draft positions / nodes."""
+    import oracle
+    if d["kind"] == "linear":
+        off = d["offsets"]
+        o0, o1 = int(off[bb]), int(off[bb + 1])
+        t = o0 + bb
+        oracle.verify_linear(d["target"][t:t + o1 - o0 + 1], d["draft"][o0:o1], d["dtype"],
+                             np.array([0, o1 - o0]), d["tokens"][o0:o1],
+                             d["temp_target"][bb:bb + 1], d["temp_draft"][bb:bb + 1],
+                             seed=0, step=0, row_ids=np.array([bb]))
+        return o1 - o0
+    if d["kind"] == "tree_wor":
+        oracle.verify_tree_sampled_wor(d["target"][bb:bb + 1], d["draft"][bb:bb + 1], d["dtype"],
+                                       d["parents"][bb:bb + 1], d["tokens"][bb:bb + 1],
+                                       d["n_nodes"][bb:bb + 1], d["temp_target"][bb:bb + 1],
+                                       d["temp_draft"][bb:bb + 1], row_ids=np.array([bb]))
+    else:
+        oracle.verify_tree_topk(d["target"][bb:bb + 1], d["dtype"], d["parents"][bb:bb + 1],
+                                d["tokens"][bb:bb + 1], d["n_nodes"][bb:bb + 1],
+                                d["temp_target"][bb:bb + 1], row_ids=np.array([bb]))
+    return int(d["n_nodes"][bb]) - 1
+
+
+def _pool_worker(arg):
+    w, n, deadline = arg
+    d = _POOL_DATA
+    B = len(d["offsets"]) - 1 if d["kind"] == "linear" else d["B"]
+    units = rows = 0
+    b = w
+    while time.monotonic() < deadline:
+        units += _oracle_batch_row(d, b % B)
+        rows += 1
+        b += n
+    return units, rows
+
+
+def cpu_baseline_pool(d, seconds):
+    """The oracle over all host cores: one process per core (at most 16), forked
+    before the GPU is touched, worker w taking batch rows w, w + n, ... for
+    ~seconds.  (A thread pool gains nothing: the oracle's per-position work is
+    Python that holds the interpreter lock.)"""
+    import multiprocessing
+    global _POOL_DATA
+    n = min(16, len(os.sched_getaffinity(0)))
+    _POOL_DATA = d
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.monotonic()
+    with ctx.Pool(n) as pool:
+        res = pool.map(_pool_worker, [(w, n, t0 + seconds) for w in range(n)])
+    dt = time.monotonic() - t0
+    _POOL_DATA = None
+    units = sum(r[0] for r in res)
+    rows = sum(r[1] for r in res)
+    linear = d["kind"] == "linear"
+    return dict(value=units / dt, unit="verified draft positions/s" if linear else "verified draft nodes/s",
+                cores=n, kind="oracle",
+                sample="%d batch rows (%d %s) of the same workload in %.1f s, NumPy float64 in "
+                       "%d processes (%s)"
+                       % (rows, units, "draft positions" if linear else "draft nodes", dt, n,
+                          cpu_model()))
+
+
 def cpu_baseline_tree(d, seconds):
     import oracle
     B = d["B"]
@@ -243,8 +320,16 @@ def main():
     import synth
     import rejection_sampling_verify_04_amd as sv
 
-    torch.cuda.set_device(0)
     wl = args.workload
+    # The oracle over all host cores runs first: its worker processes are
+    # forked before anything touches the GPU.
+    early = None
+    pool_baseline = None
+    if wl in synth.WORKLOADS:
+        early = synth.WORKLOADS[wl]()
+        if not args.no_cpu_baseline:
+            pool_baseline = cpu_baseline_pool(early, args.cpu_seconds)
+    torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     dev = torch.device("cuda", 0)
 
@@ -358,7 +443,7 @@ def main():
         unit = "verified query tokens/s"
         metric = "verify-attention query tokens/sec + achieved HBM GB/s (% of peak)"
     else:
-        d = synth.WORKLOADS[wl]()
+        d = early if early is not None else synth.WORKLOADS[wl]()
         per_call = synth.logits_bytes(d)
         nc = copies_for(per_call)
         if d["kind"] == "linear":
@@ -504,6 +589,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)
         else:
             out["cpu_baseline"] = cpu_baseline_tree(d, args.cpu_seconds)
+        if pool_baseline is not None:
+            out["cpu_baseline_pool"] = pool_baseline
     print(json.dumps(out), flush=True)
 
 
