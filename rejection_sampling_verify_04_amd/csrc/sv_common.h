@@ -170,6 +170,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+__device__ __forceinline__ unsigned long long wave_or_u64(unsigned long long v) {
+  v |= dpp_u64<kDppXor1>(v);
+  v |= dpp_u64<kDppXor2>(v);
+  v |= dpp_u64<kDppHalfMirror>(v);
+  v |= dpp_u64<kDppMirror>(v);
+  return readlane_u64(v, 0) | readlane_u64(v, 16) | readlane_u64(v, 32) | readlane_u64(v, 48);
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
   uint64_t w = dpp_u64<kDppXor1>(v);
   v = w > v ? w : v;

@@ -295,7 +295,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(ur), V, (int)ch * kChunk + r * kSubSpan);
   }
-
   if (cache) {
     for (int i = threadIdx.x; i <= a.B; i += kThreads) {
       if (a.tree) {
@@ -304,7 +303,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
           s_i[i] = (nn >= 1 && nn <= a.N) ? nn : 0;   // a bad count: no row is read
           s_f0[i] = a.temp_a[i];
           s_f1[i] = a.temp_b[i];
-          if (cache_inner) s_inner[i] = 0ull;
         }
       } else {
         s_i[i] = a.offsets[i];
@@ -315,51 +313,24 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       }
     }
     __syncthreads();
-    if (cache_inner) {
-      // 16 parents per thread in flight at once (clamped indices: no load
-      // behind a branch, so none is waited for alone)
-      const int N = a.N, BN = a.B * N;
-      constexpr int kBatch = 16;
-      for (int i0 = threadIdx.x; i0 < BN; i0 += kThreads * kBatch) {
-        int pv[kBatch];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) pv[k] = a.parents[min(i0 + k * kThreads, BN - 1)];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const int i = i0 + k * kThreads;
-          const int b = i / N, c = i - b * N;
-          const int par = pv[k];
-          if (i < BN && c > 0 && c < s_i[b] && par >= 0 && par < c)
-            atomicOr(&s_inner[b], 1ull << par);
-        }
-      }
-      __syncthreads();
-    }
   }
+  // Exclusive prefix over the trees of cnt(b) (two trees per thread) into pre.
+  auto tree_prefix = [&](int* pre, auto cnt) {
+    const int i0 = 2 * threadIdx.x;
+    const int c0 = i0 < a.B ? cnt(i0) : 0, c1 = i0 + 1 < a.B ? cnt(i0 + 1) : 0;
+    double tot;
+    const int ex = (int)block_exclusive_scan<kWaves>((double)(c0 + c1), s_scan, &tot);
+    if (i0 < a.B) pre[i0] = ex;
+    if (i0 + 1 < a.B) pre[i0 + 1] = ex + c0;
+    if (threadIdx.x == 0) pre[a.B] = (int)tot;
+    __syncthreads();
+  };
   uint32_t n_t = 0;   // compacted: used target rows (they come first)
   if (compact) {
-    // exclusive prefixes of the used rows per tree, two trees per thread
-    for (int h = 0; h < 2; ++h) {
-      const bool q = h == 1;
-      if (q && !tree_q) break;
-      int* pre = q ? s_pq : s_pt;
-      const int i0 = 2 * threadIdx.x;
-      auto cnt = [&](int b) -> int {
-        if (b >= a.B) return 0;
-        return q ? __popcll(s_inner[b]) : s_i[b];
-      };
-      const int c0 = cnt(i0), c1 = cnt(i0 + 1);
-      double tot;
-      const int ex = (int)block_exclusive_scan<kWaves>((double)(c0 + c1), s_scan, &tot);
-      if (i0 < a.B) pre[i0] = ex;
-      if (i0 + 1 < a.B) pre[i0 + 1] = ex + c0;
-      if (threadIdx.x == 0) pre[a.B] = (int)tot;
-      __syncthreads();
-    }
+    tree_prefix(s_pt, [&](int b) { return s_i[b]; });
     n_t = (uint32_t)s_pt[a.B];
-    total = (n_t + (tree_q ? (uint32_t)s_pq[a.B] : 0u)) * nc;
   }
-  // The row of iteration row x.
+  // The row of iteration row x (draft rows: once the inner masks are known).
   auto row_of = [&](uint32_t x) -> uint32_t {
     if (!compact) return x;
     const int N = a.N;
@@ -371,9 +342,46 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     const int b = wave_find_batch_row(s_pq, a.B, (long long)y, 0);
     return (uint32_t)a.n_a + (uint32_t)(b * N + wave_kth_bit(s_inner[b], (int)y - s_pq[b]));
   };
+  // A compacted wave whose first unit is a target row issues its loads now,
+  // ahead of the inner masks of the draft rows.
+  bool issued = false;
+  if (compact && a.vec_ok && ur < n_t) {
+    const uint32_t r0 = row_of(ur);
+#pragma unroll
+    for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(r0), V, (int)ch * kChunk + r * kSubSpan);
+    issued = true;
+  }
+  if (cache_inner) {
+    // one wave per tree (a lane per node, N <= 64): the mask is the OR of the
+    // lanes' parent bits; a wave's trees are taken 16 at a time, their
+    // parents loaded together (clamped indices: no load behind a branch)
+    const int N = a.N;
+    constexpr int kMaskBatch = 16;
+    const int c = lane < N ? lane : N - 1;
+    for (int b0 = wave; b0 < a.B; b0 += kWaves * kMaskBatch) {
+      int pv[kMaskBatch];
+#pragma unroll
+      for (int k = 0; k < kMaskBatch; ++k)
+        pv[k] = a.parents[(long long)min(b0 + k * kWaves, a.B - 1) * N + c];
+#pragma unroll
+      for (int k = 0; k < kMaskBatch; ++k) {
+        const int b = b0 + k * kWaves;
+        const int bc = b < a.B ? b : a.B - 1;
+        const int par = pv[k];
+        const bool kid = b < a.B && lane > 0 && lane < s_i[bc] && par >= 0 && par < lane;
+        const unsigned long long m = wave_or_u64(kid ? 1ull << par : 0ull);
+        if (lane == 0 && b < a.B) s_inner[b] = m;
+      }
+    }
+    __syncthreads();
+  }
+  if (compact) {
+    if (tree_q) tree_prefix(s_pq, [&](int b) { return __popcll(s_inner[b]); });
+    total = (n_t + (tree_q ? (uint32_t)s_pq[a.B] : 0u)) * nc;
+  }
   if (u >= total) return;
   uint32_t row = row_of(ur);
-  if (compact && a.vec_ok) {
+  if (compact && a.vec_ok && !issued) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
   }
