@@ -314,13 +314,14 @@ int spec_verify_telemetry_summary(const sv_telemetry* acc, double* out, hipStrea
  * Draft candidates (blog.lonae.com/posts/2026-draft-model-kv-jDwzYp,
  * tree-attention paragraphs: every draft position branches into the
  * draft's top-k candidates).  For each of R draft rows [R, V] `dtype`, the
- * k tokens of largest logit, largest first (ties to the lower id), and
- * their log-probabilities log softmax(x / T)[token] at the row's
- * temperature (temp [R], NULL for 1; T = 0: 0 for the first token and -inf
- * for the rest; a negative or non-finite T: tokens -1, NaN).  1 <= k <= 64,
- * k <= V.  tokens, logprob: [R, k].  One work item per row (a radix select
- * on order-preserving keys, then the keys above the k-th and, in index
- * order, enough keys equal to it).
+ * k tokens of largest logit, largest first (equal logits to the lower id;
+ * -0 and +0 are equal), and their log-probabilities log softmax(x / T)[token]
+ * at the row's temperature (temp [R], NULL for 1; T = 0: 0 for the first
+ * token and -inf for the rest; a negative or non-finite T: tokens -1, NaN).
+ * 1 <= k <= 64, k <= V.  NaN logits are undefined behaviour.  tokens,
+ * logprob: [R, k].  One work item per row: the logits at or above a lower
+ * bound of the k-th largest are ranked directly; when more than 1024 tie
+ * there, a radix select over the row takes over.
  */
 int spec_verify_draft_topk(const void* logits, int dtype, int R, int V, int k,
                            const float* temp, int32_t* tokens, float* logprob, hipStream_t stream);

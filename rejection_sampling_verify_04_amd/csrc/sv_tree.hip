@@ -3,7 +3,8 @@
 //                 in one chunk of the stop row.
 //   SAMPLED_WOR   tree_wor_kernel walks it with the whole block: one
 //                 vocabulary pass over the node's target and draft rows per
-//                 rejected sibling, then the draw.
+//                 rejected sibling (the target term kept in LDS across a
+//                 node's passes when V <= 32768), then the draw.
 //
 // Sources: tree walk over siblings drawn by top-k or by temperature sampling
 // (kwkr.cn/news/620872 §5.3; blog.lonae.com/posts/
