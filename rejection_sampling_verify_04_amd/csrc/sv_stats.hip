@@ -508,6 +508,69 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     T = T1;
   }
 }
+// Linear batches that one round of work items covers: a work item of four
+// waves per (row, chunk), wave w reducing sub-segment w (2048 logits, all of
+// its loads in flight at once), the four wave partials merged in LDS.
+// Shorter waves than one chunk each spread the exponentials evenly over the
+// SIMDs when there are few chunks per SIMD.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void stats_kernel_by_chunk(StatsArgs a) {
+  __shared__ int s_off[kStatsCache + 1];   // the gather's batch-row offsets
+  __shared__ Partial s_part[kWaves];
+
+  const int n_gblk = gather_blocks(a);
+  if ((int)blockIdx.x < n_gblk) {
+    gather_logits<DT>(a, s_off);
+    return;
+  }
+  const uint32_t nc = (uint32_t)a.n_chunks;
+  const uint32_t unit = blockIdx.x - n_gblk;
+  const uint32_t r = unit / nc, c = unit - r * nc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int V = a.V;
+  const long long rowbytes = (long long)V * SegLoad<DT>::ES;
+  const char* rowp = r < a.n_a ? (const char*)a.rows_a + (long long)r * rowbytes
+                               : (const char*)a.rows_b + ((long long)r - a.n_a) * rowbytes;
+  const int seg0 = (int)c * kChunk + wave * kSubSpan;
+  SegLoad<DT> seg;
+  if (a.vec_ok) seg.issue(rowp, V, seg0);
+  // the row's temperature, its batch row found from the offsets
+  const float T = r < a.n_a ? a.temp_a[wave_find_batch_row(a.offsets, a.B, (long long)r, 1)]
+                            : a.temp_b[wave_find_batch_row(a.offsets, a.B, (long long)r - a.n_a, 0)];
+  const bool ok = temp_ok(T);   // a bad temperature is reported by the finish pass
+  const bool greedy = T == 0.0f;
+  const float k2 = greedy ? 0.0f : log2e_over_t(T);
+  LaneStats st{-__builtin_huge_valf(), seg0 + lane * SegLoad<DT>::EPV, 0.0};
+  if (ok) {
+    float v[kPerLane];
+    if (a.vec_ok) seg.unpack(v);
+    else seg_load_scalar<DT>(rowp, V, seg0, v);
+    lane_fold<DT>(v, seg0, greedy, k2, st);
+  }
+  const Partial p = ok ? wave_combine(st, greedy) : Partial{0.0f, 0, 0.0};
+  if (lane == 0) s_part[wave] = p;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Partial out = s_part[0];
+    if (ok && greedy) {
+      // the largest value, at its lowest index (the waves' ranges increase)
+      for (int w = 1; w < kWaves; ++w)
+        if (s_part[w].c > out.c) out = s_part[w];
+    } else if (ok) {
+      float C = s_part[0].c;
+      for (int w = 1; w < kWaves; ++w) C = fmaxf(C, s_part[w].c);
+      double sum = 0.0;
+      if (C > -__builtin_huge_valf()) {
+        for (int w = 0; w < kWaves; ++w)
+          if (s_part[w].s != 0.0) sum += scale_pow2(s_part[w].s, s_part[w].c - C);
+      }
+      out = Partial{C, 0, sum};
+    }
+    a.part[(long long)r * nc + c] = out;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Raw Philox words (diagnostic entry point).
 
@@ -539,6 +602,11 @@ static int stats_resident_blocks(int dt, int ring) {
   return resident_blocks(2, stats_kernel<0, 2>, kThreads);
 }
 
+static int stats_by_chunk_resident_blocks(int dt) {
+  return dt == 1 ? resident_blocks(5, stats_kernel_by_chunk<1>, kThreads)
+                 : resident_blocks(6, stats_kernel_by_chunk<0>, kThreads);
+}
+
 // Pass 1.  Launched with events, the events bracket the kernel's dispatch.
 hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_t ev_start,
                         hipEvent_t ev_stop) {
@@ -552,6 +620,13 @@ hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_
     if (timed) hipExtLaunchKernelGGL(K, grid, block, 0, st, ev_start, ev_stop, 0, a); \
     else K<<<grid, block, 0, st>>>(a);                                        \
   } while (0)
+  // linear batches that one round of (row, chunk) work items covers
+  if (!a.tree && units <= stats_by_chunk_resident_blocks(dt)) {
+    const dim3 grid((unsigned)(units + gather_blocks(a)));
+    if (dt == 1) SV_LAUNCH((stats_kernel_by_chunk<1>));
+    else SV_LAUNCH((stats_kernel_by_chunk<0>));
+    return hipGetLastError();
+  }
   const long long want = (units + kWaves - 1) / kWaves;
   // a whole chunk in flight per wave when one round of waves covers the call
   const int ring = (dt == 1 && want <= stats_resident_blocks(1, 4)) ? 4 : 2;
