@@ -292,6 +292,15 @@ def load_traffic(path, workload, kernel_sig):
     return t.get("hbm_bytes_per_launch")
 
 
+def dominant_kernel(wl):
+    """The kernel whose duration the roofline reports: the vocabulary pass, which
+    for linear calls of one round of (row, chunk) work items is its by-chunk form."""
+    return {"attn_tree": "attn_kernel", "kv_commit": "kv_commit_kernel",
+            "draft_topk": "draft_topk_kernel", "tree_prune": "tree_prune_kernel",
+            "linear_v32k": "stats_kernel_by_chunk",
+            "linear_v1000": "stats_kernel_by_chunk"}.get(wl, "stats_kernel")
+
+
 def kernel_source_sig(wl):
     """SHA-1 over the sources that the dominant kernel is compiled from (its
     own file and the headers that file includes)."""
@@ -574,9 +583,7 @@ def main():
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=traffic,
-                kernel={"attn_tree": "attn_kernel", "kv_commit": "kv_commit_kernel",
-                        "draft_topk": "draft_topk_kernel",
-                        "tree_prune": "tree_prune_kernel"}.get(wl, "stats_kernel"),
+                kernel=dominant_kernel(wl),
                 algorithmic_bytes_per_launch=int(alg_bytes),
                 avg_kernel_us=round(avg_kern_s * 1e6, 2),
                 median_kernel_us=round(float(np.median(kern_ms)) * 1e3, 2),
