@@ -55,6 +55,13 @@ def test_ragged_multichunk_fp32_unaligned():
     check(ragged(12, gammas, 10007, synth.F32, sigma=0.4), "ragged 10007 fp32 (scalar path)")
 
 
+def test_ragged_fp32_five_chunks():
+    # V = 40000 fp32 (aligned, 5 chunks): the pipelined mass pass in fp32
+    rng = np.random.default_rng(21)
+    gammas = rng.integers(0, 7, size=10)
+    check(ragged(21, gammas, 40000, synth.F32, sigma=0.5), "ragged 40000 fp32")
+
+
 def test_unaligned_bf16():
     check(ragged(13, [3, 5, 0, 2], 8191, synth.BF16, sigma=0.5), "8191 bf16 (scalar path)")
 
