@@ -288,10 +288,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   uint32_t ur = u / nc, ch = u - ur * nc;   // ur: row in the order the units run
 
   SegLoad<DT> ring[RING];
-  // The first chunk's loads go out before anything else (compacted trees:
-  // once the row map is known); an unused tree row is still allocated, so
-  // reading it is harmless.
-  if (!compact && a.vec_ok && u < total) {
+  // The first chunk's loads go out before anything else.  Compacted trees
+  // issue them for row ur as if no row were unused (full trees keep them)
+  // and issue again below if the row map moves the unit; an unused tree row
+  // is still allocated, so reading it is harmless.
+  if (a.vec_ok && u < total) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(ur), V, (int)ch * kChunk + r * kSubSpan);
   }
@@ -342,13 +343,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     const int b = wave_find_batch_row(s_pq, a.B, (long long)y, 0);
     return (uint32_t)a.n_a + (uint32_t)(b * N + wave_kth_bit(s_inner[b], (int)y - s_pq[b]));
   };
-  // A compacted wave whose first unit is a target row issues its loads now,
-  // ahead of the inner masks of the draft rows.
+  // A compacted wave whose first unit is a target row has its loads right
+  // now, ahead of the inner masks of the draft rows.
   bool issued = false;
   if (compact && a.vec_ok && ur < n_t) {
     const uint32_t r0 = row_of(ur);
+    if (r0 != ur) {
 #pragma unroll
-    for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(r0), V, (int)ch * kChunk + r * kSubSpan);
+      for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(r0), V, (int)ch * kChunk + r * kSubSpan);
+    }
     issued = true;
   }
   if (cache_inner) {
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
   if (u >= total) return;
   uint32_t row = row_of(ur);
-  if (compact && a.vec_ok && !issued) {
+  if (compact && a.vec_ok && !issued && row != ur) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
   }
