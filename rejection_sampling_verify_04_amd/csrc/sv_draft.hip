@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
       const int np = pq < 0 ? 0 : (here ? s_new[pq] : 0);
       const uint32_t key = here ? ((uint32_t)np << 10) | (uint32_t)rq : 0xFFFFFFFFu;
       int pos = 0;
-      for (int j = 0; j < K; ++j) pos += __builtin_amdgcn_readlane(key, j) < key;
+      for (int j = 0; j < K; ++j) pos += (uint32_t)__builtin_amdgcn_readlane((int)key, j) < key;
       const int n_here = __popcll(__ballot(here));
       if (here) s_new[ci] = base + pos;
       base += n_here;
