@@ -407,7 +407,9 @@ __device__ __forceinline__ void wor_weights(const WorDist& d, int V, int chunk,
 
 // Block totals of NV per-thread values, each formed exactly as
 // block_exclusive_scan forms its total (so a chunk's mass here equals the
-// total of the draw's in-chunk scan bit for bit).  All threads get them.
+// total of the draw's in-chunk scan bit for bit).  Lane i of wave 0 forms
+// total i (the wave-order sum) and shares it; all threads get them.
+// s_red holds (kFinWaves + 1) * NV values.
 template <int NV>
 __device__ __forceinline__ void block_totals(const double v[NV], double* s_red, double t[NV]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -418,13 +420,15 @@ __device__ __forceinline__ void block_totals(const double v[NV], double* s_red, 
     if (lane == 63) s_red[w * NV + i] = incl;
   }
   __syncthreads();
+  if (threadIdx.x < NV) {
+    double s = s_red[threadIdx.x];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    double s = s_red[i];
-#pragma unroll
-    for (int k = 1; k < kFinWaves; ++k) s += s_red[k * NV + i];
-    t[i] = s;
+    for (int k = 1; k < kFinWaves; ++k) s += s_red[k * NV + threadIdx.x];
+    s_red[kFinWaves * NV + threadIdx.x] = s;
   }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) t[i] = s_red[kFinWaves * NV + i];
 }
 
 // One pass over the node's rows: chunk masses of the weights into s_mass
@@ -531,9 +535,9 @@ __device__ __forceinline__ void wor_fill(const WorDist& d, int V, float* s_a) {
 // and the draft row's values from `r`.
 template <int DT, bool WANT_E>
 __device__ __forceinline__ void wor_weights_c(const WorDist& d, int V, int chunk, int tix,
-                                              const StopVec<DT>& r, const float* s_a, float lam,
-                                              const int* ex_tok, const float* ex_lam, int nex,
-                                              int t_cur, float w[kPerThread],
+                                              bool excl, const StopVec<DT>& r, const float* s_a,
+                                              float lam, const int* ex_tok, const float* ex_lam,
+                                              int nex, int t_cur, float w[kPerThread],
                                               float be[kPerThread]) {
   constexpr int EPV = StopVec<DT>::EPV;
   const int e0 = chunk * kChunk + tix * kPerThread;
@@ -555,6 +559,17 @@ __device__ __forceinline__ void wor_weights_c(const WorDist& d, int V, int chunk
   const float4 lo = ca[0], hi = ca[1];
   av[0] = lo.x; av[1] = lo.y; av[2] = lo.z; av[3] = lo.w;
   av[4] = hi.x; av[5] = hi.y; av[6] = hi.z; av[7] = hi.w;
+  if (!excl && !d.onehot && e0 + kPerThread <= V) {
+    // no excluded token (nor t_cur) among these elements, sampled rows, all
+    // inside the row: lambda for every element (the same values as below)
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const float b = exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
+      w[e] = fmaxf(fmaf(-lam, b, av[e]), 0.0f);
+      if (WANT_E) be[e] = b;
+    }
+    return;
+  }
   float lv[kPerThread];
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) lv[e] = lam;
@@ -615,11 +630,23 @@ __device__ double wor_pass_c(const WorDist& d, int V, float lam, const int* ex_t
       r[c].q[j] = *(const uint4*)(d.yrow + (ej < V ? (long long)ej * ES : 0));
     }
   }
+  // the chunks in which an excluded token (or t_cur) falls among this
+  // thread's elements: one scan of the list per pass
+  uint32_t hit = 0u;
+  for (int k = 0; k < nex; ++k) {
+    const int t = ex_tok[k], c = t / kChunk;
+    if ((t - c * kChunk) / kPerThread == tix) hit |= 1u << c;
+  }
+  if (WANT_E && t_cur >= 0) {
+    const int c = t_cur / kChunk;
+    if ((t_cur - c * kChunk) / kPerThread == tix) hit |= 1u << c;
+  }
   double v[NC + 1], e_acc = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float w[kPerThread], be[kPerThread];
-    wor_weights_c<DT, WANT_E>(d, V, c, tix, r[c], s_a, lam, ex_tok, ex_lam, nex, t_cur, w, be);
+    wor_weights_c<DT, WANT_E>(d, V, c, tix, ((hit >> c) & 1u) != 0u, r[c], s_a, lam, ex_tok,
+                              ex_lam, nex, t_cur, w, be);
     v[c] = thread_total(w);
     if (WANT_E) e_acc += thread_total(be);
     // one chunk's values live at a time
@@ -651,7 +678,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   __shared__ double s_ex_lam[kMaxNodes];           // their lambda (ratios)
   __shared__ unsigned long long s_inner;
   __shared__ int s_flags;
-  __shared__ double s_red[kFinWaves * ((NC > kWorGroup ? NC : kWorGroup) + 1)];
+  __shared__ double s_red[(kFinWaves + 1) * ((NC > kWorGroup ? NC : kWorGroup) + 1)];
   __shared__ double s_scan[kFinWaves];
   __shared__ double s_mass[kMaxChunks];
   __shared__ int s_found[kFinWaves], s_last[kFinWaves];
