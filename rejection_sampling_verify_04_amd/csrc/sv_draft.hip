@@ -419,7 +419,11 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
     }
     s_depth[i] = depth;
     s_rank[i] = rank;
-    atomicMax(&s_maxd, depth);
+  }
+  {
+    // the deepest candidate: a wave maximum, then one LDS atomic per wave
+    const int wm = (int)wave_max_u64((unsigned long long)depth);
+    if ((tid & 63) == 0 && wm > 0) atomicMax(&s_maxd, wm);
   }
   __syncthreads();
   const int maxd = bad ? 0 : min(s_maxd, kPruneMax);
@@ -502,7 +506,11 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
     a.parents[ob + ni] = par < 0 ? 0 : s_new[par];
     a.tokens[ob + ni] = a.cand_token[cb + i];
     a.cum_logprob[ob + ni] = (float)cum;
-    if (exp(cum) >= a.tau) atomicAdd(&s_pass, 1);
+  }
+  {
+    // kept nodes of cumulative probability >= tau: a count per wave
+    const int np = __popcll(__ballot(mine && !bad && keep && exp(cum) >= a.tau));
+    if ((tid & 63) == 0 && np > 0) atomicAdd(&s_pass, np);
   }
   if (tid == 0 && !bad) {
     a.parents[ob] = -1;

@@ -727,7 +727,6 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     par = -1;
     tok = 0;
   }
-  if (tid == 0) s_inner = 0ull;
   for (int base = wave * R; base < n_rows; base += kFinWaves * R) {
     const Partial q = base == wave * R ? q0 : load_part(base + sub);
     const int r = base + sub;
@@ -756,7 +755,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     s_tok[tid] = tok;
   }
   __syncthreads();
-  if (tid < 64 && par >= 0) atomicOr(&s_inner, 1ull << par);
+  if (tid < 64) {   // the nodes with children: a wave OR of the parent bits
+    const unsigned long long m = wave_or_u64(par >= 0 ? 1ull << par : 0ull);
+    if (tid == 0) s_inner = m;
+  }
   __syncthreads();
   if (tid < 64) {
     const unsigned long long inner = s_inner;
