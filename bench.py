@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--workload", default="linear_v32k",
                     choices=["linear_v1000", "linear_v32k", "linear_v128k", "bimodal_v152k",
                              "tree_v32k", "tree_wor_v32k", "attn_tree", "kv_commit",
-                             "draft_topk", "tree_prune"])
+                             "draft_topk", "tree_prune", "telemetry", "gamma_update"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying one HIP graph")
@@ -278,6 +278,25 @@ def cpu_baseline_prune(par, tok, logq, n_max, seconds):
                        % (n, dt))
 
 
+def cpu_baseline_control(wl, na, off, seconds):
+    """The oracle's telemetry counters or gamma update over the same rows until ~seconds."""
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    gam = np.diff(off)
+    hist = np.zeros(len(na), dtype=np.int64)
+    while time.perf_counter() - t0 < seconds:
+        if wl == "telemetry":
+            oracle.telemetry.add_linear(oracle.telemetry.empty(), na, off)
+        else:
+            hist, _, _ = oracle.control.gamma_update(hist, na, gam)
+        n += len(na)
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="batch rows/s", cores=1, kind="oracle",
+                sample="%d batch rows (%d calls of %d) in %.1f s, single-threaded Python"
+                       % (n, n // len(na), len(na), dt))
+
+
 def load_traffic(path, workload, kernel_sig):
     """HBM bytes per launch of the dominant kernel, from counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size); None when
@@ -298,7 +317,9 @@ def dominant_kernel(wl):
     return {"attn_tree": "attn_kernel", "kv_commit": "kv_commit_kernel",
             "draft_topk": "draft_topk_kernel", "tree_prune": "tree_prune_kernel",
             "linear_v32k": "stats_kernel_by_chunk",
-            "linear_v1000": "stats_kernel_by_chunk"}.get(wl, "stats_kernel")
+            "linear_v1000": "stats_kernel_by_chunk",
+            "telemetry": "telemetry_linear_kernel",
+            "gamma_update": "gamma_update_kernel"}.get(wl, "stats_kernel")
 
 
 def kernel_source_sig(wl):
@@ -307,7 +328,8 @@ def kernel_source_sig(wl):
     import hashlib
     csrc = os.path.join(ROOT, "rejection_sampling_verify_04_amd", "csrc")
     own = {"attn_tree": "sv_attn.hip", "kv_commit": "sv_kv.hip", "draft_topk": "sv_draft.hip",
-           "tree_prune": "sv_draft.hip"}.get(wl, "sv_stats.hip")
+           "tree_prune": "sv_draft.hip", "telemetry": "sv_telemetry.hip",
+           "gamma_update": "sv_control.hip"}.get(wl, "sv_stats.hip")
     names = [own, "sv_common.h", "sv_internal.h"]
     h = hashlib.sha1()
     for name in names:
@@ -382,6 +404,39 @@ def main():
                           forest="4-wide, 4-deep, top-4 log q of random draft rows")
             unit = "pruned trees/s"
             metric = "tree pruning: trees/sec"
+        flops = 0
+    elif wl in ("telemetry", "gamma_update"):
+        # The control work after a round of the bimodal batch (B=256, ragged
+        # gamma): the round's counters, or the next gamma per request from the
+        # 16-step history.  Outcomes from the library's own verify of it.
+        bm = synth.bimodal_v152k()
+        gv = sv.verify_linear(to_dev_logits(torch, bm["target"], 1), to_dev_logits(torch, bm["draft"], 1),
+                              torch.from_numpy(bm["offsets"]).cuda(), torch.from_numpy(bm["tokens"]).cuda(),
+                              torch.from_numpy(bm["temp_target"]).cuda(),
+                              torch.from_numpy(bm["temp_draft"]).cuda())
+        na_dev = gv["num_accepted"]
+        off_dev = torch.from_numpy(bm["offsets"]).cuda()
+        torch.cuda.synchronize()
+        ctl_na, ctl_off = na_dev.cpu().numpy(), bm["offsets"]
+        Bc = int(na_dev.shape[0])
+        units = Bc
+        if wl == "telemetry":
+            acc = sv.telemetry_block()
+            alg_bytes = Bc * 8 + 156 * 8
+
+            def step(i, ev=None):
+                sv.telemetry_linear(na_dev, off_dev, acc)
+            unit = "batch rows/s"
+            metric = "round telemetry: batch rows/sec"
+        else:
+            hist = torch.zeros(Bc, dtype=torch.int32, device=dev)
+            alg_bytes = Bc * 24
+
+            def step(i, ev=None):
+                sv.gamma_update(hist, na_dev, off_dev)
+            unit = "requests/s"
+            metric = "dynamic gamma update: requests/sec"
+        config = dict(workload=wl, B=Bc, gamma="ragged 2/4/8 (bimodal batch)")
         flops = 0
     elif wl == "kv_commit":
         # The commit after a SAMPLED_WOR tree round: paths from the library's
@@ -551,7 +606,7 @@ def main():
     # HIP events attached to that kernel's dispatch on the call's stream.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    hooked = wl not in ("draft_topk", "tree_prune")
+    hooked = wl not in ("draft_topk", "tree_prune", "telemetry", "gamma_update")
     for i in range(args.steps):
         if hooked:
             step(args.warmup + i, evs[i])
@@ -602,6 +657,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_kv(kc, vc, L0, na, pa, N, args.cpu_seconds)
         elif wl == "draft_topk":
             out["cpu_baseline"] = cpu_baseline_topk(rows, kk, args.cpu_seconds)
+        elif wl in ("telemetry", "gamma_update"):
+            out["cpu_baseline"] = cpu_baseline_control(wl, ctl_na, ctl_off, args.cpu_seconds)
         elif wl == "tree_prune":
             out["cpu_baseline"] = cpu_baseline_prune(par, ctok.cpu().numpy(), clog.cpu().numpy(),
                                                      n_max, args.cpu_seconds)

@@ -10,8 +10,9 @@
 // depth of the deepest node for a tree; a tree path is hit when the round
 // accepted its first node below the root.
 //
-// Linear rows: one thread per row, counts gathered in LDS, one device-scope
-// atomic add per non-zero counter per work item.  Tree rows: one wave per
+// Linear rows: one thread per row; the counters every row adds to are summed
+// per wave first, the histogram bins counted in LDS; one device-scope atomic
+// add per non-zero counter per work item.  Tree rows: one wave per
 // tree, one lane per node.
 #include <hip/hip_runtime.h>
 
@@ -40,19 +41,29 @@ __global__ __launch_bounds__(256) void telemetry_linear_kernel(const int* num_ac
   for (int i = threadIdx.x; i < kTmCounters; i += 256) s_c[i] = 0u;
   __syncthreads();
   const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b < B) {
-    const int n = num_accepted[b];
-    const int g = off[b + 1] - off[b];
-    if (n < 0 || g < 0 || n > g) {
-      atomicAdd(&s_c[kTmErrors], 1u);
-    } else {
-      atomicAdd(&s_c[kTmRounds], 1u);
-      atomicAdd(&s_c[kTmDrafted], (uint32_t)g);
-      atomicAdd(&s_c[kTmAccepted], (uint32_t)n);
-      if (n == g) atomicAdd(&s_c[kTmFull], 1u);
-      if (g > 0) atomicAdd(&s_c[kTmRate + rate_bin(n, g)], 1u);
-      atomicAdd(&s_c[kTmPos + min(n, SV_TELEM_POS_BINS - 1)], 1u);
+  const int bc = b < B ? b : B - 1;   // clamped: every lane loads
+  const int n = num_accepted[bc];
+  const int g = off[bc + 1] - off[bc];
+  const bool err = b < B && (n < 0 || g < 0 || n > g);
+  const bool ok = b < B && !err;
+  // the counters every row adds to: a wave's total, one LDS atomic per wave
+  const unsigned long long m_ok = __ballot(ok), m_err = __ballot(err),
+                           m_full = __ballot(ok && n == g);
+  const uint32_t drafted = (uint32_t)wave_sum(ok ? (double)g : 0.0);
+  const uint32_t accepted = (uint32_t)wave_sum(ok ? (double)n : 0.0);
+  if ((threadIdx.x & 63) == 0) {
+    if (m_err) atomicAdd(&s_c[kTmErrors], (uint32_t)__popcll(m_err));
+    if (m_ok) {
+      atomicAdd(&s_c[kTmRounds], (uint32_t)__popcll(m_ok));
+      atomicAdd(&s_c[kTmDrafted], drafted);
+      atomicAdd(&s_c[kTmAccepted], accepted);
     }
+    if (m_full) atomicAdd(&s_c[kTmFull], (uint32_t)__popcll(m_full));
+  }
+  // histogram bins, spread over their addresses
+  if (ok) {
+    if (g > 0) atomicAdd(&s_c[kTmRate + rate_bin(n, g)], 1u);
+    atomicAdd(&s_c[kTmPos + min(n, SV_TELEM_POS_BINS - 1)], 1u);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kTmCounters; i += 256)
