@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--workload", default="linear_v32k",
                     choices=["linear_v1000", "linear_v32k", "linear_v128k", "bimodal_v152k",
                              "tree_v32k", "tree_wor_v32k", "attn_tree", "kv_commit",
-                             "draft_topk", "tree_prune", "telemetry", "gamma_update"])
+                             "draft_topk", "tree_prune", "telemetry", "telemetry_tree",
+                             "gamma_update"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying one HIP graph")
@@ -279,22 +280,26 @@ def cpu_baseline_prune(par, tok, logq, n_max, seconds):
 
 
 def cpu_baseline_control(wl, na, off, seconds):
-    """The oracle's telemetry counters or gamma update over the same rows until ~seconds."""
+    """The oracle's telemetry counters (linear rows or trees) or gamma update over
+    the same rows until ~seconds."""
     import oracle
     t0 = time.perf_counter()
     n = 0
-    gam = np.diff(off)
+    gam = np.diff(off) if wl == "gamma_update" else None
     hist = np.zeros(len(na), dtype=np.int64)
     while time.perf_counter() - t0 < seconds:
         if wl == "telemetry":
             oracle.telemetry.add_linear(oracle.telemetry.empty(), na, off)
+        elif wl == "telemetry_tree":
+            oracle.telemetry.add_tree(oracle.telemetry.empty(), na, off[0], off[1], None)
         else:
             hist, _, _ = oracle.control.gamma_update(hist, na, gam)
         n += len(na)
     dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="batch rows/s", cores=1, kind="oracle",
-                sample="%d batch rows (%d calls of %d) in %.1f s, single-threaded Python"
-                       % (n, n // len(na), len(na), dt))
+    unit = {"telemetry": "batch rows/s", "telemetry_tree": "trees/s"}.get(wl, "requests/s")
+    return dict(value=n / dt, unit=unit, cores=1, kind="oracle",
+                sample="%d %s (%d calls of %d) in %.1f s, single-threaded Python"
+                       % (n, unit[:-2], n // len(na), len(na), dt))
 
 
 def load_traffic(path, workload, kernel_sig):
@@ -319,6 +324,7 @@ def dominant_kernel(wl):
             "linear_v32k": "stats_kernel_by_chunk",
             "linear_v1000": "stats_kernel_by_chunk",
             "telemetry": "telemetry_linear_kernel",
+            "telemetry_tree": "telemetry_tree_kernel",
             "gamma_update": "gamma_update_kernel"}.get(wl, "stats_kernel")
 
 
@@ -329,6 +335,7 @@ def kernel_source_sig(wl):
     csrc = os.path.join(ROOT, "rejection_sampling_verify_04_amd", "csrc")
     own = {"attn_tree": "sv_attn.hip", "kv_commit": "sv_kv.hip", "draft_topk": "sv_draft.hip",
            "tree_prune": "sv_draft.hip", "telemetry": "sv_telemetry.hip",
+           "telemetry_tree": "sv_telemetry.hip",
            "gamma_update": "sv_control.hip"}.get(wl, "sv_stats.hip")
     names = [own, "sv_common.h", "sv_internal.h"]
     h = hashlib.sha1()
@@ -437,6 +444,29 @@ def main():
             unit = "requests/s"
             metric = "dynamic gamma update: requests/sec"
         config = dict(workload=wl, B=Bc, gamma="ragged 2/4/8 (bimodal batch)")
+        flops = 0
+    elif wl == "telemetry_tree":
+        # The counters after a TOPK round of the tree_v32k trees (B=64, 64
+        # nodes each): outcomes from the library's own verify of them.
+        tr = synth.tree_v32k()
+        par_dev = torch.from_numpy(tr["parents"]).cuda()
+        gv = sv.verify_tree(to_dev_logits(torch, tr["target"], 1), par_dev,
+                            torch.from_numpy(tr["tokens"]).cuda(),
+                            torch.from_numpy(tr["temp_target"]).cuda())
+        na_dev, path_dev = gv["num_accepted"], gv["path_nodes"]
+        torch.cuda.synchronize()
+        Bc, Nt = tr["parents"].shape
+        ctl_na = na_dev.cpu().numpy()
+        ctl_off = (path_dev.cpu().numpy(), tr["parents"])
+        units = Bc
+        acc = sv.telemetry_block()
+        alg_bytes = Bc * 4 + Bc * (Nt - 1) * 4 + Bc * Nt * 4 + 156 * 8
+
+        def step(i, ev=None):
+            sv.telemetry_tree(na_dev, path_dev, par_dev, acc)
+        unit = "trees/s"
+        metric = "round telemetry: trees/sec"
+        config = dict(workload=wl, B=Bc, nodes=Nt, trees="tree_v32k, TOPK walk")
         flops = 0
     elif wl == "kv_commit":
         # The commit after a SAMPLED_WOR tree round: paths from the library's
@@ -606,7 +636,8 @@ def main():
     # HIP events attached to that kernel's dispatch on the call's stream.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    hooked = wl not in ("draft_topk", "tree_prune", "telemetry", "gamma_update")
+    hooked = wl not in ("draft_topk", "tree_prune", "telemetry", "telemetry_tree",
+                        "gamma_update")
     for i in range(args.steps):
         if hooked:
             step(args.warmup + i, evs[i])
@@ -657,7 +688,7 @@ def main():
             out["cpu_baseline"] = cpu_baseline_kv(kc, vc, L0, na, pa, N, args.cpu_seconds)
         elif wl == "draft_topk":
             out["cpu_baseline"] = cpu_baseline_topk(rows, kk, args.cpu_seconds)
-        elif wl in ("telemetry", "gamma_update"):
+        elif wl in ("telemetry", "telemetry_tree", "gamma_update"):
             out["cpu_baseline"] = cpu_baseline_control(wl, ctl_na, ctl_off, args.cpu_seconds)
         elif wl == "tree_prune":
             out["cpu_baseline"] = cpu_baseline_prune(par, ctok.cpu().numpy(), clog.cpu().numpy(),

@@ -12,8 +12,7 @@
 //
 // Linear rows: one thread per row; the counters every row adds to are summed
 // per wave first, the histogram bins counted in LDS; one device-scope atomic
-// add per non-zero counter per work item.  Tree rows: one wave per
-// tree, one lane per node.
+// add per non-zero counter per work item.
 #include <hip/hip_runtime.h>
 
 #include "spec_verify.h"
@@ -70,70 +69,86 @@ __global__ __launch_bounds__(256) void telemetry_linear_kernel(const int* num_ac
     if (s_c[i]) atomicAdd(&acc[i], (unsigned long long)s_c[i]);
 }
 
-__global__ __launch_bounds__(64) void telemetry_tree_kernel(const int* num_accepted,
-                                                            const int* path, const int* parents,
-                                                            const int* n_nodes, int N,
-                                                            unsigned long long* acc) {
-  __shared__ int s_par[kMaxNodes], s_depth[kMaxNodes];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const int nn = n_nodes ? n_nodes[b] : N;
-  const int n = num_accepted[b];
+// Tree rows: one wave per tree, one lane per node, kTmTreeWaves trees per
+// block.  Depth and the depth-1 ancestor come from pointer jumping over the
+// lanes (six doublings cover 63 levels), the inner-node mask from a wave OR,
+// sibling ranks from one ballot per inner node; a tree's counters go to the
+// block's LDS copy, which adds to the device block once per non-zero counter.
+constexpr int kTmTreeWaves = 4;
+
+__global__ __launch_bounds__(64 * kTmTreeWaves) void telemetry_tree_kernel(
+    const int* num_accepted, const int* path, const int* parents, const int* n_nodes, int B,
+    int N, unsigned long long* acc) {
+  __shared__ uint32_t s_c[kTmCounters];
+  for (int i = threadIdx.x; i < kTmCounters; i += 64 * kTmTreeWaves) s_c[i] = 0u;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kTmTreeWaves + (threadIdx.x >> 6);
+  const bool live = b < B;             // wave-uniform
+  const int bc = live ? b : B - 1;     // clamped: every wave loads in bounds
+  // every load at once, each index clamped into its row
+  const int nn = n_nodes ? n_nodes[bc] : N;
+  const int n = num_accepted[bc];
+  const int par_ld = parents[(long long)bc * N + min(lane, N - 1)];
+  const int pj_ld = N > 1 ? path[(long long)bc * (N - 1) + min(lane, N - 2)] : 0;
   const bool node = lane < nn && lane < N;
-  int par = -1;
-  if (node && lane > 0) par = parents[(long long)b * N + lane];
+  const int par = node && lane > 0 ? par_ld : -1;
   const bool shape_ok = nn >= 1 && nn <= N && n >= 0 && n < nn;
   const bool bad_par = node && lane > 0 && (par < 0 || par >= lane);
-  int pj = 0;   // this lane's accepted node (lane < n)
-  if (lane < n && lane < N - 1 && shape_ok) pj = path[(long long)b * (N - 1) + lane];
-  const bool bad_path = lane < n && shape_ok && (pj < 1 || pj >= nn);
-  if (!shape_ok || __ballot(bad_par) || __ballot(bad_path)) {
-    if (lane == 0) atomicAdd(&acc[kTmErrors], 1ull);
-    return;
+  const bool bad_path = lane < n && shape_ok && (pj_ld < 1 || pj_ld >= nn);
+  const bool ok = live && shape_ok && !__ballot(bad_par) && !__ballot(bad_path);
+  const bool child = ok && node && lane > 0;   // a node below the root of a valid tree
+  const int p0 = child ? par : 0;
+  const int pj = ok && lane < n ? pj_ld : 0;   // this lane's accepted node (lane < n)
+  // depth: (a, d) = an ancestor and the distance to it; the root is its own, at 0
+  int a = p0, d = child ? 1 : 0;
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    d += __shfl(d, a);
+    a = __shfl(a, a);
   }
-  s_par[lane] = node ? par : -1;
-  __syncthreads();
-  // depth: walk up the ancestors (parents precede children)
-  int depth = 0;
-  if (node) {
-    for (int x = lane; x > 0; x = s_par[x]) ++depth;
-  }
-  s_depth[lane] = node ? depth : 0;
-  const unsigned long long inner = [&] {
-    unsigned long long m = 0ull;
-    for (int c = 1; c < nn; ++c) m |= 1ull << s_par[c];
-    return m;
-  }();
-  __syncthreads();
+  const int depth = d;
+  // the depth-1 ancestor of every node (nodes at depth <= 1 are their own)
+  int top = depth <= 1 ? lane : p0;
+#pragma unroll
+  for (int s = 0; s < 6; ++s) top = __shfl(top, top);
+  const unsigned long long inner = wave_or_u64(child ? 1ull << p0 : 0ull);
   // rank among the siblings (test order = node index)
   int rank = 0;
-  if (node && lane > 0)
-    for (int y = 1; y < lane; ++y) rank += s_par[y] == par;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (unsigned long long m = inner; m; m &= m - 1ull) {
+    const int p = __builtin_ctzll(m);
+    const unsigned long long sib = __ballot(child && p0 == p);
+    if (child && p0 == p) rank = __popcll(sib & below);
+  }
   int g = depth;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) g = max(g, __shfl_xor(g, o));
-  const bool leaf = node && !((inner >> lane) & 1ull);
+  const bool leaf = ok && node && !((inner >> lane) & 1ull);
   const int first = __shfl(pj, 0);
-  bool hit = false;
-  if (leaf && n > 0) {
-    int x = lane;
-    while (x > 0 && s_depth[x] > 1) x = s_par[x];
-    hit = x == first;
-  }
+  const bool hit = leaf && n > 0 && top == first;
   const int n_leaves = __popcll(__ballot(leaf));
   const int n_hit = __popcll(__ballot(hit));
   const int last = n > 0 ? __shfl(pj, n - 1) : 0;
   const int rank_acc = __shfl(rank, pj);   // rank of this lane's accepted node
-  if (lane < n) atomicAdd(&acc[kTmRank + min(rank_acc, SV_TELEM_RANK_BINS - 1)], 1ull);
-  if (lane == 0) {
-    atomicAdd(&acc[kTmRounds], 1ull);
-    atomicAdd(&acc[kTmDrafted], (unsigned long long)g);
-    atomicAdd(&acc[kTmAccepted], (unsigned long long)n);
-    if (!((inner >> last) & 1ull)) atomicAdd(&acc[kTmFull], 1ull);
-    if (g > 0) atomicAdd(&acc[kTmRate + rate_bin(n, g)], 1ull);
-    atomicAdd(&acc[kTmPos + min(n, SV_TELEM_POS_BINS - 1)], 1ull);
-    atomicAdd(&acc[kTmPaths], (unsigned long long)n_leaves);
-    atomicAdd(&acc[kTmPathsHit], (unsigned long long)n_hit);
+  __syncthreads();   // s_c cleared
+  if (ok && lane < n) atomicAdd(&s_c[kTmRank + min(rank_acc, SV_TELEM_RANK_BINS - 1)], 1u);
+  if (lane == 0 && live) {
+    if (!ok) {
+      atomicAdd(&s_c[kTmErrors], 1u);
+    } else {
+      atomicAdd(&s_c[kTmRounds], 1u);
+      atomicAdd(&s_c[kTmDrafted], (uint32_t)g);
+      atomicAdd(&s_c[kTmAccepted], (uint32_t)n);
+      if (!((inner >> last) & 1ull)) atomicAdd(&s_c[kTmFull], 1u);
+      if (g > 0) atomicAdd(&s_c[kTmRate + rate_bin(n, g)], 1u);
+      atomicAdd(&s_c[kTmPos + min(n, SV_TELEM_POS_BINS - 1)], 1u);
+      atomicAdd(&s_c[kTmPaths], (uint32_t)n_leaves);
+      atomicAdd(&s_c[kTmPathsHit], (uint32_t)n_hit);
+    }
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTmCounters; i += 64 * kTmTreeWaves)
+    if (s_c[i]) atomicAdd(&acc[i], (unsigned long long)s_c[i]);
 }
 
 // The derived signals of a window (one thread): acceptance rate, average
@@ -184,9 +199,9 @@ hipError_t launch_telemetry_linear(const int* num_accepted, const int* off, int 
 hipError_t launch_telemetry_tree(const int* num_accepted, const int* path, const int* parents,
                                  const int* n_nodes, int B, int N, sv_telemetry* acc,
                                  hipStream_t st) {
-  telemetry_tree_kernel<<<dim3((unsigned)B), dim3(64), 0, st>>>(num_accepted, path, parents,
-                                                              n_nodes, N,
-                                                              (unsigned long long*)acc);
+  telemetry_tree_kernel<<<dim3((unsigned)((B + kTmTreeWaves - 1) / kTmTreeWaves)),
+                          dim3(64 * kTmTreeWaves), 0, st>>>(num_accepted, path, parents, n_nodes,
+                                                            B, N, (unsigned long long*)acc);
   return hipGetLastError();
 }
 

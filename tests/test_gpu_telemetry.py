@@ -85,3 +85,24 @@ def test_bimodal_full_size():
     h = np.array(sv.telemetry_fields(acc)["acc_rate_hist"])
     say("[telemetry] bimodal acceptance histogram (5%% bins): %s" % h.tolist())
     assert h[:6].sum() > h[6:10].sum() and h[10:].sum() > h[6:10].sum()
+
+
+def test_tree_full_width_ragged_batch():
+    """64-node trees (every lane of a wave a node), a batch that leaves the last
+    block of four trees part-filled, error rows mixed in, then the full-size
+    tree workload (B=64, N=64, V=32000 bf16) in the same window."""
+    import rejection_sampling_verify_04_amd as sv
+    acc = sv.telemetry_block()
+    t = TM.empty()
+    d = synth.tree_v32k(seed=91, B=37, V=2000)
+    g = run_tree(d)
+    n = g["num_accepted"].copy()
+    n[::5] = -1
+    sv.telemetry_tree(i32(n), i32(g["path_nodes"]), i32(d["parents"]), acc)
+    TM.add_tree(t, n, g["path_nodes"], d["parents"], None)
+    d = synth.tree_v32k()
+    g = run_tree(d)
+    sv.telemetry_tree(i32(g["num_accepted"]), i32(g["path_nodes"]), i32(d["parents"]), acc)
+    TM.add_tree(t, g["num_accepted"], g["path_nodes"], d["parents"], None)
+    assert t["error_rows"] == 8 and t["rounds"] == 64 + 29
+    compare(acc, t, "64-node trees, B=37 with error rows, then B=64")
