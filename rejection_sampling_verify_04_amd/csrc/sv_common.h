@@ -233,6 +233,20 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* scratch
 }
 
 // A value that is the same in every lane, kept in scalar registers.
+// A 32-bit input word that every thread of the work item reads at the same
+// address, read as a scalar load (constant address space): its wait does not
+// also wait for the vector loads issued before it.  Only for inputs that no
+// kernel of the launch writes.
+__device__ __forceinline__ uint32_t load_uniform_u32(const void* p) {
+  return *(const __attribute__((address_space(4))) uint32_t*)p;
+}
+__device__ __forceinline__ int load_uniform_i32(const int* p) {
+  return (int)load_uniform_u32(p);
+}
+__device__ __forceinline__ float load_uniform_f32(const float* p) {
+  return __uint_as_float(load_uniform_u32(p));
+}
+
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ float uni(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));

@@ -83,6 +83,12 @@ __device__ LinRecord linear_decide(const LinearArgs& a, int b, bool write_output
   auto row_of = [&](int rr) -> long long {
     return rr <= g ? tr0 + rr : a.n_target_rows + o0 + (rr - g - 1);
   };
+  // the draft tokens and the logits at them (gathered by the vocabulary pass)
+  // (no branch around them, so that nothing waits for them before their use)
+  const int li = min(lane, g > 0 ? g - 1 : 0);
+  const int tok = *(g > 0 ? a.tokens + o0 + li : a.off);
+  const float x = *(g > 0 ? a.gath + o0 + li : (const float*)a.off);
+  const float y = *(g > 0 ? a.gath + a.total_draft + o0 + li : (const float*)a.off);
   // rows wave + 4 k (k < kDecideRowsPerWave), clamped into [0, nr): loaded
   // and merged unconditionally
   Partial q[kDecideRowsPerWave];
@@ -91,13 +97,8 @@ __device__ LinRecord linear_decide(const LinearArgs& a, int b, bool write_output
     q[k] = lane_partial(a.part + row_of(min(wave + k * kFinWaves, nr - 1)) * n_parts, n_parts);
   // lane l's Philox block of slot l, formed while the loads are in flight
   // (wave 0 uses it: word 0 tests d_{l-1}, word 1 is the draw at stop l)
-  const uint32_t rid = a.row_ids ? a.row_ids[b] : (uint32_t)b;
+  const uint32_t rid = a.row_ids ? load_uniform_u32(a.row_ids + b) : (uint32_t)b;
   const uint4 wl = verify_words(a.seed, a.step, rid, (uint32_t)lane);
-  // the draft tokens and the logits at them (gathered by the vocabulary pass)
-  const int li = min(lane, g > 0 ? g - 1 : 0);
-  const int tok = *(g > 0 ? a.tokens + o0 + li : a.off);
-  const float x = g > 0 ? a.gath[o0 + li] : 0.0f;
-  const float y = g > 0 ? a.gath[a.total_draft + o0 + li] : 0.0f;
 #pragma unroll
   for (int k = 0; k < kDecideRowsPerWave; ++k) {
     const int rr = min(wave + k * kFinWaves, nr - 1);
@@ -407,13 +408,16 @@ __global__ __launch_bounds__(64) void linear_select_kernel(LinearArgs a) {
     wv[k] = wsb[i < nws ? i : 0];
   }
   const LinRecord r = a.rec[b];
+  // the record and the wave totals are in flight together: the record is
+  // waited for here (its kind, as a scalar), the totals by their LDS stores
+  asm volatile("" ::"s"(r.kind));
+#pragma unroll
+  for (int k = 0; k < kPerLaneWs; ++k)
+    if (lane + 64 * k < nws) s_ws[lane + 64 * k] = wv[k];
+  __syncthreads();
   int warn = 0;
   if (r.kind == kKindReject || r.kind == kKindBonus) {
     StopDist d = record_dist<DT>(a, b, r);
-#pragma unroll
-    for (int k = 0; k < kPerLaneWs; ++k)
-      if (lane + 64 * k < nws) s_ws[lane + 64 * k] = wv[k];
-    __syncthreads();
     auto chunk_masses = [&]() -> double {
       double m = 0.0;
       if (lane < nc) {
