@@ -94,7 +94,8 @@ __device__ __forceinline__ void seg_load_scalar(const char* rowp, int V, int seg
 #pragma unroll
     for (int k = 0; k < EPV; ++k) {
       const int e = seg0 + (j * 64 + lane) * EPV + k;
-      v[j * EPV + k] = e < V ? load_logit<DT>(rowp, e) : -__builtin_huge_valf();
+      const float x = load_logit<DT>(rowp, e < V ? e : V - 1);   // clamped: no branch
+      v[j * EPV + k] = e < V ? x : -__builtin_huge_valf();
     }
   }
 }

@@ -355,11 +355,13 @@ __device__ __forceinline__ void wor_weights(const WorDist& d, int V, int chunk,
       }
     }
   } else {
+    // indices clamped into the row: every load is issued, none behind a branch
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const int idx = e0 + e;
-      xp[e] = idx < V ? load_logit<DT>(d.xrow, idx) : 0.0f;
-      xq[e] = idx < V ? load_logit<DT>(d.yrow, idx) : 0.0f;
+      const int idx = e0 + e, ic = idx < V ? idx : V - 1;
+      const float p = load_logit<DT>(d.xrow, ic), q = load_logit<DT>(d.yrow, ic);
+      xp[e] = idx < V ? p : 0.0f;
+      xq[e] = idx < V ? q : 0.0f;
     }
   }
   float lv[kPerThread];
