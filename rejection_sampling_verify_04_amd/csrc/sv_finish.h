@@ -258,14 +258,11 @@ __device__ __forceinline__ void stop_weights_from(const StopDist& d, int V, int 
       }
     }
   } else {
-    // indices clamped into the row: every load is issued, none behind a branch
-    const void* qsrc = need_q ? d.qrow : d.prow;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const int idx = e0 + e, ic = idx < V ? idx : V - 1;
-      const float p = load_logit<DT>(d.prow, ic), q = load_logit<DT>(qsrc, ic);
-      xp[e] = idx < V ? p : 0.0f;
-      xq[e] = (need_q && idx < V) ? q : 0.0f;
+      const int idx = e0 + e;
+      xp[e] = idx < V ? load_logit<DT>(d.prow, idx) : 0.0f;
+      xq[e] = (need_q && idx < V) ? load_logit<DT>(d.qrow, idx) : 0.0f;
     }
   }
   // per-element range and mask tests only where they can matter

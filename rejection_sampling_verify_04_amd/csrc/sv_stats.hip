@@ -94,8 +94,7 @@ __device__ __forceinline__ void seg_load_scalar(const char* rowp, int V, int seg
 #pragma unroll
     for (int k = 0; k < EPV; ++k) {
       const int e = seg0 + (j * 64 + lane) * EPV + k;
-      const float x = load_logit<DT>(rowp, e < V ? e : V - 1);   // clamped: no branch
-      v[j * EPV + k] = e < V ? x : -__builtin_huge_valf();
+      v[j * EPV + k] = e < V ? load_logit<DT>(rowp, e) : -__builtin_huge_valf();
     }
   }
 }
