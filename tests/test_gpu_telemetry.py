@@ -106,3 +106,32 @@ def test_tree_full_width_ragged_batch():
     TM.add_tree(t, g["num_accepted"], g["path_nodes"], d["parents"], None)
     assert t["error_rows"] == 8 and t["rounds"] == 64 + 29
     compare(acc, t, "64-node trees, B=37 with error rows, then B=64")
+
+
+def test_tree_degenerate_shapes():
+    """Root-only trees (N=1: no path, every tree a full accept of zero tokens),
+    two-node trees, and a batch of one tree, in one window."""
+    import rejection_sampling_verify_04_amd as sv
+    torch = torch_mod()
+    acc = sv.telemetry_block()
+    t = TM.empty()
+    # N = 1: the path array is empty
+    par1 = np.full((5, 1), -1, dtype=np.int32)
+    n1 = np.zeros(5, dtype=np.int32)
+    sv.telemetry_tree(i32(n1), torch.zeros((5, 0), dtype=torch.int32, device="cuda"), i32(par1), acc)
+    TM.add_tree(t, n1, np.zeros((5, 0), dtype=np.int32), par1, None)
+    # N = 2: a root and one child, accepted or not, one error row
+    par2 = np.array([[-1, 0]] * 6, dtype=np.int32)
+    n2 = np.array([0, 1, 1, 0, -1, 1], dtype=np.int32)
+    path2 = np.array([[1 if k > 0 else -1] for k in n2], dtype=np.int32)
+    sv.telemetry_tree(i32(n2), i32(path2), i32(par2), acc)
+    TM.add_tree(t, n2, path2, par2, None)
+    # one tree of 64 nodes, a chain accepted to depth 3
+    par3 = np.array([[-1] + list(range(63))], dtype=np.int32)
+    n3 = np.array([3], dtype=np.int32)
+    path3 = np.full((1, 63), -1, dtype=np.int32)
+    path3[0, :3] = [1, 2, 3]
+    sv.telemetry_tree(i32(n3), i32(path3), i32(par3), acc)
+    TM.add_tree(t, n3, path3, par3, None)
+    assert t["rounds"] == 11 and t["error_rows"] == 1 and t["tree_paths_hit"] == 4
+    compare(acc, t, "root-only, two-node and single-chain trees")
