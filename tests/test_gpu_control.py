@@ -199,3 +199,45 @@ def test_tree_prune_matches_oracle():
     bad[2, 10] = 50                     # a parent after its child
     out = sv.tree_prune(i32(bad), i32(tok), f32(lq), 64)
     assert out["n_nodes"].cpu().numpy()[2] == 0
+
+
+def test_drafting_full_size_sampled():
+    """The drafting workloads at their full size and launch shape: top-4 of
+    1024 draft rows over V=32000 bf16 (every 32nd row checked), then the
+    pruning of 64 full 4-wide, 4-deep forests (340 candidates, log q from the
+    library's own top-4 of random rows) to 64 nodes (every tree checked)."""
+    import rejection_sampling_verify_04_amd as sv
+    torch = torch_mod()
+    rng = np.random.default_rng(11)
+    R, V, k = 1024, 32000, 4
+    bits = synth.bf16_bits(rng.standard_normal((R, V), dtype=np.float32) * np.float32(2.0))
+    tok, lp = sv.draft_topk(logits_to_dev(bits, 1), k)
+    tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
+    vals = synth.bf16_values(bits[::32]).astype(np.float64)
+    for i, r in enumerate(range(0, R, 32)):
+        rt, rl = OD.topk_candidates(vals[i], k, 1.0)
+        assert np.array_equal(tok[r], rt), (r, tok[r], rt)
+        assert np.all(np.abs(lp[r] - rl) <= 1e-5 * np.maximum(1.0, np.abs(rl))), r
+    say("[control] draft top-k full size: 32 of 1024 rows checked")
+    Bp, C, n_max = 64, 340, 64
+    par = np.zeros((Bp, C), dtype=np.int32)
+    lvl = [list(range(0, 4)), list(range(4, 20)), list(range(20, 84)), list(range(84, 340))]
+    for d in range(4):
+        for j, c in enumerate(lvl[d]):
+            par[:, c] = -1 if d == 0 else lvl[d - 1][j // 4]
+    cl = torch.from_numpy(rng.standard_normal((Bp * 85, V // 8), dtype=np.float32)).cuda()
+    ct, clq = sv.draft_topk(cl, 4)
+    ctok = ct.reshape(Bp, C).contiguous()
+    clog = clq.reshape(Bp, C).contiguous()
+    out = sv.tree_prune(i32(par), ctok, clog, n_max, tau=0.1)
+    got = {kk: v.cpu().numpy() for kk, v in out.items()}
+    tk, lq = ctok.cpu().numpy(), clog.cpu().numpy()
+    for b in range(Bp):
+        rp, rtk, rc, rpass = OD.prune_tree(par[b], tk[b], lq[b].astype(np.float64), n_max, 0.1)
+        n = len(rp)
+        assert got["n_nodes"][b] == n == n_max
+        assert np.array_equal(got["parents"][b, :n], rp), b
+        assert np.array_equal(got["tokens"][b, :n], rtk), b
+        assert np.array_equal(got["cum_logprob"][b, :n], rc.astype(np.float32)), b
+        assert got["n_pass"][b] == rpass, b
+    say("[control] tree prune full size: 64 forests of 340 candidates -> 64 nodes")
