@@ -50,9 +50,18 @@ __global__ __launch_bounds__(kFinThreads) void gamma_update_kernel(uint32_t* his
     const int b = b0 + threadIdx.x;
     int g_new = 0;
     if (b < B) {
-      const uint32_t w = history_push(history[b], num_accepted[b], off[b + 1] - off[b]);
+      // every load issued together, none behind a branch: the temperature
+      // from a valid address whether or not it is used, and the offsets
+      // held in registers (the asm) before the push, which uses them only
+      // for a valid count
+      const float tb = *(temp ? temp + b : (const float*)(num_accepted + b));
+      const uint32_t h = history[b];
+      const int n = num_accepted[b];
+      const int o0 = off[b], o1 = off[b + 1];
+      asm volatile("" ::"v"(o0), "v"(o1));
+      const uint32_t w = history_push(h, n, o1 - o0);
       history[b] = w;
-      g_new = (couple && temp && temp[b] > 0.8f) ? 1 : gamma_from(w);
+      g_new = (couple && temp && tb > 0.8f) ? 1 : gamma_from(w);
       gamma_next[b] = g_new;
     }
     double total;
