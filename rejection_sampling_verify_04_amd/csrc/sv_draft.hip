@@ -118,6 +118,9 @@ void draft_topk_kernel(const void* logits, int V, int k, const float* temp, int*
       okv[j] = vj * EPV < V;
       raw[j] = __builtin_nontemporal_load((const u32x4_t*)(row + (long long)(okv[j] ? vj : 0) * 16));
     }
+    // keep the unpacking below the last load: otherwise the scheduler starts
+    // unpacking the first vector, and waits for it, before the others go out
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kTopkRegVecs; ++j) {
       const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
