@@ -122,6 +122,19 @@ __device__ __forceinline__ int wave_find_batch_row(const int* off, int B, long l
   return lo;
 }
 
+// As wave_find_batch_row for a uniform x, by a binary search of scalar loads
+// (offsets non-decreasing): the loads are waited for on the scalar counter,
+// so vector loads issued before them are not waited for with them.
+__device__ __forceinline__ int scalar_find_batch_row(const int* off, int B, long long x, int add) {
+  int lo = 0, hi = B;   // off[lo] + add lo <= x; keys at hi and above exceed x
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((long long)load_uniform_i32(off + mid) + (long long)add * mid <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Largest b in [0, B) with off[b] <= i, each lane for its own i (fixed
 // number of steps: ceil(log2(B))).
 __device__ __forceinline__ int lane_batch_row(const int* off, int B, long long i) {
@@ -538,9 +551,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel_by_chunk(StatsArgs a) {
   const int seg0 = (int)c * kChunk + wave * kSubSpan;
   SegLoad<DT> seg;
   if (a.vec_ok) seg.issue(rowp, V, seg0);
-  // the row's temperature, its batch row found from the offsets
-  const float T = r < a.n_a ? a.temp_a[wave_find_batch_row(a.offsets, a.B, (long long)r, 1)]
-                            : a.temp_b[wave_find_batch_row(a.offsets, a.B, (long long)r - a.n_a, 0)];
+  // the row's temperature, its batch row found from the offsets (scalar
+  // loads, done while the row's loads are in flight)
+  const bool is_t = r < a.n_a;
+  const int bb = is_t ? scalar_find_batch_row(a.offsets, a.B, (long long)r, 1)
+                      : scalar_find_batch_row(a.offsets, a.B, (long long)r - a.n_a, 0);
+  const float T = load_uniform_f32((is_t ? a.temp_a : a.temp_b) + bb);
   const bool ok = temp_ok(T);   // a bad temperature is reported by the finish pass
   const bool greedy = T == 0.0f;
   const float k2 = greedy ? 0.0f : log2e_over_t(T);
