@@ -384,14 +384,15 @@ int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_i
                              int n_rows, int n_slots, uint32_t* out_words, hipStream_t stream);
 
 /*
- * Diagnostic timing hook (for benchmarks): the next spec_verify_linear,
- * spec_verify_tree, spec_verify_attn or spec_verify_kv_commit call attaches
- * `begin` and `end` to the dispatch of its dominant kernel (the vocabulary
- * pass, the attention kernel or the commit kernel), so the events bracket
- * that kernel alone, as a profiler sees it;
- * then the hook forgets both.  Either may be NULL to clear the hook.  Not
- * for use under stream capture.  Process-wide and not thread-safe; it
- * changes no output and skips no work.
+ * Diagnostic timing hook (for benchmarks): the calling thread's next
+ * spec_verify_linear, spec_verify_tree, spec_verify_attn or
+ * spec_verify_kv_commit call attaches `begin` and `end` to the dispatch of
+ * its dominant kernel (the vocabulary pass, the attention kernel or the
+ * commit kernel), so the events bracket that kernel alone, as a profiler
+ * sees it; then the hook forgets both.  Either may be NULL to clear the
+ * hook.  The hook is per host thread: a call made on another thread neither
+ * sees nor consumes it, so the entry points stay reentrant and thread-safe.
+ * Not for use under stream capture.  It changes no output and skips no work.
  */
 int spec_verify_profile_next(hipEvent_t begin, hipEvent_t end);
 

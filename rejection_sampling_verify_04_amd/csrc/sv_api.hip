@@ -10,7 +10,8 @@ constexpr size_t kAlign = SV_WORKSPACE_ALIGN;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int n_chunks_for(int V) { return (V + sv::kChunk - 1) / sv::kChunk; }
+// Chunks of a row of V elements (in 64 bits: V may be near INT_MAX).
+int n_chunks_for(int V) { return (int)(((long long)V + sv::kChunk - 1) / sv::kChunk); }
 
 // Workspace: [partials | gathered logits | chunk wave totals | per-row
 // decision records], each aligned.  n_gath = logits gathered at draft tokens.
@@ -32,13 +33,22 @@ Layout layout(long long n_rows, int B, int V, long long n_gath, bool linear) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// One-shot timing hook (spec_verify_profile_next).
-hipEvent_t g_prof_begin = nullptr, g_prof_end = nullptr;
+// One-shot timing hook (spec_verify_profile_next), one per host thread: an
+// armed pair is seen and consumed only by calls on the thread that armed it.
+struct ProfHook {
+  hipEvent_t begin, end;
+};
+thread_local ProfHook t_prof = {nullptr, nullptr};
+
+ProfHook take_prof_hook() {
+  const ProfHook h = t_prof;
+  t_prof = ProfHook{nullptr, nullptr};
+  return h;
+}
 
 hipError_t launch_stats_timed(int dtype, const sv::StatsArgs& s, hipStream_t stream) {
-  hipEvent_t b = g_prof_begin, e = g_prof_end;
-  g_prof_begin = g_prof_end = nullptr;
-  return sv::launch_stats(dtype, s, stream, b, e);
+  const ProfHook h = take_prof_hook();
+  return sv::launch_stats(dtype, s, stream, h.begin, h.end);
 }
 
 int check_workspace(void* ws, size_t bytes, size_t need) {
@@ -261,9 +271,8 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
   a.scale_log2 = (float)((double)scale * sv::kLog2e);
   a.out = (uint16_t*)out;
   a.lse = lse;
-  hipEvent_t b = g_prof_begin, e = g_prof_end;
-  g_prof_begin = g_prof_end = nullptr;
-  if (sv::launch_attn(a, stream, b, e) != hipSuccess) return SV_ERR_HIP;
+  const ProfHook h = take_prof_hook();
+  if (sv::launch_attn(a, stream, h.begin, h.end) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 
@@ -277,8 +286,15 @@ int spec_verify_kv_commit(void* k_cache, void* v_cache, int layers, long long la
   if (B == 0) return SV_OK;
   if (!k_cache || !v_cache || !prefix_len || !num_accepted || !new_len) return SV_ERR_INVALID_ARG;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return SV_ERR_INVALID_ARG;
-  const long long per_layer = (long long)B * H * S_max * d;
+  // elements per layer and of the whole cache must fit a signed 64-bit index
+  const long long kIdxMax = 1LL << 62;
+  long long per_layer = 1;
+  for (long long f : {(long long)B, (long long)H, (long long)S_max, (long long)d}) {
+    if (per_layer > kIdxMax / f) return SV_ERR_INVALID_ARG;
+    per_layer *= f;
+  }
   if (layers > 1 && (layer_stride < per_layer || layer_stride % 8 != 0)) return SV_ERR_INVALID_ARG;
+  if (layers > 1 && layer_stride > (kIdxMax - per_layer) / (layers - 1)) return SV_ERR_INVALID_ARG;
   if (path_nodes && path_stride < N - 1) return SV_ERR_INVALID_ARG;
   if ((long long)layers * B >= (1LL << 31)) return SV_ERR_INVALID_ARG;
   sv::KvArgs a{};
@@ -296,9 +312,8 @@ int spec_verify_kv_commit(void* k_cache, void* v_cache, int layers, long long la
   a.d = d;
   a.n_new = N;
   a.new_len = new_len;
-  hipEvent_t eb = g_prof_begin, ee = g_prof_end;
-  g_prof_begin = g_prof_end = nullptr;
-  if (sv::launch_kv_commit(a, stream, eb, ee) != hipSuccess) return SV_ERR_HIP;
+  const ProfHook h = take_prof_hook();
+  if (sv::launch_kv_commit(a, stream, h.begin, h.end) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 
@@ -400,8 +415,7 @@ int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_i
 }
 
 int spec_verify_profile_next(hipEvent_t begin, hipEvent_t end) {
-  g_prof_begin = begin;
-  g_prof_end = end;
+  t_prof = ProfHook{begin, end};
   return SV_OK;
 }
 

@@ -17,12 +17,16 @@
 
 namespace sv {
 
+// Only the newest 16 outcomes survive a push, so at most 16 are shifted in:
+// the last min(steps, 16) of n ones followed (after a rejection) by a zero.
+// The loop is bounded whatever num_accepted holds.
 __device__ __forceinline__ uint32_t history_push(uint32_t w, int n, int g) {
   if (n < 0) return w;
   uint32_t hist = w & 0xFFFFu, count = (w >> 16) & 0x1Fu;
-  const int steps = n + (n < g ? 1 : 0);
-  for (int s = 0; s < steps; ++s) {
-    hist = ((hist << 1) | (s < n ? 1u : 0u)) & 0xFFFFu;
+  const int z = n < g ? 1 : 0;
+  const int k = n >= 16 ? 16 : min(n + z, 16);
+  for (int s = 0; s < k; ++s) {
+    hist = ((hist << 1) | (s < k - z ? 1u : 0u)) & 0xFFFFu;
     count = min(count + 1u, 16u);
   }
   return hist | (count << 16);

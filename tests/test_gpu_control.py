@@ -45,6 +45,32 @@ def test_gamma_update_matches_oracle():
     say("[control] gamma update: B=%d ok, gamma histogram %s" % (B, np.bincount(g_ref).tolist()))
 
 
+def test_gamma_update_long_rounds():
+    """Counts of 15..40 and a huge count: only the newest 16 outcomes are kept."""
+    import rejection_sampling_verify_04_amd as sv
+    torch = torch_mod()
+    rng = np.random.default_rng(101)
+    B = 300
+    count = rng.integers(0, 17, size=B)
+    hist = (rng.integers(0, 1 << 16, size=B) & ((1 << count) - 1)) | (count << 16)
+    g = rng.integers(14, 42, size=B)
+    n = np.array([rng.integers(13, gi + 1) for gi in g], dtype=np.int32)
+    off = np.concatenate([[0], np.cumsum(g)]).astype(np.int32)
+    h_dev = torch.from_numpy(hist.astype(np.int32)).cuda()
+    gn, on = sv.gamma_update(h_dev, i32(n), i32(off))
+    h_ref, g_ref, o_ref = OC.gamma_update(hist, n, g)
+    assert np.array_equal(h_dev.cpu().numpy(), h_ref)
+    assert np.array_equal(gn.cpu().numpy(), g_ref)
+    assert np.array_equal(on.cpu().numpy(), o_ref)
+    # a count of 2^31 - 1 (a corrupt input) pushes sixteen ones, in bounded time
+    big = np.array([2 ** 31 - 1, 2 ** 31 - 1], dtype=np.int32)
+    h_dev = torch.from_numpy(np.array([0, (3 << 16) | 0b101], dtype=np.int32)).cuda()
+    gn, _ = sv.gamma_update(h_dev, i32(big), i32([0, 8, 16]))
+    assert list(h_dev.cpu().numpy()) == [(16 << 16) | 0xFFFF] * 2
+    assert list(gn.cpu().numpy()) == [8, 8]
+    say("[control] gamma update, long rounds: ok")
+
+
 def test_gamma_closed_loop():
     """Five rounds: draft with the controller's gammas, verify and update on the GPU."""
     import rejection_sampling_verify_04_amd as sv

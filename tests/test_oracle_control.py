@@ -41,6 +41,15 @@ def test_rounds_become_outcomes():
     assert C.gamma_of(w) == 8                        # 12 / 16
 
 
+def test_long_rounds_keep_the_newest_sixteen():
+    # 20 accepted then a rejection: the newest 16 are fifteen ones, then the zero
+    assert C.push(word(0x1234, 9), 20, 30) == word(0xFFFE, 16)
+    # 40 of 40 accepted: sixteen ones, no zero
+    assert C.push(word(0, 16), 40, 40) == word(0xFFFF, 16)
+    # exactly 16 outcomes (15 ones, a zero) replace the whole window
+    assert C.push(word(0xFFFF, 16), 15, 16) == word(0xFFFE, 16)
+
+
 def test_window_forgets_old_outcomes():
     w = 0
     for _ in range(4):
