@@ -3,13 +3,17 @@
 
 A step is one call of the verify hot path on one batch of synthetic input
 that is already resident in device memory.  The default workload is the
-linear verify B=32, gamma=5, V=32000 bf16 (160 draft positions per step).
+largest verify configuration that one GPU holds: the bimodal-acceptance batch,
+B=256 ragged rows over V=152064 bf16 with gamma in {2, 4, 8} from a 16-step
+acceptance history (about 1124 draft positions and 765 MB of logits per step).
 Other workloads (--workload) measure the remaining configurations.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by
 torch.cuda.synchronize(); the K steps are captured as one HIP graph and
-replayed (one untimed replay first), so host launch overhead does not pace
-the GPU.  The dominant kernel's duration comes from the same K steps run
+replayed, so host launch overhead does not pace the GPU.  Before the timed
+replay the graph is replayed untimed until the GPU has been busy for 0.25 s,
+so that its clocks have settled (the first replays of a cold GPU run up to
+20% slower).  The dominant kernel's duration comes from the same K steps run
 right after, each with a pair of HIP events attached to that kernel's
 dispatch on the call's own stream (the library's one-shot timing hook).
 Inputs rotate over enough copies to exceed the 256 MB Infinity Cache, so
@@ -41,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="linear_v32k",
+    ap.add_argument("--workload", default="bimodal_v152k",
                     choices=["linear_v1000", "linear_v32k", "linear_v128k", "bimodal_v152k",
                              "tree_v32k", "tree_wor_v32k", "attn_tree", "kv_commit",
                              "draft_topk", "tree_prune", "telemetry", "telemetry_tree",
@@ -159,14 +163,25 @@ def _pool_worker(arg):
     return units, rows
 
 
+def host_cores():
+    """Cores this process may run on, the machine's count, and the CPU model."""
+    return dict(affinity=len(os.sched_getaffinity(0)), machine=os.cpu_count(), model=cpu_model())
+
+
+# One GPU's share of its host's CPUs: worker pools stay within it whatever
+# larger count the machine reports.
+HOST_SHARE = 16
+
+
 def cpu_baseline_pool(d, seconds):
-    """The oracle over all host cores: one process per core (at most 16), forked
-    before the GPU is touched, worker w taking batch rows w, w + n, ... for
-    ~seconds.  (A thread pool gains nothing: the oracle's per-position work is
-    Python that holds the interpreter lock.)"""
+    """The oracle over the host cores: one process per core (at most the 16-core
+    share of one GPU), forked before the GPU is touched, worker w taking batch
+    rows w, w + n, ... for ~seconds.  (A thread pool gains nothing: the oracle's
+    per-position work is Python that holds the interpreter lock.)"""
     import multiprocessing
     global _POOL_DATA
-    n = min(16, len(os.sched_getaffinity(0)))
+    hc = host_cores()
+    n = min(HOST_SHARE, hc["affinity"])
     _POOL_DATA = d
     ctx = multiprocessing.get_context("fork")
     t0 = time.monotonic()
@@ -178,11 +193,12 @@ def cpu_baseline_pool(d, seconds):
     rows = sum(r[1] for r in res)
     linear = d["kind"] == "linear"
     return dict(value=units / dt, unit="verified draft positions/s" if linear else "verified draft nodes/s",
-                cores=n, kind="oracle",
+                cores=n, kind="oracle", host_cores=hc,
                 sample="%d batch rows (%d %s) of the same workload in %.1f s, NumPy float64 in "
-                       "%d processes (%s)"
+                       "%d processes (%s; %d cores in this process's affinity mask, %d on the "
+                       "machine; the pool is capped at one GPU's %d-core share)"
                        % (rows, units, "draft positions" if linear else "draft nodes", dt, n,
-                          cpu_model()))
+                          hc["model"], hc["affinity"], hc["machine"] or 0, HOST_SHARE))
 
 
 def cpu_baseline_tree(d, seconds):
@@ -613,6 +629,12 @@ def main():
         step(i)
     torch.cuda.synchronize()
     use_graph = not args.no_graph and wl not in ("attn_tree",)
+    # The GPU's clocks ramp up over the first milliseconds of sustained work
+    # (a 20-step replay of the bimodal batch runs at 180-195 us per step for
+    # its first few replays, then settles at 162 us), so untimed work goes on
+    # until the device has been busy for `settle` seconds before the timed
+    # region.
+    settle = 0.25
     if use_graph:
         # The K timed steps are captured once and replayed as one graph, so
         # the host does not pace the GPU.
@@ -620,13 +642,27 @@ def main():
         with torch.cuda.graph(graph):
             for i in range(args.steps):
                 step(args.warmup + i)
-        graph.replay()          # untimed: uploads the graph
-        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        n_untimed = 0
+        while n_untimed < 1 or time.perf_counter() - t_w < settle:
+            graph.replay()      # untimed: the first uploads the graph
+            torch.cuda.synchronize()
+            n_untimed += 1
+        untimed = "%d eager steps, then %d untimed replays of the timed graph (%.2f s)" % (
+            args.warmup, n_untimed, time.perf_counter() - t_w)
         t0 = time.perf_counter()
         graph.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     else:
+        t_w = time.perf_counter()
+        n_untimed = 0
+        while time.perf_counter() - t_w < settle:
+            step(args.warmup + n_untimed)
+            torch.cuda.synchronize()
+            n_untimed += 1
+        untimed = "%d eager steps, then %d more untimed steps (%.2f s)" % (
+            args.warmup, n_untimed, time.perf_counter() - t_w)
         t0 = time.perf_counter()
         for i in range(args.steps):
             step(args.warmup + i)
@@ -674,11 +710,17 @@ def main():
                 avg_kernel_us=round(avg_kern_s * 1e6, 2),
                 median_kernel_us=round(float(np.median(kern_ms)) * 1e3, 2),
                 hot_cache_kernel_us=round(float(np.median(hot_ms)) * 1e3, 2))
+    # The whole call as a caller sees it (every kernel of the step, back to
+    # back in the replayed graph) against the same algorithmic bytes.
+    whole = alg_bytes / (ms_per_step / 1e3) / 1e9
+    roof["whole_call"] = dict(achieved=round(whole, 1), frac=round(whole / HBM_PEAK_GBS, 4),
+                              us_per_call=round(ms_per_step * 1e3, 2))
     if flops:
         roof["mfma_tflops"] = round(flops / avg_kern_s / 1e12, 2)
         roof["mfma_util"] = round(flops / avg_kern_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
 
     config["launch"] = "hip graph of %d steps" % args.steps if use_graph else "eager"
+    config["untimed_warmup"] = untimed
     out = dict(metric=metric, value=round(units / (ms_per_step / 1e3), 1), unit=unit, n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_per_step, 5),
                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
@@ -699,6 +741,7 @@ def main():
             out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)
         else:
             out["cpu_baseline"] = cpu_baseline_tree(d, args.cpu_seconds)
+        out["cpu_baseline"].setdefault("host_cores", host_cores())
         if pool_baseline is not None:
             out["cpu_baseline_pool"] = pool_baseline
     print(json.dumps(out), flush=True)

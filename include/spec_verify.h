@@ -384,6 +384,17 @@ int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_i
                              int n_rows, int n_slots, uint32_t* out_words, hipStream_t stream);
 
 /*
+ * Diagnostic: y[i] = the hardware base-2 exponential (one v_exp_f32) of the
+ * float32 x[i], for i < n: the function every probability, stop weight and
+ * row sum of the verify calls is formed with (2^(x k - c) with k = log2(e)/T
+ * and an integer offset c).  Lets a caller pin its error, which sets how far
+ * a draw's cumulative masses may sit from their exact values.  x and y are
+ * device arrays of n floats (they may be the same array).  Errors:
+ * SV_ERR_INVALID_ARG for n < 0 or a null pointer when n > 0.
+ */
+int spec_verify_exp2(const float* x, float* y, int n, hipStream_t stream);
+
+/*
  * Diagnostic timing hook (for benchmarks): the calling thread's next
  * spec_verify_linear, spec_verify_tree, spec_verify_attn or
  * spec_verify_kv_commit call attaches `begin` and `end` to the dispatch of

@@ -65,6 +65,8 @@ def library():
                                    vp, vp, vp]
     L.spec_verify_profile_next.restype = i32
     L.spec_verify_profile_next.argtypes = [vp, vp]
+    L.spec_verify_exp2.restype = i32
+    L.spec_verify_exp2.argtypes = [vp, vp, i32, vp]
     L.spec_verify_philox_words.restype = i32
     L.spec_verify_philox_words.argtypes = [u64, u64, vp, i32, i32, vp, vp]
     L.spec_verify_telemetry_linear.restype = i32
@@ -456,6 +458,17 @@ def profile_next(begin_event, end_event, ensure_created=True):
         end_event.record()
     library().spec_verify_profile_next(ctypes.c_void_p(begin_event.cuda_event),
                                        ctypes.c_void_p(end_event.cuda_event))
+
+
+def exp2_hw(x, stream=None):
+    """The hardware 2^x the verify kernels use, elementwise over a float32 device tensor."""
+    L = library()
+    _dev(x, "x", torch.float32)
+    y = torch.empty_like(x)
+    st = L.spec_verify_exp2(_ptr(x), _ptr(y), int(x.numel()), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_exp2")
+    return y
 
 
 def philox_words(seed, step, n_rows, n_slots, row_ids=None, stream=None):

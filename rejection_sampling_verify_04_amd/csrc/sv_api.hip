@@ -414,6 +414,14 @@ int spec_verify_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_i
   return SV_OK;
 }
 
+int spec_verify_exp2(const float* x, float* y, int n, hipStream_t stream) {
+  if (n < 0) return SV_ERR_INVALID_ARG;
+  if (n == 0) return SV_OK;
+  if (!x || !y) return SV_ERR_INVALID_ARG;
+  if (sv::launch_exp2_words(x, y, n, stream) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
 int spec_verify_profile_next(hipEvent_t begin, hipEvent_t end) {
   t_prof = ProfHook{begin, end};
   return SV_OK;

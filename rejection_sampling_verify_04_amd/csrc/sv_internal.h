@@ -155,6 +155,7 @@ hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_
                         hipEvent_t ev_stop);
 hipError_t launch_linear_finish(int dtype, const LinearArgs& a, hipStream_t st);
 hipError_t launch_tree_finish(int dtype, const TreeArgs& a, hipStream_t st);
+hipError_t launch_exp2_words(const float* x, float* y, int n, hipStream_t st);
 hipError_t launch_philox_words(uint64_t seed, uint64_t step, const uint32_t* row_ids,
                                int n_rows, int n_slots, uint32_t* out, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);

@@ -605,6 +605,14 @@ __global__ __launch_bounds__(kThreads) void philox_words_kernel(uint64_t seed, u
   *o = w;
 }
 
+// The hardware 2^x of every probability the verify forms (diagnostic entry
+// point): one element per thread.
+__global__ __launch_bounds__(kThreads) void exp2_words_kernel(const float* x, float* y, int n) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  y[i] = exp2_hw(x[i]);
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers.
 
@@ -664,6 +672,12 @@ hipError_t launch_philox_words(uint64_t seed, uint64_t step, const uint32_t* row
   const long long blocks = (n + kThreads - 1) / kThreads;
   philox_words_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(seed, step, row_ids,
                                                                          n_rows, n_slots, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_exp2_words(const float* x, float* y, int n, hipStream_t st) {
+  const long long blocks = ((long long)n + kThreads - 1) / kThreads;
+  exp2_words_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
   return hipGetLastError();
 }
 

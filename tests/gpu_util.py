@@ -2,10 +2,14 @@
 library through its binding, and compare with the oracle by the parity rules.
 
 Parity rules (same seeded inputs on both sides):
-* accepted counts and token ids are bit-exact, except from the first decision
-  the oracle flags: an acceptance with |u - ratio| < 1e-6, or a draw whose
-  u * R lies within 1e-6 of a cumulative-mass boundary; outputs from a flagged
-  decision on are excused (a float32 implementation may take it either way);
+* accepted counts and token ids are bit-exact, except from the first
+  acceptance the oracle flags (|u - ratio| < 1e-6): outputs from a flagged
+  acceptance on are excused (a float32 implementation may take it either way);
+* every emitted draw is compared: the GPU's token must be one that inverse CDF
+  can return for stop weights within the float32 error bound of
+  tests/draw_bound.py (the oracle's token, or a neighbour across a cumulative
+  boundary that lies inside the bound); the counts of exact matches, of
+  in-bound differences and of decidable draws are reported;
 * probabilities (p_at_draft, q_at_draft, p_at_node): |gpu - oracle| <=
   1e-5 * |oracle|, with a 1e-30 absolute floor;
 * attention output within 2e-2 absolute (bf16 output).
@@ -18,6 +22,8 @@ import pytest
 
 import oracle
 from oracle import linear as OL
+from oracle.philox import verify_uniforms
+import draw_bound as DB
 
 PROB_RTOL = 1e-5
 PROB_ATOL = 1e-30
@@ -86,12 +92,28 @@ def assert_probs(gpu, ref, what):
     return float(rel.max()) if rel.size else 0.0
 
 
-def compare_linear(gpu, ref, d):
-    """Assert parity; return a summary dict (flag counts, max unflagged |delta r|)."""
+def linear_draw_weights(d, b, r):
+    """Exact stop weights of a linear row's draw and their float32 bound."""
+    off = d["offsets"]
+    o0, o1 = int(off[b]), int(off[b + 1])
+    n = r.num_accepted
+    x = oracle.decode_logits(d["target"][o0 + b + n], d["dtype"])
+    Tt = float(d["temp_target"][b])
+    if r.stop_kind == "reject" and not (r.status & OL.ROW_WARN_RZERO):
+        y = oracle.decode_logits(d["draft"][o0 + n], d["dtype"])
+        return DB.residual_bound(x, y, Tt, float(d["temp_draft"][b]))
+    return DB.prob_bound(x, Tt)
+
+
+def compare_linear(gpu, ref, d, seed=None, step=None, row_ids=None):
+    """Assert parity; return a summary dict (flag counts, draw tally, max unflagged |delta r|)."""
     num_acc, out_tokens, p_at, q_at, status, results = ref
     off = np.asarray(d["offsets"], dtype=np.int64)
     B = len(off) - 1
-    n_flag_acc = n_flag_smp = 0
+    seed = d["seed"] if seed is None else seed
+    step = d["step"] if step is None else step
+    n_flag_acc = 0
+    tally = DB.DrawTally()
     max_dr = 0.0
     g_n = gpu["num_accepted"]
     g_out = gpu["out_tokens"]
@@ -114,11 +136,17 @@ def compare_linear(gpu, ref, d):
             assert g_n[b] == n, "row %d: num_accepted gpu %d oracle %d (min margin %.3g)" % (
                 b, g_n[b], n, r.min_accept_margin)
             assert np.array_equal(out_g[:n], r.out_tokens[:n]), "row %d accepted tokens" % b
-            if r.flagged_sample:
-                n_flag_smp += 1
+            if r.stop_kind == "greedy":
+                assert out_g[n] == r.out_tokens[n], "row %d (greedy): drawn token gpu %d oracle %d" % (
+                    b, out_g[n], r.out_tokens[n])
             else:
-                assert out_g[n] == r.out_tokens[n], "row %d (%s): drawn token gpu %d oracle %d" % (
-                    b, r.stop_kind, out_g[n], r.out_tokens[n])
+                rid = b if row_ids is None else int(row_ids[b])
+                u = verify_uniforms(seed, step, rid, g + 1)[1][n]
+                w, e = linear_draw_weights(d, b, r)
+                try:
+                    tally.add(int(out_g[n]), w, e, u)
+                except AssertionError as ex:
+                    raise AssertionError("row %d (%s): %s" % (b, r.stop_kind, ex))
             assert np.all(out_g[n + 1:] == -1)
         else:
             n_flag_acc += 1
@@ -143,7 +171,7 @@ def compare_linear(gpu, ref, d):
     if "p_at_draft" in gpu and sel.size:
         rel_p = assert_probs(gpu["p_at_draft"][sel], p_at[sel], "p_at_draft")
         rel_q = assert_probs(gpu["q_at_draft"][sel], q_at[sel], "q_at_draft")
-    return dict(flagged_accept=n_flag_acc, flagged_sample=n_flag_smp, max_unflagged_dr=max_dr,
+    return dict(flagged_accept=n_flag_acc, draws=tally.summary(), max_unflagged_dr=max_dr,
                 max_rel_p=rel_p, max_rel_q=rel_q)
 
 
@@ -173,10 +201,35 @@ def run_oracle_tree(d):
                                    step=d["step"])
 
 
+def tree_draw_weights(d, b, r):
+    """Exact stop weights of a tree row's draw, their float32 bound and the
+    tokens the draw masks (TOPK: the rejected children)."""
+    node = r.stop_node
+    nn = d["parents"].shape[1] if d.get("n_nodes") is None else int(d["n_nodes"][b])
+    par = d["parents"][b]
+    kids = [c for c in range(1, nn) if int(par[c]) == node]
+    toks = [int(d["tokens"][b][c]) for c in kids]
+    x = oracle.decode_logits(d["target"][b][node], d["dtype"])
+    Tt = float(d["temp_target"][b])
+    V = len(x)
+    if d["kind"] == "tree_wor":
+        y = oracle.decode_logits(d["draft"][b][node], d["dtype"])
+        w, e = DB.wor_bound(x, y, Tt, float(d["temp_draft"][b]), toks)
+        return w, e, None
+    w, e = DB.prob_bound(x, Tt)
+    if r.status & OL.ROW_WARN_RZERO or not toks:
+        return w, e, None
+    masked = np.zeros(V, dtype=bool)
+    masked[toks] = True
+    w = np.where(masked, 0.0, w)
+    return w, e, masked
+
+
 def compare_tree(gpu, ref, d):
     num_acc, path, out_tokens, p_at, status, results = ref
     B, N = d["parents"].shape
-    n_flag = n_smp = 0
+    n_flag = 0
+    tally = DB.DrawTally()
     for b in range(B):
         r = results[b]
         if r.status & OL.ROW_ERROR_MASK:
@@ -190,12 +243,18 @@ def compare_tree(gpu, ref, d):
                 b, gpu["num_accepted"][b], n)
             assert np.array_equal(gpu["path_nodes"][b][:n], r.path_nodes[:n])
             assert np.array_equal(gpu["out_tokens"][b][:n], r.out_tokens[:n])
-            if r.flagged_sample:
-                n_smp += 1
-            else:
+            if r.stop_kind == "greedy":
                 assert gpu["out_tokens"][b][n] == r.out_tokens[n], (
-                    "tree row %d (%s at node %d): drawn token gpu %d oracle %d" % (
-                        b, r.stop_kind, r.stop_node, gpu["out_tokens"][b][n], r.out_tokens[n]))
+                    "tree row %d (greedy at node %d): drawn token gpu %d oracle %d" % (
+                        b, r.stop_node, gpu["out_tokens"][b][n], r.out_tokens[n]))
+            else:
+                u = verify_uniforms(d["seed"], d["step"], b, N)[1][r.stop_node]
+                w, e, masked = tree_draw_weights(d, b, r)
+                try:
+                    tally.add(int(gpu["out_tokens"][b][n]), w, e, u, masked)
+                except AssertionError as ex:
+                    raise AssertionError("tree row %d (%s at node %d): %s" % (
+                        b, r.stop_kind, r.stop_node, ex))
             assert np.all(gpu["out_tokens"][b][n + 1:] == -1)
             assert np.all(gpu["path_nodes"][b][n:] == -1)
             # the same walk tests the same children: the zero-q warning agrees
@@ -207,4 +266,4 @@ def compare_tree(gpu, ref, d):
             assert np.array_equal(gpu["out_tokens"][b][:f], r.out_tokens[:f])
         nn = N if d.get("n_nodes") is None else int(d["n_nodes"][b])
         assert_probs(gpu["p_at_node"][b][1:nn], p_at[b][1:nn], "p_at_node")
-    return dict(flagged_accept=n_flag, flagged_sample=n_smp)
+    return dict(flagged_accept=n_flag, draws=tally.summary())

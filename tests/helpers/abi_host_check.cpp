@@ -108,6 +108,9 @@ void worker(int tid, size_t ws_linear, size_t ws_tree) {
            SV_ERR_INVALID_ARG);
     EXPECT(spec_verify_philox_words(0, 0, nullptr, 3, 5, (uint32_t*)P(8), nullptr),
            SV_ERR_INVALID_ARG);
+    EXPECT(spec_verify_exp2(fp, (float*)P(256), -1, nullptr), SV_ERR_INVALID_ARG);
+    EXPECT(spec_verify_exp2(nullptr, (float*)P(256), 5, nullptr), SV_ERR_INVALID_ARG);
+    EXPECT(spec_verify_exp2(nullptr, nullptr, 0, nullptr), SV_OK);
     if (spec_verify_status_string(SV_ERR_HIP)[0] == 0) g_fail++;
   }
 }

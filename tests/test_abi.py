@@ -136,6 +136,9 @@ def test_tree_and_attn_host_validation(lib):
     gu = lib.spec_verify_gamma_update
     assert gu(p, p, p, None, 1, 4, p, None, None) == -1     # coupling without temperatures
     assert gu(p, p, p, None, 0, 0, p, None, None) == 0      # empty
+    assert lib.spec_verify_exp2(p, p, -1, None) == -1
+    assert lib.spec_verify_exp2(None, p, 4, None) == -1
+    assert lib.spec_verify_exp2(None, None, 0, None) == 0
     assert lib.spec_verify_philox_words(0, 0, None, 0, 5, None, None) == 0
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, None, None) == -1
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, ctypes.c_void_p(8), None) == -1

@@ -23,7 +23,8 @@ def check(d, label, **kw):
                                                          int(d["offsets"][-1])))
     gpu = run_linear(d, **kw)
     ref = run_oracle_linear(d, **kw)
-    s = compare_linear(gpu, ref, d)
+    s = compare_linear(gpu, ref, d, seed=kw.get("seed"), step=kw.get("step"),
+                       row_ids=kw.get("row_ids"))
     say("[linear] %s: ok %s" % (label, s))
     return gpu, ref, s
 
