@@ -67,6 +67,7 @@ extern "C" {
 #define SV_ERR_UNSUPPORTED (-2) /* valid request this build does not implement */
 #define SV_ERR_WORKSPACE (-3)   /* workspace missing, too small or misaligned */
 #define SV_ERR_HIP (-4)         /* a kernel launch failed */
+#define SV_ERR_SCRATCH (-5)     /* needs more than the static scratch of a _noalloc call */
 
 /* Logit element types. */
 #define SV_F32 0
@@ -90,6 +91,7 @@ extern "C" {
 #define SV_MAX_TOPK 64
 #define SV_MAX_CANDIDATES 1024
 #define SV_WORKSPACE_ALIGN 256
+#define SV_STATIC_SCRATCH_BYTES (4u << 20) /* per-GPU scratch of spec_verify_linear_noalloc */
 
 /* Library version, (major << 16) | minor. */
 int spec_verify_version(void);
@@ -143,6 +145,34 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
                        int32_t* num_accepted, int32_t* out_tokens,
                        float* p_at_draft, float* q_at_draft, int32_t* row_status,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture that must not call hipMalloc, tight serving loops, and harnesses
+ * that forbid allocation.  The same verify as spec_verify_linear (same
+ * arguments, outputs, row statuses and results), without the workspace
+ * arguments: the workspace is a static device array of
+ * SV_STATIC_SCRATCH_BYTES (4 MiB) that the library keeps on each GPU it runs
+ * on until the process ends.  The call allocates nothing; the caller still
+ * passes inputs and outputs.  The GPU is the calling thread's current device.
+ *
+ * Returns SV_ERR_SCRATCH, before any launch, when
+ * spec_verify_linear_workspace_size(B, total_draft, V, dtype) exceeds
+ * SV_STATIC_SCRATCH_BYTES (B = 256 rows with 1130 drafts at V = 152064 need
+ * about 1.4 MB); SV_ERR_HIP when the array's device address cannot be had;
+ * otherwise what spec_verify_linear returns.  Nothing in the array has to
+ * start at zero: a call reads only bytes it wrote earlier in the same call.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on two streams, or from two host threads without ordering)
+ * race on it and give undefined results; calls ordered on one stream do not.
+ */
+int spec_verify_linear_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                               int B, int V, int total_draft, const int32_t* draft_offsets,
+                               const int32_t* draft_tokens, const float* temp_target,
+                               const float* temp_draft, uint64_t seed, uint64_t step,
+                               const uint32_t* row_ids, int32_t* num_accepted,
+                               int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                               int32_t* row_status, hipStream_t stream);
 
 /*
  * Tree verify (kwkr §5.3; cf-1 §5.4; lonae tree-attention paragraphs), TOPK

@@ -20,6 +20,8 @@ SV_BF16 = 1
 SV_TREE_TOPK = 0
 SV_TREE_SAMPLED_WOR = 1
 SV_WORKSPACE_ALIGN = 256
+SV_STATIC_SCRATCH_BYTES = 4 << 20
+SV_ERR_SCRATCH = -5
 
 ROW_BAD_TOKEN = 1
 ROW_BAD_SHAPE = 2
@@ -55,6 +57,9 @@ def library():
     L.spec_verify_linear.restype = i32
     L.spec_verify_linear.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, u64, u64, vp,
                                      vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_linear_noalloc.restype = i32
+    L.spec_verify_linear_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, u64, u64,
+                                             vp, vp, vp, vp, vp, vp, vp]
     L.spec_verify_tree_workspace_size.restype = sz
     L.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
     L.spec_verify_tree.restype = i32
@@ -181,6 +186,43 @@ def verify_linear(target_logits, draft_logits, draft_offsets, draft_tokens, temp
         _ptr(outputs.get("row_status")), _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_linear")
+    return outputs
+
+
+def verify_linear_noalloc(target_logits, draft_logits, draft_offsets, draft_tokens, temp_target,
+                          temp_draft, seed=0, step=0, row_ids=None, outputs=None, stream=None):
+    """Linear verify with the library's static per-GPU scratch as its workspace
+    (see spec_verify_linear_noalloc): nothing is allocated when `outputs`
+    (the dict verify_linear returns) is passed in."""
+    L = library()
+    _dev(target_logits, "target_logits")
+    _dev(draft_logits, "draft_logits", target_logits.dtype)
+    dt = _logit_code(target_logits, "target_logits")
+    _dev(draft_offsets, "draft_offsets", torch.int32)
+    _dev(draft_tokens, "draft_tokens", torch.int32)
+    _dev(temp_target, "temp_target", torch.float32)
+    _dev(temp_draft, "temp_draft", torch.float32)
+    if row_ids is not None:
+        _dev(row_ids, "row_ids", torch.int32)
+    B = draft_offsets.numel() - 1
+    total = draft_tokens.numel()
+    V = target_logits.shape[-1]
+    dev = target_logits.device
+    if outputs is None:
+        outputs = dict(
+            num_accepted=torch.empty(B, dtype=torch.int32, device=dev),
+            out_tokens=torch.empty(total + B, dtype=torch.int32, device=dev),
+            row_status=torch.empty(B, dtype=torch.int32, device=dev),
+            p_at_draft=torch.empty(total, dtype=torch.float32, device=dev),
+            q_at_draft=torch.empty(total, dtype=torch.float32, device=dev))
+    st = L.spec_verify_linear_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), dt, B, V, total, _ptr(draft_offsets),
+        _ptr(draft_tokens), _ptr(temp_target), _ptr(temp_draft), int(seed), int(step),
+        _ptr(row_ids), _ptr(outputs["num_accepted"]), _ptr(outputs["out_tokens"]),
+        _ptr(outputs.get("p_at_draft")), _ptr(outputs.get("q_at_draft")),
+        _ptr(outputs.get("row_status")), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_linear_noalloc")
     return outputs
 
 

@@ -56,53 +56,62 @@ int check_workspace(void* ws, size_t bytes, size_t need) {
   return SV_OK;
 }
 
-}  // namespace
+// Workspace of the allocation-free linear verify: a static device array, one
+// copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: each device's copy is found once, with that
+// device current, through hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SV_STATIC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[sv::kMaxDevices];
 
-extern "C" {
-
-int spec_verify_version(void) { return (0 << 16) | 1; }
-
-const char* spec_verify_status_string(int status) {
-  switch (status) {
-    case SV_OK: return "ok";
-    case SV_ERR_INVALID_ARG: return "invalid argument";
-    case SV_ERR_UNSUPPORTED: return "unsupported request";
-    case SV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
-    case SV_ERR_HIP: return "HIP kernel launch failed";
-    default: return "unknown status";
-  }
+// This device's copy of `scratch` (nullptr if its address cannot be had).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= sv::kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch[dev].store(q, std::memory_order_release);
+  return q;
 }
 
-size_t spec_verify_linear_workspace_size(int B, int total_draft, int V, int dtype) {
-  (void)dtype;
-  if (B < 0 || total_draft < 0 || V < 1) return 0;
-  return layout(2LL * total_draft + B, B, V, 2LL * total_draft, true).total;
-}
-
-int spec_verify_linear(const void* target_logits, const void* draft_logits, int dtype, int B,
-                       int V, int total_draft, const int32_t* draft_offsets,
-                       const int32_t* draft_tokens, const float* temp_target,
-                       const float* temp_draft, uint64_t seed, uint64_t step,
-                       const uint32_t* row_ids, int32_t* num_accepted, int32_t* out_tokens,
-                       float* p_at_draft, float* q_at_draft, int32_t* row_status,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Argument checks of the linear verify; SV_OK, with the workspace layout in
+// *l, when the call has work to do (*empty false).
+int linear_check(const void* target_logits, const void* draft_logits, int dtype, int B, int V,
+                 int total_draft, const int32_t* draft_offsets, const int32_t* draft_tokens,
+                 const float* temp_target, const float* temp_draft, const int32_t* num_accepted,
+                 const int32_t* out_tokens, Layout* l, bool* empty) {
+  *empty = false;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
   if (B < 0 || V < 1 || total_draft < 0) return SV_ERR_INVALID_ARG;
   if ((long long)total_draft > (long long)B * SV_MAX_GAMMA) return SV_ERR_INVALID_ARG;
-  if (B == 0) return SV_OK;
+  if (B == 0) {
+    *empty = true;
+    return SV_OK;
+  }
   if (n_chunks_for(V) > sv::kMaxChunks) return SV_ERR_UNSUPPORTED;
   if (!target_logits || !draft_offsets || !temp_target || !temp_draft || !num_accepted ||
       !out_tokens)
     return SV_ERR_INVALID_ARG;
   if (total_draft > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_INVALID_ARG;
-  const long long n_t = (long long)total_draft + B;
-  const long long n_rows = n_t + total_draft;
+  const long long n_rows = 2LL * total_draft + B;
   const int nc = n_chunks_for(V);
   if (sv::stats_items(n_rows, nc) >= (1LL << 31) || (long long)B * nc >= (1LL << 31))
     return SV_ERR_INVALID_ARG;
-  const Layout l = layout(n_rows, B, V, 2LL * total_draft, true);
-  const int wst = check_workspace(workspace, workspace_bytes, l.total);
-  if (wst != SV_OK) return wst;
+  *l = layout(n_rows, B, V, 2LL * total_draft, true);
+  return SV_OK;
+}
+
+// The linear verify's launches on a checked call, with its workspace.
+int linear_run(const void* target_logits, const void* draft_logits, int dtype, int B, int V,
+               int total_draft, const int32_t* draft_offsets, const int32_t* draft_tokens,
+               const float* temp_target, const float* temp_draft, uint64_t seed, uint64_t step,
+               const uint32_t* row_ids, int32_t* num_accepted, int32_t* out_tokens,
+               float* p_at_draft, float* q_at_draft, int32_t* row_status, const Layout& l,
+               void* workspace, hipStream_t stream) {
+  const long long n_t = (long long)total_draft + B;
+  const long long n_rows = n_t + total_draft;
+  const int nc = n_chunks_for(V);
 
   const int es = dtype == SV_BF16 ? 2 : 4;
   const int vec_ok = ((long long)V * es) % 16 == 0 && aligned16(target_logits) &&
@@ -158,6 +167,72 @@ int spec_verify_linear(const void* target_logits, const void* draft_logits, int 
   f.vec_ok = vec_ok;
   if (sv::launch_linear_finish(dtype, f, stream) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_version(void) { return (0 << 16) | 1; }
+
+const char* spec_verify_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported request";
+    case SV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case SV_ERR_HIP: return "HIP kernel launch failed";
+    case SV_ERR_SCRATCH: return "request needs more than the built-in static scratch";
+    default: return "unknown status";
+  }
+}
+
+size_t spec_verify_linear_workspace_size(int B, int total_draft, int V, int dtype) {
+  (void)dtype;
+  if (B < 0 || total_draft < 0 || V < 1) return 0;
+  return layout(2LL * total_draft + B, B, V, 2LL * total_draft, true).total;
+}
+
+
+int spec_verify_linear(const void* target_logits, const void* draft_logits, int dtype, int B,
+                       int V, int total_draft, const int32_t* draft_offsets,
+                       const int32_t* draft_tokens, const float* temp_target,
+                       const float* temp_draft, uint64_t seed, uint64_t step,
+                       const uint32_t* row_ids, int32_t* num_accepted, int32_t* out_tokens,
+                       float* p_at_draft, float* q_at_draft, int32_t* row_status,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Layout l;
+  bool empty;
+  int st = linear_check(target_logits, draft_logits, dtype, B, V, total_draft, draft_offsets,
+                        draft_tokens, temp_target, temp_draft, num_accepted, out_tokens, &l,
+                        &empty);
+  if (st != SV_OK || empty) return st;
+  st = check_workspace(workspace, workspace_bytes, l.total);
+  if (st != SV_OK) return st;
+  return linear_run(target_logits, draft_logits, dtype, B, V, total_draft, draft_offsets,
+                    draft_tokens, temp_target, temp_draft, seed, step, row_ids, num_accepted,
+                    out_tokens, p_at_draft, q_at_draft, row_status, l, workspace, stream);
+}
+
+int spec_verify_linear_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                               int B, int V, int total_draft, const int32_t* draft_offsets,
+                               const int32_t* draft_tokens, const float* temp_target,
+                               const float* temp_draft, uint64_t seed, uint64_t step,
+                               const uint32_t* row_ids, int32_t* num_accepted,
+                               int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                               int32_t* row_status, hipStream_t stream) {
+  Layout l;
+  bool empty;
+  const int st = linear_check(target_logits, draft_logits, dtype, B, V, total_draft,
+                              draft_offsets, draft_tokens, temp_target, temp_draft, num_accepted,
+                              out_tokens, &l, &empty);
+  if (st != SV_OK || empty) return st;
+  if (l.total > (size_t)SV_STATIC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (!ws) return SV_ERR_HIP;
+  return linear_run(target_logits, draft_logits, dtype, B, V, total_draft, draft_offsets,
+                    draft_tokens, temp_target, temp_draft, seed, step, row_ids, num_accepted,
+                    out_tokens, p_at_draft, q_at_draft, row_status, l, ws, stream);
 }
 
 // Sized for either candidate mode (SAMPLED_WOR keeps the draft rows' partials

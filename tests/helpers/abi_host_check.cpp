@@ -108,6 +108,14 @@ void worker(int tid, size_t ws_linear, size_t ws_tree) {
            SV_ERR_INVALID_ARG);
     EXPECT(spec_verify_philox_words(0, 0, nullptr, 3, 5, (uint32_t*)P(8), nullptr),
            SV_ERR_INVALID_ARG);
+    EXPECT(spec_verify_linear_noalloc(p, p, 7, 2, 100, 4, ip, ip, fp, fp, 0, 0, nullptr, op, op,
+                                      nullptr, nullptr, nullptr, nullptr), SV_ERR_INVALID_ARG);
+    EXPECT(spec_verify_linear_noalloc(p, p, SV_BF16, 4096, 152064, 4096 * 8, ip, ip, fp, fp, 0, 0,
+                                      nullptr, op, op, nullptr, nullptr, nullptr, nullptr),
+           SV_ERR_SCRATCH);
+    EXPECT(spec_verify_linear_noalloc(p, p, SV_BF16, INT_MAX, INT_MAX, INT_MAX, ip, ip, fp, fp, 0,
+                                      0, nullptr, op, op, nullptr, nullptr, nullptr, nullptr),
+           SV_ERR_UNSUPPORTED);
     EXPECT(spec_verify_exp2(fp, (float*)P(256), -1, nullptr), SV_ERR_INVALID_ARG);
     EXPECT(spec_verify_exp2(nullptr, (float*)P(256), 5, nullptr), SV_ERR_INVALID_ARG);
     EXPECT(spec_verify_exp2(nullptr, nullptr, 0, nullptr), SV_OK);

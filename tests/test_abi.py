@@ -55,7 +55,7 @@ def test_version_and_status_strings(lib):
     import rejection_sampling_verify_04_amd as sv
     assert sv.version() >= 1
     assert sv.status_string(0) == "ok"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert sv.status_string(code) not in ("ok", "unknown status")
     assert sv.status_string(-99) == "unknown status"
 
@@ -142,3 +142,23 @@ def test_tree_and_attn_host_validation(lib):
     assert lib.spec_verify_philox_words(0, 0, None, 0, 5, None, None) == 0
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, None, None) == -1
     assert lib.spec_verify_philox_words(0, 0, None, 3, 5, ctypes.c_void_p(8), None) == -1
+
+
+def test_noalloc_host_validation(lib):
+    """The allocation-free linear verify refuses, before any launch, what the
+    workspace entry point refuses, and requests beyond its static scratch."""
+    import rejection_sampling_verify_04_amd as sv
+    p = ctypes.c_void_p(256)
+    call = lambda dtype, B, V, total, target=p: lib.spec_verify_linear_noalloc(
+        target, p, dtype, B, V, total, p, p, p, p, 0, 0, None, p, p, None, None, None, None)
+    assert call(7, 2, 100, 4) == -1                 # dtype
+    assert call(1, 2, 100, 129) == -1               # some gamma_b > 64
+    assert call(1, 0, 100, 0) == 0                  # empty batch: no-op
+    assert call(1, 2, 100, 4, target=None) == -1
+    assert call(1, 2, 64 * 8192 + 1, 4) == -2       # vocabulary beyond the chunk table
+    need = lib.spec_verify_linear_workspace_size(4096, 4096 * 8, 152064, 1)
+    assert need > sv.SV_STATIC_SCRATCH_BYTES
+    assert call(1, 4096, 152064, 4096 * 8) == sv.SV_ERR_SCRATCH
+    # the configurations it is for fit
+    assert lib.spec_verify_linear_workspace_size(256, 1130, 152064, 1) <= sv.SV_STATIC_SCRATCH_BYTES
+    assert lib.spec_verify_linear_workspace_size(128, 1024, 128256, 1) <= sv.SV_STATIC_SCRATCH_BYTES
