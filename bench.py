@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying one HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle-seconds", type=float, default=0.25,
+                    help="untimed work before the timed steps, so that the GPU clocks settle "
+                         "(0 for counter runs, which need few dispatches)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -634,7 +637,7 @@ def main():
     # its first few replays, then settles at 162 us), so untimed work goes on
     # until the device has been busy for `settle` seconds before the timed
     # region.
-    settle = 0.25
+    settle = args.settle_seconds
     if use_graph:
         # The K timed steps are captured once and replayed as one graph, so
         # the host does not pace the GPU.

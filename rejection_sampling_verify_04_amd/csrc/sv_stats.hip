@@ -254,8 +254,9 @@ __device__ __forceinline__ int wave_kth_bit(unsigned long long m, int k) {
   return hit ? __ffsll((long long)hit) - 1 : 0;
 }
 
-// RING = sub-segments in flight per wave: 2 for streaming many chunks per
-// wave, 4 (a whole chunk) when every wave has about one chunk.
+// RING = sub-segments in flight per wave: 2, or 4 (a whole chunk) with fewer
+// resident waves; the launch takes the one whose grid ends in the fuller
+// round.
 //
 // Tree rows are compacted when the trees' shapes fit in LDS: the units run
 // over the used rows only (each tree's first n_nodes target rows, then the
@@ -655,8 +656,18 @@ hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t st, hipEvent_
     return hipGetLastError();
   }
   const long long want = (units + kWaves - 1) / kWaves;
-  // a whole chunk in flight per wave when one round of waves covers the call
-  const int ring = (dt == 1 && want <= stats_resident_blocks(1, 4)) ? 4 : 2;
+  // A whole chunk in flight per wave (RING 4, fewer resident waves) when its
+  // grid covers the units in whole rounds at least as well as RING 2's: the
+  // last round of a streaming grid runs with too few waves to fill HBM, so
+  // the fuller last round wins (bimodal batch 121.5 -> 118.6 us, SAMPLED_WOR
+  // trees 60.7 -> 59.0 us; one round of waves is always whole).
+  auto round_fill = [&](int r) {
+    const long long items = std::min<long long>(want, stats_resident_blocks(dt, r));
+    const long long waves = items * kWaves;
+    const long long rounds = (units + waves - 1) / waves;
+    return (double)units / (double)(rounds * waves);
+  };
+  const int ring = (dt == 1 && round_fill(4) >= round_fill(2)) ? 4 : 2;
   const dim3 grid((unsigned)(std::min<long long>(want, stats_resident_blocks(dt, ring)) +
                              gather_blocks(a)));
   if (dt == 1 && ring == 4) SV_LAUNCH((stats_kernel<1, 4>));
