@@ -257,12 +257,14 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
 // Q = q's mass left in q_j sets mu = lambda + P / Q and
 // G = sum_v max(0, a - L'_v b), L'_v = mu for tokens still in q_j; then
 // lambda = mu and P = G (both unchanged when G = 0: the residual is empty).
-// One vocabulary pass over the node's two rows forms G per chunk (and, when
-// q(t_j) is more than half of Q, the draft mass that stays once t_j leaves;
-// otherwise that is Q - q(t_j)), so a walk costs one pass per rejected
-// sibling, plus the draw.  When every child is rejected, the draw's weights
-// are the last pass's, and its chunk masses are reused.  A pass is bound by
-// the vector ALU of its one CU (two exponentials per element).
+// One vocabulary pass over the node's weights forms G (and, when q(t_j) is
+// more than half of Q, the draft mass that stays once t_j leaves; otherwise
+// that is Q - q(t_j)), so a walk costs one pass per rejected sibling, plus
+// the draw.  When every child is rejected, the draw's weights are the last
+// pass's.  Without the cache a pass reads the node's two rows and forms two
+// exponentials per element; with it (V of at most 4 chunks) only a node's
+// first pass does, and the later ones form max(0, a - L b) from LDS and
+// registers.
 
 // The rows of one tree node as the SAMPLED_WOR passes read them, with
 // p(v) = 2^(x p_k - p_c) p_inv_s + [v = p_amax] (and q likewise): a sampled
@@ -470,12 +472,8 @@ __device__ double wor_pass(const WorDist& d, int V, int nc, float lam,
   return G;
 }
 
-// With the vocabulary in at most NC_MAX chunks, a node's target term
-// a(v) = p(v) is kept in LDS as float32 from the node's first pass on:
-// between the passes of one node only lambda changes, so the later passes
-// read the draft row alone and form one exponential per element.  a is
-// formed by the same expression as in wor_weights, so every weight is the
-// same value either way.
+// Vocabularies of at most this many chunks keep a node's terms in a cache
+// (a(v) in LDS, b(v) in registers; below).
 constexpr int kWorCacheChunks = 4;   // V <= 32768
 
 // threadIdx.x as a value the compiler cannot prove invariant: what a pass
@@ -487,88 +485,37 @@ __device__ __forceinline__ int opaque_tid() {
   return t;
 }
 
-// a(v) of this thread's elements of every chunk into s_a (each thread later
-// reads back only what it wrote, so no barrier is needed).  All loads are
-// in flight together; addresses past V are clamped into the row.
-template <int DT, int NC>
-__device__ __forceinline__ void wor_fill(const WorDist& d, int V, float* s_a) {
-  constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV, NV = StopVec<DT>::NV;
-  const int tix = opaque_tid();
-  uint4 raw[NC][NV];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int e0 = c * kChunk + tix * kPerThread;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int ej = e0 + j * EPV;
-      raw[c][j] = *(const uint4*)(d.xrow + (ej < V ? (long long)ej * ES : 0));
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int e0 = c * kChunk + tix * kPerThread;
-    float xp[kPerThread], av[kPerThread];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const uint32_t rw[4] = {raw[c][j].x, raw[c][j].y, raw[c][j].z, raw[c][j].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        if (DT == 1) {
-          xp[j * 8 + 2 * h] = bf16_lo(rw[h]);
-          xp[j * 8 + 2 * h + 1] = bf16_hi(rw[h]);
-        } else {
-          xp[j * EPV + h] = __uint_as_float(rw[h]);
-        }
-      }
-    }
-    // the expression of wor_weights (fmaf with a zero addend rounds as the
-    // plain product does)
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
-      av[e] = fmaf(exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)), d.p_inv_s,
-                   e0 + e == d.p_amax ? 1.0f : 0.0f);
-    float4* ca = (float4*)(s_a + e0);
-    ca[0] = make_float4(av[0], av[1], av[2], av[3]);
-    ca[1] = make_float4(av[4], av[5], av[6], av[7]);
-  }
-}
+// With the vocabulary in at most NC chunks, a node's target term a(v) = p(v)
+// is kept in LDS and its draft term b(v) = q(v) in registers (this thread's
+// NC * 8 elements), filled by the node's first pass: between the passes of
+// one node only lambda changes, so every later pass forms max(0, a - L b)
+// with no global load and no exponential.  a and b are formed by the
+// expressions of wor_weights (elements past V hold 0, whose weight is 0), so
+// every weight is the same value as the draw forms from memory.  Each thread
+// reads back only the a values it wrote, so the LDS cache needs no barrier.
+//
+// A pass needs only the total G of the new weights (and sometimes the draft
+// mass left): one block reduction of two values.  The chunk masses, which
+// only the draw needs, are formed once, by wor_masses_r, when the walk ends
+// on a rejection.
 
-// As wor_weights (vector path), with a(v) read from the node's cache s_a
-// and the draft row's values from `r`.
-template <int DT, bool WANT_E>
-__device__ __forceinline__ void wor_weights_c(const WorDist& d, int V, int chunk, int tix,
-                                              bool excl, const StopVec<DT>& r, const float* s_a,
-                                              float lam, const int* ex_tok, const float* ex_lam,
-                                              int nex, int t_cur, float w[kPerThread],
-                                              float be[kPerThread]) {
-  constexpr int EPV = StopVec<DT>::EPV;
-  const int e0 = chunk * kChunk + tix * kPerThread;
-  float xq[kPerThread], av[kPerThread];
-#pragma unroll
-  for (int j = 0; j < StopVec<DT>::NV; ++j) {
-    const uint32_t sw[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      if (DT == 1) {
-        xq[j * 8 + 2 * h] = bf16_lo(sw[h]);
-        xq[j * 8 + 2 * h + 1] = bf16_hi(sw[h]);
-      } else {
-        xq[j * EPV + h] = __uint_as_float(sw[h]);
-      }
-    }
-  }
+// This thread's weights of chunk c from the cache (and, for WANT_E, the
+// draft terms outside the excluded tokens and t_cur).
+template <int NC, bool WANT_E>
+__device__ __forceinline__ void wor_chunk_r(const float* s_a, const float (&rb)[NC * kPerThread],
+                                            int c, int tix, bool hit, float lam,
+                                            const int* ex_tok, const float* ex_lam, int nex,
+                                            int t_cur, float w[kPerThread], float be[kPerThread]) {
+  const int e0 = c * kChunk + tix * kPerThread;
   const float4* ca = (const float4*)(s_a + e0);
   const float4 lo = ca[0], hi = ca[1];
-  av[0] = lo.x; av[1] = lo.y; av[2] = lo.z; av[3] = lo.w;
-  av[4] = hi.x; av[5] = hi.y; av[6] = hi.z; av[7] = hi.w;
-  if (!excl && !d.onehot && e0 + kPerThread <= V) {
-    // no excluded token (nor t_cur) among these elements, sampled rows, all
-    // inside the row: lambda for every element (the same values as below)
+  const float av[kPerThread] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  if (!hit) {
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const float b = exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
-      w[e] = fmaxf(fmaf(-lam, b, av[e]), 0.0f);
-      if (WANT_E) be[e] = b;
+      const float bv = rb[c * kPerThread + e];
+      w[e] = fmaxf(fmaf(-lam, bv, av[e]), 0.0f);
+      if (WANT_E) be[e] = bv;
     }
     return;
   }
@@ -590,81 +537,151 @@ __device__ __forceinline__ void wor_weights_c(const WorDist& d, int V, int chunk
     }
   }
   if (WANT_E && (unsigned)(t_cur - e0) < (unsigned)kPerThread) exm |= 1u << (t_cur - e0);
-  if (!d.onehot && e0 + kPerThread <= V) {
-    // sampled rows, elements all inside the row (the same values as below)
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const float b = exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
-      w[e] = fmaxf(fmaf(-lv[e], b, av[e]), 0.0f);
-      if (WANT_E) be[e] = ((exm >> e) & 1u) ? 0.0f : b;
-    }
-    return;
-  }
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const int idx = e0 + e;
-    const float b = fmaf(exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)), d.q_inv_s,
-                         idx == d.q_amax ? 1.0f : 0.0f);
-    const float wv = fmaxf(fmaf(-lv[e], b, av[e]), 0.0f);
-    const bool in = idx < V;
-    w[e] = in ? wv : 0.0f;
-    if (WANT_E) be[e] = (in && !((exm >> e) & 1u)) ? b : 0.0f;
+    const float bv = rb[c * kPerThread + e];
+    w[e] = fmaxf(fmaf(-lv[e], bv, av[e]), 0.0f);
+    if (WANT_E) be[e] = ((exm >> e) & 1u) ? 0.0f : bv;
   }
 }
 
-// wor_pass over NC chunks with the node's cache: the draft row's loads of
-// every chunk are in flight together, and one block reduction serves the
-// pass.  The totals are formed as in wor_pass, so the results are the same
-// values.
-template <int DT, int NC, bool WANT_E>
-__device__ double wor_pass_c(const WorDist& d, int V, float lam, const int* ex_tok,
-                             const float* ex_lam, int nex, int t_cur, const float* s_a,
-                             double* s_mass, double* s_red, double* E) {
-  constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV;
-  const int tix = opaque_tid();
-  StopVec<DT> r[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int e0 = c * kChunk + tix * kPerThread;
-#pragma unroll
-    for (int j = 0; j < StopVec<DT>::NV; ++j) {
-      const int ej = e0 + j * EPV;
-      r[c].q[j] = *(const uint4*)(d.yrow + (ej < V ? (long long)ej * ES : 0));
-    }
-  }
-  // the chunks in which an excluded token (or t_cur) falls among this
-  // thread's elements: one scan of the list per pass
+// The chunks in which an excluded token (or t_cur) falls among this thread's
+// elements: one scan of the list.
+__device__ __forceinline__ uint32_t wor_hits(int tix, const int* ex_tok, int nex, int t_cur) {
   uint32_t hit = 0u;
   for (int k = 0; k < nex; ++k) {
     const int t = ex_tok[k], c = t / kChunk;
     if ((t - c * kChunk) / kPerThread == tix) hit |= 1u << c;
   }
-  if (WANT_E && t_cur >= 0) {
+  if (t_cur >= 0) {
     const int c = t_cur / kChunk;
     if ((t_cur - c * kChunk) / kPerThread == tix) hit |= 1u << c;
   }
-  double v[NC + 1], e_acc = 0.0;
+  return hit;
+}
+
+// G (and E) of one pass from the cache: one block reduction of two values.
+template <int NC, bool WANT_E>
+__device__ __forceinline__ double wor_total_r(const float* s_a, const float (&rb)[NC * kPerThread],
+                                              float lam, const int* ex_tok, const float* ex_lam,
+                                              int nex, int t_cur, double* s_red, double* E) {
+  const int tix = opaque_tid();
+  const uint32_t hit = wor_hits(tix, ex_tok, nex, WANT_E ? t_cur : -1);
+  double v[2] = {0.0, 0.0};
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float w[kPerThread], be[kPerThread];
-    wor_weights_c<DT, WANT_E>(d, V, c, tix, ((hit >> c) & 1u) != 0u, r[c], s_a, lam, ex_tok,
-                              ex_lam, nex, t_cur, w, be);
-    v[c] = thread_total(w);
-    if (WANT_E) e_acc += thread_total(be);
-    // one chunk's values live at a time
-    __builtin_amdgcn_sched_barrier(0);
+    wor_chunk_r<NC, WANT_E>(s_a, rb, c, tix, ((hit >> c) & 1u) != 0u, lam, ex_tok, ex_lam, nex,
+                            t_cur, w, be);
+    v[0] += thread_total(w);
+    if (WANT_E) v[1] += thread_total(be);
   }
-  v[NC] = e_acc;
-  double t[NC + 1];
-  block_totals<NC + 1>(v, s_red, t);
+  double t[2];
+  block_totals<2>(v, s_red, t);
+  if (WANT_E) *E = t[1];
+  return t[0];
+}
+
+// The chunk masses of the current weights into s_mass (formed as the draw's
+// block scan forms its total); returns their sum.
+template <int NC>
+__device__ __forceinline__ double wor_masses_r(const float* s_a, const float (&rb)[NC * kPerThread],
+                                               float lam, const int* ex_tok, const float* ex_lam,
+                                               int nex, double* s_mass, double* s_red) {
+  const int tix = opaque_tid();
+  const uint32_t hit = wor_hits(tix, ex_tok, nex, -1);
+  double v[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float w[kPerThread], be[kPerThread];
+    wor_chunk_r<NC, false>(s_a, rb, c, tix, ((hit >> c) & 1u) != 0u, lam, ex_tok, ex_lam, nex, -1,
+                           w, be);
+    v[c] = thread_total(w);
+  }
+  double t[NC];
+  block_totals<NC>(v, s_red, t);
   double G = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     G += t[c];
     if (threadIdx.x == 0) s_mass[c] = t[c];
   }
-  if (WANT_E) *E = t[NC];
   return G;
+}
+
+// A node's first pass: fills the cache (a into LDS, b into registers) and
+// forms the pass's G (and E) from the same values, two chunks' loads of both
+// rows in flight at a time.  No token is excluded yet at a node's first pass.
+template <int DT, int NC, bool WANT_E>
+__device__ __forceinline__ double wor_fill_total(const WorDist& d, int V, float* s_a,
+                                                 float (&rb)[NC * kPerThread], float lam,
+                                                 int t_cur, double* s_red, double* E) {
+  constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV, NV = StopVec<DT>::NV;
+  constexpr int kGroup = 2;
+  const int tix = opaque_tid();
+  double v[2] = {0.0, 0.0};
+#pragma unroll
+  for (int g0 = 0; g0 < NC; g0 += kGroup) {
+    uint4 rx[kGroup][NV], ry[kGroup][NV];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const int c = g0 + k < NC ? g0 + k : NC - 1;
+      const int e0 = c * kChunk + tix * kPerThread;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int ej = e0 + j * EPV;
+        const long long off = ej < V ? (long long)ej * ES : 0;
+        rx[k][j] = *(const uint4*)(d.xrow + off);
+        ry[k][j] = *(const uint4*)(d.yrow + off);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const int c = g0 + k;
+      if (c >= NC) break;
+      const int e0 = c * kChunk + tix * kPerThread;
+      float xp[kPerThread], xq[kPerThread], av[kPerThread], w[kPerThread], be[kPerThread];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const uint32_t rw[4] = {rx[k][j].x, rx[k][j].y, rx[k][j].z, rx[k][j].w};
+        const uint32_t sw[4] = {ry[k][j].x, ry[k][j].y, ry[k][j].z, ry[k][j].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if (DT == 1) {
+            xp[j * 8 + 2 * h] = bf16_lo(rw[h]);
+            xp[j * 8 + 2 * h + 1] = bf16_hi(rw[h]);
+            xq[j * 8 + 2 * h] = bf16_lo(sw[h]);
+            xq[j * 8 + 2 * h + 1] = bf16_hi(sw[h]);
+          } else {
+            xp[j * EPV + h] = __uint_as_float(rw[h]);
+            xq[j * EPV + h] = __uint_as_float(sw[h]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        const int idx = e0 + e;
+        const float a = fmaf(exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)), d.p_inv_s,
+                             idx == d.p_amax ? 1.0f : 0.0f);
+        const float b = fmaf(exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)), d.q_inv_s,
+                             idx == d.q_amax ? 1.0f : 0.0f);
+        av[e] = idx < V ? a : 0.0f;
+        const float bv = idx < V ? b : 0.0f;
+        rb[c * kPerThread + e] = bv;
+        w[e] = fmaxf(fmaf(-lam, bv, av[e]), 0.0f);
+        if (WANT_E) be[e] = idx == t_cur ? 0.0f : bv;
+      }
+      float4* ca = (float4*)(s_a + e0);
+      ca[0] = make_float4(av[0], av[1], av[2], av[3]);
+      ca[1] = make_float4(av[4], av[5], av[6], av[7]);
+      v[0] += thread_total(w);
+      if (WANT_E) v[1] += thread_total(be);
+    }
+  }
+  double t[2];
+  block_totals<2>(v, s_red, t);
+  if (WANT_E) *E = t[1];
+  return t[0];
 }
 
 template <int DT, bool VEC, int NC>
@@ -674,6 +691,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   __shared__ int s_rowok[kMaxNodes], s_qrowok[kMaxNodes];
   __shared__ double s_pa[kMaxNodes], s_qb[kMaxNodes], s_uacc[kMaxNodes];
   __shared__ double s_cm[kMaxNodes * (NC ? NC : kMaxChunks)];  // p's mass per (node, chunk)
+
   __shared__ __attribute__((aligned(16))) float s_a[NC ? NC * kChunk : 4];   // a(v) of cached_node
   __shared__ int s_ex_tok[kMaxNodes];              // tokens of the rejected siblings
   __shared__ float s_ex_lamf[kMaxNodes];           // their lambda (weights)
@@ -806,19 +824,21 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   double lam = 0.0;
   int nex = 0;
   bool have_masses = false;   // s_mass holds the masses of the current weights
-  int cached_node = -1;       // the node whose a(v) s_a holds (NC > 0)
-  // One pass at this node: wor_pass, or with the cache (filled at the
-  // node's first pass) wor_pass_c.
+  int cached_node = -1;       // the node whose a(v), b(v) s_a, reg_b hold (NC > 0)
+  float reg_b[NC ? NC * kPerThread : 1];   // b(v) of cached_node
+  // One pass at this node: wor_pass, or from the registers (filled at the
+  // node's first pass) wor_pass_r.
   auto pass = [&](bool want_e, float lamf, int t_cur, double* E) -> double {
     if constexpr (NC > 0) {
       if (cached_node != node) {
-        wor_fill<DT, NC>(d, V, s_a);
         cached_node = node;
+        return want_e ? wor_fill_total<DT, NC, true>(d, V, s_a, reg_b, lamf, t_cur, s_red, E)
+                      : wor_fill_total<DT, NC, false>(d, V, s_a, reg_b, lamf, -1, s_red, E);
       }
-      return want_e ? wor_pass_c<DT, NC, true>(d, V, lamf, s_ex_tok, s_ex_lamf, nex, t_cur, s_a,
-                                               s_mass, s_red, E)
-                    : wor_pass_c<DT, NC, false>(d, V, lamf, s_ex_tok, s_ex_lamf, nex, t_cur, s_a,
-                                                s_mass, s_red, E);
+      return want_e ? wor_total_r<NC, true>(s_a, reg_b, lamf, s_ex_tok, s_ex_lamf, nex, t_cur,
+                                            s_red, E)
+                    : wor_total_r<NC, false>(s_a, reg_b, lamf, s_ex_tok, s_ex_lamf, nex, t_cur,
+                                             s_red, E);
     } else {
       return want_e ? wor_pass<DT, VEC, true>(d, V, nc, lamf, s_ex_tok, s_ex_lamf, nex, t_cur,
                                               s_mass, s_red, E)
@@ -911,9 +931,15 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     if (!kids) {
       // leaf: bonus draw from p
       if (tid < nc) s_mass[tid] = s_cm[stop * nc + tid];
-    } else if (!have_masses) {
-      // the last rejection left p_j as it was: masses of its weights
-      pass(false, lam_f32(lam), -1, nullptr);
+    } else {
+      if constexpr (NC > 0) {
+        // every child rejected: the chunk masses of the current weights,
+        // from the node's cache (its passes formed totals only)
+        wor_masses_r<NC>(s_a, reg_b, lam_f32(lam), s_ex_tok, s_ex_lamf, nex, s_mass, s_red);
+      } else {
+        // the last rejection left p_j as it was: masses of its weights
+        if (!have_masses) pass(false, lam_f32(lam), -1, nullptr);
+      }
     }
     __syncthreads();
     double R = 0.0;

@@ -8,7 +8,8 @@ resource remarks for gfx950 (CPU only: device code is compiled, nothing runs).
 - Draft top-k rows re-read from memory are built for 8 waves per SIMD (two
   1024-thread rows per compute unit); the register-resident variant keeps its
   registers.
-- No hot kernel spills registers, apart from the re-reading top-k variant.
+- No hot kernel spills registers, apart from the re-reading top-k variant and a
+  few prologue values of the SAMPLED_WOR walk with its 4-chunk cache.
 """
 
 import os
@@ -69,7 +70,13 @@ def test_streaming_stats_and_finish_passes_do_not_spill():
                         ("sv_tree.hip", "_ZN2sv11tree_kernel"), ("sv_tree.hip", "_ZN2sv15tree_wor_kernel"),
                         ("sv_kv.hip", "_ZN2sv16kv_commit_kernel")):
         for name, r in kernels(src, prefix).items():
-            assert r["spill"] == 0, (name, r)
+            if name.startswith("_ZN2sv15tree_wor_kernel") and name.endswith("Li4EEEvNS_8TreeArgsE"):
+                # the SAMPLED_WOR walk with a 4-chunk cache keeps 32 draft terms per
+                # thread in registers at the 128-VGPR limit of a 1024-thread work
+                # item; a few prologue values spill (three dwords reloaded per pass)
+                assert r["spill"] <= 16, (name, r)
+            else:
+                assert r["spill"] == 0, (name, r)
 
 
 def test_attention_two_waves_per_simd():
