@@ -339,7 +339,7 @@ def dominant_kernel(wl):
     """The kernel whose duration the roofline reports: the vocabulary pass, which
     for linear calls of one round of (row, chunk) work items is its by-chunk form."""
     return {"attn_tree": "attn_kernel", "kv_commit": "kv_commit_kernel",
-            "draft_topk": "draft_topk_kernel", "tree_prune": "tree_prune_kernel",
+            "draft_topk": "draft_topk_small_kernel", "tree_prune": "tree_prune_kernel",
             "linear_v32k": "stats_kernel_by_chunk",
             "linear_v1000": "stats_kernel_by_chunk",
             "telemetry": "telemetry_linear_kernel",
@@ -673,35 +673,40 @@ def main():
         wall = time.perf_counter() - t0
     # Dominant kernel's duration: the same K steps again, each with a pair of
     # HIP events attached to that kernel's dispatch on the call's stream.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     hooked = wl not in ("draft_topk", "tree_prune", "telemetry", "telemetry_tree",
                         "gamma_update")
-    for i in range(args.steps):
+    # One kernel per step: a pair of events around GROUP calls in a row on the
+    # current stream, divided by GROUP, so that the events' own fixed cost
+    # (a few microseconds) is not charged to each launch of a short kernel.
+    group = 1 if hooked else max(1, min(10, args.steps))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps // group)]
+    for i, ev in enumerate(evs):
         if hooked:
-            step(args.warmup + i, evs[i])
+            step(args.warmup + i, ev)
         else:
-            # one kernel per step: events around the call on the current stream
-            evs[i][0].record()
-            step(args.warmup + i)
-            evs[i][1].record()
+            ev[0].record()
+            for j in range(group):
+                step(args.warmup + i * group + j)
+            ev[1].record()
     torch.cuda.synchronize()
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = [a.elapsed_time(b) / group for a, b in evs]
     avg_kern_s = float(np.mean(kern_ms)) / 1e3
     ms_per_step = wall * 1e3 / args.steps
     # Hot cache, labelled as such: the same input copy every call, so inputs
     # that fit the 256 MB Infinity Cache come largely from it.
     hot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(min(args.steps, 50))]
+           for _ in range(max(1, min(args.steps, 50) // group))]
     for ev in hot:
         if hooked:
             step(0, ev)
         else:
             ev[0].record()
-            step(0)
+            for _ in range(group):
+                step(0)
             ev[1].record()
     torch.cuda.synchronize()
-    hot_ms = [a.elapsed_time(b) for a, b in hot]
+    hot_ms = [a.elapsed_time(b) / group for a, b in hot]
 
     achieved = alg_bytes / avg_kern_s / 1e9
     traffic = load_traffic(args.traffic_json, wl, kernel_source_sig(wl))

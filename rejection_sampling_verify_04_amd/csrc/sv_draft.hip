@@ -537,6 +537,206 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
   }
 }
 
+// Small top-k (k <= 4) of bf16 rows of up to 32768 logits, aligned: one work
+// item of 256 threads per row, so that four rows share a compute unit
+// and their loads and ALU work overlap.  Each thread keeps its 16 vectors
+// (128 logits) packed in registers.  L, the k-th largest of the four waves'
+// maxima, bounds the top k from below; the logits >= L are gathered and
+// ranked (larger value first, lower id on ties).  More than kTopkCand of
+// them (ties at the top) take k rounds of a block-wide argmax instead.  The
+// softmax normaliser is formed online in the same pass as the maximum, so
+// each vector is reduced as it arrives.
+constexpr int kTopkSmallThreads = 256;
+constexpr int kTopkSmallWaves = kTopkSmallThreads / 64;
+constexpr int kTopkSmallVecs = 16;                     // 16-byte vectors per thread
+constexpr int kTopkSmallK = kTopkSmallWaves;           // k <= the waves' count
+constexpr int kTopkSmallMaxV = kTopkSmallVecs * kTopkSmallThreads * 8;
+
+__global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
+    const void* logits, int V, int k, const float* temp, int* tokens, float* logprob) {
+  __shared__ float s_wm[kTopkSmallWaves], s_wc[kTopkSmallWaves];
+  __shared__ double s_ws[kTopkSmallWaves];
+  __shared__ double s_scan[kTopkSmallWaves];
+  __shared__ unsigned long long s_wk[kTopkSmallWaves];
+  __shared__ unsigned long long s_top[kTopkSmallK];
+  __shared__ float s_cval[kTopkCand];
+  __shared__ int s_cidx[kTopkCand];
+
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const char* row = (const char*)logits + (long long)r * V * 2;
+  // every load is issued before anything waits: the temperature as a scalar
+  const float T = temp ? load_uniform_f32(temp + r) : 1.0f;
+  u32x4_t raw[kTopkSmallVecs];
+#pragma unroll
+  for (int j = 0; j < kTopkSmallVecs; ++j) {
+    const int vj = tid + j * kTopkSmallThreads;
+    raw[j] = __builtin_nontemporal_load((const u32x4_t*)(row + (long long)(vj * 8 < V ? vj : 0) * 16));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (!temp_ok(T)) {   // reported as token -1 and a NaN log-probability
+    if (tid < k) {
+      tokens[(long long)r * k + tid] = -1;
+      logprob[(long long)r * k + tid] = __builtin_nanf("");
+    }
+    return;
+  }
+  const bool greedy = T == 0.0f;
+  const float k2 = greedy ? 0.0f : log2e_over_t(T);
+  // logit h of vector j: element (tid + 256 j) 8 + h
+  auto val = [&](int j, int h) -> float {
+    const int q = h >> 1;
+    const uint32_t word = q == 0 ? raw[j].x : (q == 1 ? raw[j].y : (q == 2 ? raw[j].z : raw[j].w));
+    return (h & 1) ? bf16_hi(word) : bf16_lo(word);
+  };
+  auto valid = [&](int j) { return (tid + j * kTopkSmallThreads) * 8 < V; };
+  auto index = [&](int j, int h) { return (tid + j * kTopkSmallThreads) * 8 + h; };
+  // the packed words as values the compiler cannot reuse across phases: each
+  // phase unpacks them again (one operation per logit) instead of keeping
+  // 128 unpacked floats live
+  auto fence_raw = [&]() {
+#pragma unroll
+    for (int j = 0; j < kTopkSmallVecs; ++j) asm volatile("" : "+v"(raw[j]));
+  };
+
+  // One pass as the vectors arrive (loads complete in issue order): the row
+  // maximum and, online, the softmax normaliser: a running integer offset
+  // c = ceil(max x k2) and the sum of 2^(x k2 - c), eight terms pairwise in
+  // float32 and then in float64, rescaled by exact powers of two when c grows.
+  // No branch in this loop: a load whose value crosses a branch join is
+  // waited for at the join, which would make the first vector wait for all
+  // of them.  Vectors past V read as -inf; a greedy row (k2 = 0) forms its
+  // offsets with k2 = 1 and never reads the sum.
+  const float kc = greedy ? 1.0f : k2;
+  float m = -__builtin_huge_valf(), c = -__builtin_huge_valf();
+  double sacc = 0.0;
+#pragma unroll
+  for (int j = 0; j < kTopkSmallVecs; ++j) {
+    const bool vj = valid(j);
+    float xv[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) xv[h] = vj ? val(j, h) : -__builtin_huge_valf();
+    float mj = xv[0];
+#pragma unroll
+    for (int h = 1; h < 8; ++h) mj = fmaxf(mj, xv[h]);
+    m = fmaxf(m, mj);
+    const float cn = fmaxf(c, ceilf(mj * kc));
+    sacc = sacc != 0.0 ? scale_pow2(sacc, c - cn) : 0.0;
+    c = cn;
+    const float cu = c > -__builtin_huge_valf() ? c : 0.0f;   // all -inf so far: terms are 0
+    float t[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) t[h] = exp2_hw(fmaf(xv[h], kc, -cu));
+#pragma unroll
+    for (int w2 = 4; w2 >= 1; w2 >>= 1) {
+#pragma unroll
+      for (int h = 0; h < w2; ++h) t[h] = t[2 * h] + t[2 * h + 1];
+    }
+    sacc += (double)t[0];
+  }
+  fence_raw();
+  // the waves' maxima and normalisers (sums brought to the wave's offset)
+  const float cw = wave_max(c);
+  const double sw = wave_sum(sacc != 0.0 ? scale_pow2(sacc, c - cw) : 0.0);
+  m = wave_max(m);
+  if (lane == 0) {
+    s_wm[wave] = m;
+    s_wc[wave] = cw;
+    s_ws[wave] = sw;
+  }
+  __syncthreads();
+  // L: the largest wave maximum with at least k wave maxima at or above it
+  const float mw = lane < kTopkSmallWaves ? s_wm[lane] : -__builtin_huge_valf();
+  int ge = 0;
+#pragma unroll
+  for (int j = 0; j < kTopkSmallWaves; ++j)
+    ge += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), j)) >= mw;
+  const float L = wave_max((lane < kTopkSmallWaves && ge >= k) ? mw : -__builtin_huge_valf());
+  // the row's normaliser: sum_v 2^(x_v k2 - c_row)
+  float c_row = s_wc[0];
+#pragma unroll
+  for (int w = 1; w < kTopkSmallWaves; ++w) c_row = fmaxf(c_row, s_wc[w]);
+  double S = 0.0;
+#pragma unroll
+  for (int w = 0; w < kTopkSmallWaves; ++w)
+    S += s_ws[w] != 0.0 ? scale_pow2(s_ws[w], s_wc[w] - c_row) : 0.0;
+  // the rank-th output: token and log softmax(x / T) = (x k2 - c_row) ln 2 - ln S
+  auto write_out = [&](int rank, float x, int idx) {
+    double lp;
+    if (greedy) lp = rank == 0 ? 0.0 : -__builtin_huge_val();
+    else lp = ((double)x * (double)k2 - (double)c_row) * (1.0 / kLog2e) - log(S);
+    tokens[(long long)r * k + rank] = idx;
+    logprob[(long long)r * k + rank] = (float)lp;
+  };
+
+  // the logits >= L
+  uint32_t n_cand = 0u;
+#pragma unroll
+  for (int j = 0; j < kTopkSmallVecs; ++j) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) n_cand += (valid(j) && val(j, h) >= L) ? 1u : 0u;
+  }
+  fence_raw();
+  double c_tot;
+  const uint32_t c_pos =
+      (uint32_t)block_exclusive_scan<kTopkSmallWaves>((double)n_cand, s_scan, &c_tot);
+  const int C = (int)c_tot;
+  if (C <= kTopkCand) {
+    uint32_t at = c_pos;
+#pragma unroll
+    for (int j = 0; j < kTopkSmallVecs; ++j) {
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const float x = val(j, h);
+        if (valid(j) && x >= L) {
+          s_cval[at] = x;
+          s_cidx[at] = index(j, h);
+          ++at;
+        }
+      }
+    }
+    __syncthreads();
+    // rank: larger value first, lower id on ties (values compare -0 == +0)
+    for (int i = tid; i < C; i += kTopkSmallThreads) {
+      const float x = s_cval[i];
+      const int idx = s_cidx[i];
+      int rank = 0;
+      for (int j = 0; j < C; ++j) {
+        const float xj = s_cval[j];
+        rank += xj > x || (xj == x && s_cidx[j] < idx);
+      }
+      if (rank < k) write_out(rank, x, idx);
+    }
+    return;
+  }
+  // More than kTopkCand logits tie at the top: k rounds of a block-wide
+  // argmax over the row, read again from memory (this path is rare), each
+  // below the previous winner, on keys (order key of the value, then the
+  // complement of the index: lower id wins a tie).
+  const RowKeys<1> key_at{row};
+  unsigned long long below = ~0ull;
+  for (int i = 0; i < k; ++i) {
+    unsigned long long best = 0ull;
+    for (int v = tid; v < V; v += kTopkSmallThreads) {
+      const unsigned long long key =
+          ((unsigned long long)key_at(v) << 32) | (0xFFFFFFFFu - (uint32_t)v);
+      if (key < below && key > best) best = key;
+    }
+    best = wave_max_u64(best);
+    if (lane == 0) s_wk[wave] = best;
+    __syncthreads();
+    unsigned long long b = s_wk[0];
+#pragma unroll
+    for (int w = 1; w < kTopkSmallWaves; ++w) b = s_wk[w] > b ? s_wk[w] : b;
+    if (tid == 0) s_top[i] = b;
+    below = b;
+    __syncthreads();
+  }
+  if (tid < k) {
+    const unsigned long long b = s_top[tid];
+    write_out(tid, value_of_key<1>((uint32_t)(b >> 32)), (int)(0xFFFFFFFFu - (uint32_t)b));
+  }
+}
+
 hipError_t launch_draft_topk(int dtype, const void* logits, int R, int V, int k, const float* temp,
                              int* tokens, float* logprob, hipStream_t st) {
   const int es = dtype == 1 ? 2 : 4;
@@ -544,6 +744,11 @@ hipError_t launch_draft_topk(int dtype, const void* logits, int R, int V, int k,
   // keys in registers: aligned rows of up to 4 vectors per thread
   const bool reg = vec_ok && (long long)V * es <= (long long)kTopkRegVecs * kFinThreads * 16;
   const dim3 grid((unsigned)R), block(kFinThreads);
+  if (dtype == 1 && vec_ok && V <= kTopkSmallMaxV && k <= kTopkSmallK) {
+    draft_topk_small_kernel<<<grid, dim3(kTopkSmallThreads), 0, st>>>(logits, V, k, temp, tokens,
+                                                                      logprob);
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     if (reg) draft_topk_kernel<1, true><<<grid, block, 0, st>>>(logits, V, k, temp, tokens, logprob);
     else draft_topk_kernel<1, false><<<grid, block, 0, st>>>(logits, V, k, temp, tokens, logprob);

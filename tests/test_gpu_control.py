@@ -122,6 +122,45 @@ def test_draft_topk_matches_oracle(dtype, V, R, k):
     say("[control] draft top-k dtype=%d V=%d R=%d k=%d ok" % (dtype, V, R, k))
 
 
+@pytest.mark.parametrize("V", [8, 1000, 8192, 32000, 32768])
+def test_draft_topk_small_k_path(V):
+    """k <= 4 over aligned bf16 rows of up to 32768 logits (one 256-thread work
+    item per row): every k, greedy, sampled and invalid temperatures, ties at
+    the k-th place, -inf logits, signed zeros, and more than 1024 logits tied
+    at the top (the argmax rounds)."""
+    import rejection_sampling_verify_04_amd as sv
+    rng = np.random.default_rng(106 + V)
+    R = 24
+    x = rng.normal(0, 2, size=(R, V)).astype(np.float32)
+    x[1, :] = 0.25                                           # all equal
+    x[2, rng.choice(V, min(V, 1500), replace=False)] = 7.0   # many maxima (> 1024 when V allows)
+    x[3, :] = -np.inf
+    x[3, rng.choice(V, 3, replace=False)] = [1.0, 2.0, 1.0]  # three finite logits
+    x[4, : min(V, 6)] = 9.0                                  # ties at the top, in index order
+    zeros = rng.choice(V, min(V, 40), replace=False)
+    x[5, zeros] = np.where(rng.random(len(zeros)) < 0.5, np.float32(-0.0), np.float32(0.0))
+    x[5, np.setdiff1d(np.arange(V), zeros)] = -1.0           # signed zeros on top
+    x[6] = np.round(x[6] * 2) / 2                            # coarse values: ties everywhere
+    bits = synth.bf16_bits(x)
+    vals = synth.bf16_values(bits).astype(np.float64)
+    T = rng.choice([1.0, 0.7, 1.3, 0.0], size=R).astype(np.float32)
+    T[7] = np.nan                                            # invalid: tokens -1, NaN log-probs
+    T[8] = -1.0
+    for k in (1, 2, 3, 4):
+        tok, lp = sv.draft_topk(logits_to_dev(bits, 1), k, temp=f32(T))
+        tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
+        for r in range(R):
+            if r in (7, 8):
+                assert np.all(tok[r] == -1) and np.all(np.isnan(lp[r])), (k, r)
+                continue
+            rt, rl = OD.topk_candidates(vals[r], k, float(T[r]))
+            assert np.array_equal(tok[r], rt), (V, k, r, tok[r], rt)
+            fin = np.isfinite(rl)
+            assert np.array_equal(np.isfinite(lp[r]), fin), (V, k, r, lp[r], rl)
+            assert np.all(np.abs(lp[r][fin] - rl[fin]) <= 1e-5 * np.maximum(1.0, np.abs(rl[fin])))
+    say("[control] draft top-k, small-k path V=%d ok" % V)
+
+
 def test_draft_topk_heavy_ties():
     """Rows whose top values repeat far more often than k (the whole-row path)."""
     import rejection_sampling_verify_04_amd as sv

@@ -7,7 +7,7 @@ resource remarks for gfx950 (CPU only: device code is compiled, nothing runs).
 - The attention kernel is built for 2 waves per SIMD (its K/V prefetch depth).
 - Draft top-k rows re-read from memory are built for 8 waves per SIMD (two
   1024-thread rows per compute unit); the register-resident variant keeps its
-  registers.
+  registers; the small-k variant runs four 256-thread rows per compute unit.
 - No hot kernel spills registers, apart from the re-reading top-k variant and a
   few prologue values of the SAMPLED_WOR walk with its 4-chunk cache.
 """
@@ -82,6 +82,13 @@ def test_streaming_stats_and_finish_passes_do_not_spill():
 def test_attention_two_waves_per_simd():
     for name, r in kernels("sv_attn.hip", "_ZN2sv11attn_kernel").items():
         assert r["occ"] == 2 and r["spill"] == 0, (name, r)
+
+
+def test_draft_topk_small_k_four_rows_per_cu():
+    """The small-k top-k keeps a row's 128 logits per thread packed in registers
+    and runs four 256-thread rows per compute unit."""
+    for name, r in kernels("sv_draft.hip", "_ZN2sv23draft_topk_small_kernel").items():
+        assert r["occ"] >= 4 and r["spill"] == 0, (name, r)
 
 
 def test_draft_topk_variants():
