@@ -378,7 +378,9 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
   __shared__ __align__(16) int s_par[kPruneMax];
   __shared__ int s_depth[kPruneMax], s_rank[kPruneMax], s_new[kPruneMax];
   __shared__ __align__(16) double s_cum[kPruneMax];
-  __shared__ int s_keep[kPruneMax];
+  __shared__ int s_before[kPruneMax];   // candidates ahead in the keep order
+  __shared__ int s_cnt[kPruneMax], s_off[kPruneMax], s_cur[kPruneMax], s_list[kPruneMax];
+  static_assert(kFinThreads == kPruneMax, "one thread per candidate and per parent slot");
   __shared__ int s_klist[64];
   __shared__ __align__(16) uint32_t s_tie[kPruneMax];
   __shared__ double s_scan[kFinWaves];
@@ -405,24 +407,26 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
   }
   __syncthreads();
   const bool bad = s_bad != 0;
-  // depth (walk to the root) and rank among the siblings
+  // Each parent's children (slot par + 1; -1 is the roots' parent), listed
+  // in no particular order: counts by LDS atomics, offsets by a block scan,
+  // then slots taken through per-parent cursors.
+  s_cnt[tid] = 0;
+  s_cur[tid] = 0;
+  __syncthreads();
+  if (mine && !bad) atomicAdd(&s_cnt[par + 1], 1);
+  __syncthreads();
+  double n_tot;
+  s_off[tid] = (int)block_exclusive_scan<kFinWaves>((double)s_cnt[tid], s_scan, &n_tot);
+  __syncthreads();
+  if (mine && !bad) s_list[s_off[par + 1] + atomicAdd(&s_cur[par + 1], 1)] = i;
+  __syncthreads();
+  // depth (walk to the root) and rank among the siblings (the siblings of
+  // smaller index, from the parent's list)
   int depth = 0, rank = 0;
   if (mine && !bad) {
     for (int x = i; x >= 0; x = s_par[x]) ++depth;
-    // earlier siblings: sixteen parents per step in four 16-byte LDS reads,
-    // branch-free (entries at or past i never count)
-    const int4* p4 = (const int4*)s_par;
-    for (int j = 0; j < i; j += 16) {
-      int4 q[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = p4[(j >> 2) + u];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int jj = j + 4 * u;
-        rank += (jj < i && q[u].x == par) + (jj + 1 < i && q[u].y == par) +
-                (jj + 2 < i && q[u].z == par) + (jj + 3 < i && q[u].w == par);
-      }
-    }
+    const int o = s_off[par + 1], n = s_cnt[par + 1];
+    for (int k = 0; k < n; ++k) rank += s_list[o + k] < i;
     s_depth[i] = depth;
     s_rank[i] = rank;
   }
@@ -445,33 +449,48 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
   // place in the keep order; kept if finite and among the first n_max - 1.
   // The tie order (depth, parent, rank) packs into one word: 11, 11, 10 bits.
   if (mine && !bad) s_tie[i] = ((uint32_t)depth << 21) | ((uint32_t)(par + 1) << 10) | (uint32_t)rank;
-  if (i >= C && i < ((C + 7) & ~7)) {   // the pad entries read by the eight-wide loop
+  const int C8 = (C + 7) & ~7;
+  if (i >= C && i < C8) {   // the pad entries read by the eight-wide loop
     s_cum[i] = -__builtin_huge_val();
     s_tie[i] = 0xFFFFFFFFu;
+  }
+  if (i < C) s_before[i] = 0;
+  __syncthreads();
+  // The candidates ahead of each one, counted by G groups of threads (as
+  // many as the block holds, each share at least eight wide), each over its
+  // share of the candidates; the shares are summed by LDS atomics.
+  if (!bad && C > 0) {
+    const int G = max(1, min(kFinThreads / C, C8 / 8));
+    const int S = ((C8 + 8 * G - 1) / (8 * G)) * 8;
+    const int ci = tid % C, g = tid / C;
+    if (g < G) {
+      const double cum_c = s_cum[ci];
+      const uint32_t tie = s_tie[ci];
+      int before = 0;
+      // eight candidates per step, all loads unconditional (the arrays are
+      // padded past C with entries that never count: -inf and the largest tie)
+      const int j1 = min(g * S + S, C8);
+      for (int j = g * S; j < j1; j += 8) {
+        double2 c2[4];
+        uint2 t2[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          c2[u] = ((const double2*)s_cum)[(j >> 1) + u];
+          t2[u] = ((const uint2*)s_tie)[(j >> 1) + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          before += (c2[u].x > cum_c) | ((c2[u].x == cum_c) & (t2[u].x < tie));
+          before += (c2[u].y > cum_c) | ((c2[u].y == cum_c) & (t2[u].y < tie));
+        }
+      }
+      if (before) atomicAdd(&s_before[ci], before);
+    }
   }
   __syncthreads();
   int keep = 0;
   if (mine && !bad) {
-    const uint32_t tie = s_tie[i];
-    int before = 0;
-    // eight candidates per step, all loads unconditional (the arrays are
-    // padded past C with entries that never count: -inf and the largest tie)
-    for (int j = 0; j < C; j += 8) {
-      double2 c2[4];
-      uint2 t2[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        c2[u] = ((const double2*)s_cum)[(j >> 1) + u];
-        t2[u] = ((const uint2*)s_tie)[(j >> 1) + u];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        before += (c2[u].x > cum) | ((c2[u].x == cum) & (t2[u].x < tie));
-        before += (c2[u].y > cum) | ((c2[u].y == cum) & (t2[u].y < tie));
-      }
-    }
-    keep = cum > -__builtin_huge_val() && before < a.n_max - 1;
-    s_keep[i] = keep;
+    keep = cum > -__builtin_huge_val() && s_before[i] < a.n_max - 1;
     s_new[i] = -1;
   }
   __syncthreads();
@@ -496,8 +515,11 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
       // counts
       const int np = pq < 0 ? 0 : (here ? s_new[pq] : 0);
       const uint32_t key = here ? ((uint32_t)np << 10) | (uint32_t)rq : 0xFFFFFFFFu;
+      // every lane, unrolled: a lane not at this level holds a key that
+      // never counts
       int pos = 0;
-      for (int j = 0; j < K; ++j) pos += (uint32_t)__builtin_amdgcn_readlane((int)key, j) < key;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) pos += (uint32_t)__builtin_amdgcn_readlane((int)key, j) < key;
       const int n_here = __popcll(__ballot(here));
       if (here) s_new[ci] = base + pos;
       base += n_here;

@@ -266,6 +266,36 @@ def test_tree_prune_matches_oracle():
     assert out["n_nodes"].cpu().numpy()[2] == 0
 
 
+def test_tree_prune_ties_at_limit():
+    """1024 candidates (the limit: one thread group counts each), and forests
+    of 40 and 130 (several groups share each count), whose log q come from
+    three values, so that exact ties in the cumulative log-probability are
+    common and the tie order (depth, parent, rank) decides the kept set."""
+    import rejection_sampling_verify_04_amd as sv
+    rng = np.random.default_rng(107)
+    C = 1024
+    par = np.array([-1] * 4 + [(i - 4) // 4 for i in range(4, C)], dtype=np.int32)
+    B = 3
+    pars = np.tile(par, (B, 1))
+    tok = rng.integers(0, 32000, size=(B, C)).astype(np.int32)
+    lq = rng.choice(np.array([-0.5, -1.0, -1.5], dtype=np.float32), size=(B, C))
+    n_cand = np.array([C, 40, 130], dtype=np.int32)
+    for n_max in (8, 33, 64):
+        out = sv.tree_prune(i32(pars), i32(tok), f32(lq), n_max, tau=0.2, n_cand=i32(n_cand))
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+        for b in range(B):
+            c = int(n_cand[b])
+            rp, rt, rc, rpass = OD.prune_tree(pars[b, :c], tok[b, :c], lq[b, :c].astype(np.float64),
+                                              n_max, 0.2)
+            n = len(rp)
+            assert got["n_nodes"][b] == n, (n_max, b)
+            assert np.array_equal(got["parents"][b, :n], rp), (n_max, b)
+            assert np.array_equal(got["tokens"][b, :n], rt), (n_max, b)
+            assert np.array_equal(got["cum_logprob"][b, :n], rc.astype(np.float32)), (n_max, b)
+            assert got["n_pass"][b] == rpass, (n_max, b)
+    say("[control] prune with ties at 1024, 40 and 130 candidates ok")
+
+
 def test_drafting_full_size_sampled():
     """The drafting workloads at their full size and launch shape: top-4 of
     1024 draft rows over V=32000 bf16 (every 32nd row checked), then the
