@@ -27,6 +27,14 @@ Row n of the target logits is the target distribution for the token that
 follows node n.  Node 0 is the root (the last committed token).  Node n's
 randoms are Philox position n: u_acc(n) decides node n's own acceptance,
 u_smp(n) is used for a draw made at node n.
+
+Rows read (the pages do not say what a row without a finite maximum means;
+the reading is that of the linear verify, applied to the rows the walk
+reads): the target row of every node that has children (its children are
+tested against it), in SAMPLED_WOR also that node's draft row, and, when the
+walk stops at a leaf, that leaf's target row (its bonus draw).  A row among
+them whose maximum logit is not finite makes the batch row an error row; the
+other rows are never read.
 """
 
 from dataclasses import dataclass
@@ -85,12 +93,13 @@ def verify_tree_topk_row(x, parents, node_tokens, n_nodes, temp_t, u_acc, u_smp)
     st = _check_tree(parents, node_tokens, n_nodes, V)
     if st == ROW_OK and (not np.isfinite(temp_t) or temp_t < 0):
         st = ROW_BAD_TEMP
-    if st == ROW_OK and not np.all(np.isfinite(np.max(x[:n_nodes], axis=1))):
+    inner = sorted({parents[c] for c in range(1, n_nodes)}) if st == ROW_OK else []
+    if st == ROW_OK and not all(np.isfinite(np.max(x[n])) for n in inner):
         st = ROW_NONFINITE
     if st != ROW_OK:
         return TreeRowResult(-1, path, out, p_at, st, None, False, -1, "error")
 
-    p_rows = [softmax_t(x[n], temp_t) for n in range(n_nodes)]
+    p_rows = {n: softmax_t(x[n], temp_t) for n in inner}
     for c in range(1, n_nodes):
         p_at[c] = p_rows[parents[c]][node_tokens[c]]
 
@@ -98,8 +107,15 @@ def verify_tree_topk_row(x, parents, node_tokens, n_nodes, temp_t, u_acc, u_smp)
     flagged = None
     node, depth = 0, 0
     while True:
-        p = p_rows[node]
         kids = _children(parents, n_nodes, node)
+        if not kids:
+            # a leaf: its target row is read by the bonus draw
+            if not np.isfinite(np.max(x[node])):
+                path, out, p_at = _empty(N)
+                return TreeRowResult(-1, path, out, p_at, ROW_NONFINITE, None, False, -1,
+                                     "error")
+            p_rows[node] = softmax_t(x[node], temp_t)
+        p = p_rows[node]
         removed = []
         removed_mass = 0.0
         accepted = None
@@ -151,11 +167,10 @@ def verify_tree_sampled_wor_row(x, y, parents, node_tokens, n_nodes, temp_t, tem
                          or temp_t < 0 or temp_d < 0):
         st = ROW_BAD_TEMP
     if st == ROW_OK:
-        # every distribution the walk may read must exist: the target row of
-        # each node, the draft row of each node that has children
+        # every distribution the walk's tests read must exist: the target and
+        # draft rows of each node that has children
         inner = sorted({parents[c] for c in range(1, n_nodes)})
-        if not (np.all(np.isfinite(np.max(x[:n_nodes], axis=1)))
-                and all(np.isfinite(np.max(y[n])) for n in inner)):
+        if not all(np.isfinite(np.max(x[n])) and np.isfinite(np.max(y[n])) for n in inner):
             st = ROW_NONFINITE
     if st != ROW_OK:
         return TreeRowResult(-1, path, out, p_at, st, None, False, -1, "error")
@@ -166,10 +181,14 @@ def verify_tree_sampled_wor_row(x, y, parents, node_tokens, n_nodes, temp_t, tem
     flagged = None
     node, depth = 0, 0
     while True:
-        p = softmax_t(x[node], temp_t)
-        q = softmax_t(y[node], temp_d)
         kids = _children(parents, n_nodes, node)
-        pj, qj = p.copy(), q.copy()
+        if not kids and not np.isfinite(np.max(x[node])):
+            # a leaf: its target row is read by the bonus draw
+            path, out, p_at = _empty(N)
+            return TreeRowResult(-1, path, out, p_at, ROW_NONFINITE, None, False, -1, "error")
+        p = softmax_t(x[node], temp_t)
+        q = softmax_t(y[node], temp_d) if kids else None
+        pj, qj = p.copy(), (q.copy() if kids else None)
         accepted = None
         for c in kids:
             tok = node_tokens[c]

@@ -263,7 +263,7 @@ def test_sampled_wor_error_and_warning_rows():
     assert run(x, y, [-1, 0, 3, 1], tok, 4, 1.0, 1.0, u, u).status == L.ROW_BAD_SHAPE
     assert run(x, y, par, [0, 1, 2, V], 4, 1.0, 1.0, u, u).status == L.ROW_BAD_TOKEN
     xb = x.copy()
-    xb[3] = -np.inf          # a leaf's target row is read by its bonus draw
+    xb[3] = -np.inf          # the walk (accepting 1, then 3) stops at leaf 3: its bonus draw reads it
     assert run(xb, y, par, tok, 4, 1.0, 1.0, u, u).status == L.ROW_NONFINITE
     yb = y.copy()
     yb[1] = -np.inf          # node 1 has a child, so its draft row is read
@@ -275,6 +275,45 @@ def test_sampled_wor_error_and_warning_rows():
     yq[0, 1] = -np.inf       # child token 1 impossible under the root's draft
     r = run(x, yq, par, tok, 4, 1.0, 1.0, [0.5, 0.999, 0.999, 0.999], u)
     assert r.status & L.ROW_WARN_QZERO and r.num_accepted >= 1 and r.path_nodes[0] == 1
+
+
+def test_leaf_target_rows_read_only_by_a_bonus_draw():
+    """A leaf's target row is read only when the walk stops at that leaf (its
+    bonus draw): a row without a finite maximum elsewhere among the leaves is
+    never read, in both candidate modes; an inner node's row always is."""
+    V = 6
+    x = np.zeros((4, V))
+    y = np.zeros((4, V))
+    par, tok = [-1, 0, 0, 1], [0, 1, 2, 3]
+    us = [0.5] * 4
+    to_3 = [0.5, 0.01, 0.99, 0.01]     # accept 1 (ratio 1/6), then 3: stop at leaf 3
+    to_2 = [0.5, 0.99, 0.01, 0.99]     # reject 1, accept 2 (ratio 1/5): stop at leaf 2
+    bad2 = x.copy()
+    bad2[2] = -np.inf
+    bad2n = x.copy()
+    bad2n[2, 4] = np.nan
+    for row in (bad2, bad2n):
+        r = TR.verify_tree_topk_row(row, par, tok, 4, 1.0, to_3, us)
+        assert r.status == L.ROW_OK and r.num_accepted == 2 and r.stop_node == 3
+        r = TR.verify_tree_topk_row(row, par, tok, 4, 1.0, to_2, us)
+        assert r.status == L.ROW_NONFINITE and r.num_accepted == -1
+        assert np.all(r.out_tokens == -1) and np.all(r.path_nodes == -1)
+    # SAMPLED_WOR with uniform p and q: every ratio is 1
+    wor_3 = [0.5, 0.5, 0.99, 0.5]      # accept 1, then 3
+    r = TR.verify_tree_sampled_wor_row(bad2, y, par, tok, 4, 1.0, 1.0, wor_3, us)
+    assert r.status == L.ROW_OK and r.stop_node == 3
+    r = TR.verify_tree_sampled_wor_row(bad2, y, [-1, 0, 0, 0], tok, 4, 1.0, 1.0,
+                                       [0.5, 1.5, 0.5, 0.5], us)
+    assert r.status == L.ROW_NONFINITE        # node 1 rejected, node 2 accepted: leaf 2
+    # an inner node's target row is read whatever the walk does
+    bad1 = x.copy()
+    bad1[1] = -np.inf
+    assert TR.verify_tree_topk_row(bad1, par, tok, 4, 1.0, to_2, us).status == L.ROW_NONFINITE
+    assert TR.verify_tree_sampled_wor_row(bad1, y, par, tok, 4, 1.0, 1.0, wor_3,
+                                          us).status == L.ROW_NONFINITE
+    # a tree of the root alone: the root is the leaf the walk stops at
+    r = TR.verify_tree_topk_row(bad2[2:3].repeat(4, 0), par, tok, 1, 1.0, to_3, us)
+    assert r.status == L.ROW_NONFINITE
 
 
 def test_greedy_tree_accepts_target_argmax_child():
