@@ -356,7 +356,7 @@ def kernel_source_sig(wl):
            "tree_prune": "sv_draft.hip", "telemetry": "sv_telemetry.hip",
            "telemetry_tree": "sv_telemetry.hip",
            "gamma_update": "sv_control.hip"}.get(wl, "sv_stats.hip")
-    names = [own, "sv_common.h", "sv_internal.h"]
+    names = [own, "sv_common.h", "sv_internal.h", "sv_pass.h"]
     h = hashlib.sha1()
     for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
@@ -621,8 +621,11 @@ def main():
             config = dict(workload=wl, B=Bn, nodes=N, V=d["V"],
                           mode="SAMPLED_WOR" if wor else "TOPK", input_dtype="bf16",
                           input_copies=nc)
+            # rows read by the vocabulary pass: those of the nodes with
+            # children (a leaf's row only when a walk stops there)
+            config["target_rows_read"] = synth.inner_nodes(d)
             if wor:
-                config["draft_rows_read"] = int(d["n_inner"])
+                config["draft_rows_read"] = synth.inner_nodes(d)
             unit = "verified draft nodes/s"
         alg_bytes = per_call
         flops = 0

@@ -16,6 +16,7 @@
 
 #include "sv_common.h"
 #include "sv_internal.h"
+#include "sv_pass.h"
 
 namespace sv {
 
@@ -34,73 +35,8 @@ namespace sv {
 // Offsets of sampled rows are integers (ceil of the scaled maximum), so every
 // rescale of a sum is an exact power of two.
 
-// One wave's 2048-element segment: lane l's vector j covers elements
-// seg0 + (j * 64 + l) * EPV + [0, EPV), so each load instruction of the wave
-// reads 1 KB of consecutive bytes.
-template <int DT>
-struct SegLoad {
-  static constexpr int ES = DT ? 2 : 4;          // bytes per element
-  static constexpr int EPV = 16 / ES;            // elements per 16-byte load
-  static constexpr int NV = kPerLane / EPV;      // loads per lane per segment
-  uint4 raw[NV];
-
-  // Vectors past V read as -inf.  Rows are read once here, so the loads carry
-  // the non-temporal hint.  With vectors valid (V a multiple of EPV) a vector
-  // is either wholly inside the row or wholly past it.
-  __device__ __forceinline__ void issue(const char* rowp, int V, int seg0) {
-    const int lane = threadIdx.x & 63;
-    constexpr uint32_t kNegInf = DT ? 0xff80ff80u : 0xff800000u;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int e0 = seg0 + (j * 64 + lane) * EPV;
-      if (e0 < V) {
-        const u32x4_t w =
-            __builtin_nontemporal_load((const u32x4_t*)(rowp + (long long)e0 * ES));
-        raw[j] = make_uint4(w.x, w.y, w.z, w.w);
-      } else {
-        raw[j] = make_uint4(kNegInf, kNegInf, kNegInf, kNegInf);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void unpack(float v[kPerLane]) const {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      if (DT == 1) {
-        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          v[j * 8 + 2 * h] = bf16_lo(w[h]);
-          v[j * 8 + 2 * h + 1] = bf16_hi(w[h]);
-        }
-      } else {
-        v[j * 4 + 0] = __uint_as_float(raw[j].x);
-        v[j * 4 + 1] = __uint_as_float(raw[j].y);
-        v[j * 4 + 2] = __uint_as_float(raw[j].z);
-        v[j * 4 + 3] = __uint_as_float(raw[j].w);
-      }
-    }
-  }
-};
-
-template <int DT>
-__device__ __forceinline__ void seg_load_scalar(const char* rowp, int V, int seg0,
-                                                float v[kPerLane]) {
-  constexpr int EPV = SegLoad<DT>::EPV;
-  constexpr int NV = SegLoad<DT>::NV;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-#pragma unroll
-    for (int k = 0; k < EPV; ++k) {
-      const int e = seg0 + (j * 64 + lane) * EPV + k;
-      v[j * EPV + k] = e < V ? load_logit<DT>(rowp, e) : -__builtin_huge_valf();
-    }
-  }
-}
-
 constexpr int kStatsCache = 1024;  // batch rows whose offsets/temperatures go to LDS
-constexpr int kInnerCache = 512;   // trees whose inner-node masks go to LDS (draft rows read)
+constexpr int kInnerCache = 512;   // trees whose inner-node masks go to LDS (compacted rows)
 
 // Largest j in [0, B) whose key off[j] + add * j is <= x, found by one wave
 // with 64 probes per round (B <= 64: one round; B <= 4096: two).
@@ -183,68 +119,6 @@ __device__ void gather_logits(const StatsArgs& a, int* s_off) {
   }
 }
 
-// A lane's running statistics over its elements of one chunk.
-struct LaneStats {
-  float c;     // sampled: integer log2 offset; greedy: largest value so far
-  int idx;     // greedy: first index of that value
-  double s;    // sampled: sum of 2^(x k - c)
-};
-
-// Fold one sub-segment (this lane's 32 values, in increasing index order:
-// element e of vector j sits at seg0 + (j * 64 + lane) * EPV + e).
-template <int DT>
-__device__ __forceinline__ void lane_fold(float v[kPerLane], int seg0, bool greedy, float k2,
-                                          LaneStats& st) {
-  constexpr int EPV = SegLoad<DT>::EPV;
-  constexpr int NV = SegLoad<DT>::NV;
-  const int lane = threadIdx.x & 63;
-  if (greedy) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float x = v[j * EPV + e];
-        const bool gt = x > st.c;
-        st.c = gt ? x : st.c;
-        st.idx = gt ? seg0 + (j * 64 + lane) * EPV + e : st.idx;
-      }
-    }
-    return;
-  }
-  float m = -__builtin_huge_valf();
-#pragma unroll
-  for (int e = 0; e < kPerLane; ++e) m = fmaxf(m, v[e]);
-  const float mk = ceilf(m * k2);
-  if (mk > st.c) {
-    st.s = scale_pow2(st.s, st.c - mk);
-    st.c = mk;
-  }
-  const float cu = st.c > -__builtin_huge_valf() ? st.c : 0.0f;  // all -inf so far: terms are 0
-#pragma unroll
-  for (int e = 0; e < kPerLane; ++e) v[e] = exp2_hw(fmaf(v[e], k2, -cu));
-#pragma unroll
-  for (int w = kPerLane / 2; w >= 1; w >>= 1) {
-#pragma unroll
-    for (int e = 0; e < w; ++e) v[e] += v[e + w];
-  }
-  st.s += (double)v[0];
-}
-
-// Combine the wave's lanes into the chunk's Partial.
-__device__ __forceinline__ Partial wave_combine(const LaneStats& st, bool greedy) {
-  if (greedy) {
-    const unsigned long long key =
-        ((unsigned long long)float_order_key(st.c) << 32) | (0xffffffffu - (uint32_t)st.idx);
-    const unsigned long long best = wave_max_u64(key);
-    return Partial{float_from_order_key((uint32_t)(best >> 32)),
-                   (int)(0xffffffffu - (uint32_t)best), 0.0};
-  }
-  const float C = wave_max(st.c);
-  if (!(C > -__builtin_huge_valf())) return Partial{-__builtin_huge_valf(), 0, 0.0};
-  const double t = st.s != 0.0 ? scale_pow2(st.s, st.c - C) : 0.0;
-  return Partial{C, 0, wave_sum(t)};
-}
-
 // The k-th set bit of m (whole waves; 0 if m has fewer than k + 1 bits).
 __device__ __forceinline__ int wave_kth_bit(unsigned long long m, int k) {
   const int lane = threadIdx.x & 63;
@@ -258,17 +132,20 @@ __device__ __forceinline__ int wave_kth_bit(unsigned long long m, int k) {
 // resident waves; the launch takes the one whose grid ends in the fuller
 // round.
 //
-// Tree rows are compacted when the trees' shapes fit in LDS: the units run
-// over the used rows only (each tree's first n_nodes target rows, then the
-// draft rows of the nodes that have children), so that every wave gets an
-// equal share of the work whatever the shapes.  Otherwise unused rows are
-// skipped as they come.
+// A tree's rows read here are those of the nodes that have children (their
+// children are tested against them): the target rows and, with draft rows,
+// the draft rows.  A leaf's target row is read only by a walk that stops at
+// that leaf, which forms its statistics itself.  The rows are compacted when
+// the trees' shapes fit in LDS: the units run over the used rows only (the
+// target rows of each tree's inner nodes, then their draft rows), so that
+// every wave gets an equal share of the work whatever the shapes.  Otherwise
+// unused rows are skipped as they come.
 template <int DT, int RING>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   __shared__ int s_i[kStatsCache + 1];
   __shared__ float s_f0[kStatsCache], s_f1[kStatsCache];
   __shared__ unsigned long long s_inner[kInnerCache];   // tree b: bit n set if node n has a child
-  __shared__ int s_pt[kInnerCache + 1], s_pq[kInnerCache + 1];   // used-row prefixes
+  __shared__ int s_pt[kInnerCache + 1];   // used-row prefix (inner nodes per tree)
   __shared__ double s_scan[kWaves];
 
   const int V = a.V;
@@ -293,20 +170,19 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   };
 
   const bool cache = a.B <= kStatsCache;
-  // Tree draft rows are read only for nodes with children.
+  // Tree rows are read only for nodes with children.
   const bool tree_q = a.tree && a.rows_b;
-  const bool cache_inner = tree_q && a.B <= kInnerCache;
   const bool compact = a.tree && a.B <= kInnerCache;
 
   uint32_t u = blk * kWaves + wave;
   uint32_t ur = u / nc, ch = u - ur * nc;   // ur: row in the order the units run
 
   SegLoad<DT> ring[RING];
-  // The first chunk's loads go out before anything else.  Compacted trees
-  // issue them for row ur as if no row were unused (full trees keep them)
-  // and issue again below if the row map moves the unit; an unused tree row
-  // is still allocated, so reading it is harmless.
-  if (a.vec_ok && u < total) {
+  // The first chunk's loads go out before anything else, except for
+  // compacted trees, whose row map needs the inner-node masks first.  Trees
+  // skipped as they come issue them for row ur; an unused tree row is still
+  // allocated, so reading it is harmless.
+  if (a.vec_ok && u < total && !compact) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(ur), V, (int)ch * kChunk + r * kSubSpan);
   }
@@ -341,34 +217,20 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     __syncthreads();
   };
   uint32_t n_t = 0;   // compacted: used target rows (they come first)
-  if (compact) {
-    tree_prefix(s_pt, [&](int b) { return s_i[b]; });
-    n_t = (uint32_t)s_pt[a.B];
-  }
-  // The row of iteration row x (draft rows: once the inner masks are known).
+  // The row of iteration row x (once the inner masks are known): the x-th
+  // used target row, then the used draft rows.
   auto row_of = [&](uint32_t x) -> uint32_t {
     if (!compact) return x;
     const int N = a.N;
     if (x < n_t) {
       const int b = wave_find_batch_row(s_pt, a.B, (long long)x, 0);
-      return (uint32_t)(b * N + ((int)x - s_pt[b]));
+      return (uint32_t)(b * N + wave_kth_bit(s_inner[b], (int)x - s_pt[b]));
     }
-    const uint32_t y = x - n_t;
-    const int b = wave_find_batch_row(s_pq, a.B, (long long)y, 0);
-    return (uint32_t)a.n_a + (uint32_t)(b * N + wave_kth_bit(s_inner[b], (int)y - s_pq[b]));
+    const uint32_t y = x - n_t;   // the draft rows of the same nodes, in the same order
+    const int b = wave_find_batch_row(s_pt, a.B, (long long)y, 0);
+    return (uint32_t)a.n_a + (uint32_t)(b * N + wave_kth_bit(s_inner[b], (int)y - s_pt[b]));
   };
-  // A compacted wave whose first unit is a target row has its loads right
-  // now, ahead of the inner masks of the draft rows.
-  bool issued = false;
-  if (compact && a.vec_ok && ur < n_t) {
-    const uint32_t r0 = row_of(ur);
-    if (r0 != ur) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(r0), V, (int)ch * kChunk + r * kSubSpan);
-    }
-    issued = true;
-  }
-  if (cache_inner) {
+  if (compact) {
     // one wave per tree (a lane per node, N <= 64): the mask is the OR of the
     // lanes' parent bits; a wave's trees are taken 16 at a time, their
     // parents loaded together (clamped indices: no load behind a branch)
@@ -393,19 +255,20 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     __syncthreads();
   }
   if (compact) {
-    if (tree_q) tree_prefix(s_pq, [&](int b) { return __popcll(s_inner[b]); });
-    total = (n_t + (tree_q ? (uint32_t)s_pq[a.B] : 0u)) * nc;
+    tree_prefix(s_pt, [&](int b) { return __popcll(s_inner[b]); });
+    n_t = (uint32_t)s_pt[a.B];
+    total = (tree_q ? 2u * n_t : n_t) * nc;
   }
   if (u >= total) return;
   uint32_t row = row_of(ur);
-  if (compact && a.vec_ok && !issued && row != ur) {
+  if (compact && a.vec_ok) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
   }
 
   // Whether a row's partials are needed (always, for compacted rows): tree
-  // rows past n_nodes are not, nor the draft rows of nodes without
-  // children.  Called by whole waves.
+  // rows past n_nodes are not, nor the rows of nodes without children.
+  // Called by whole waves.
   auto row_used = [&](uint32_t r) -> bool {
     if (!a.tree || compact) return true;
     const bool is_q = r >= a.n_a;
@@ -415,7 +278,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     int nn = cache ? s_i[b] : (a.n_nodes ? a.n_nodes[b] : a.N);
     if (nn > a.N) nn = 0;
     if (node >= nn) return false;
-    if (!is_q) return true;
     const int c = lane;
     const bool kid = c > node && c < nn && a.parents[(long long)b * a.N + c] == node;
     return __ballot(kid) != 0ull;

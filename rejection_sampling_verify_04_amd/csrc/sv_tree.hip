@@ -18,8 +18,55 @@
 #include "sv_common.h"
 #include "sv_internal.h"
 #include "sv_finish.h"
+#include "sv_pass.h"
 
 namespace sv {
+
+// The vocabulary pass reads the rows of the nodes that have children only.
+// A leaf's target row is read here, when the walk stops at that leaf (its
+// bonus draw): its chunk Partials formed with the pass's own per-wave
+// arithmetic, one wave per chunk, then merged as the walk's prologue merges
+// the other rows.  Leaves rs (and, for a sampled row, p's chunk masses
+// cm[0..nc)) in LDS and returns whether the row has a finite maximum.  Called
+// by every thread of the work item.
+static_assert(kPartsPerChunk == 1, "one Partial per chunk");
+template <int DT>
+__device__ bool leaf_row_stats(const char* rowp, int V, int nc, int vec_ok, bool greedy, float k2,
+                               Partial* s_part, RowStats* s_rs, double* s_cmv, int* s_ok) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int c = wave; c < nc; c += kFinWaves) {
+    const Partial p = wave_chunk_partial<DT>(rowp, V, c, vec_ok, greedy, k2);
+    if (lane == 0) s_part[c] = p;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const Partial q = s_part[lane < nc ? lane : 0];
+    RowStats rs;
+    const bool ok = merge_parts_seg(q, lane < nc, seg_width(nc), greedy, &rs);
+    if (lane == 0) {
+      *s_rs = rs;
+      *s_ok = ok;
+    }
+    if (!greedy && lane < nc) s_cmv[lane] = q.s > 0.0 ? scale_pow2(q.s, q.c - rs.c) / rs.s : 0.0;
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// The outputs of a batch row in error.
+__device__ __forceinline__ void tree_error_row(const TreeArgs& a, int b, int err) {
+  const int N = a.N;
+  const long long rb = (long long)b * N;
+  for (int i = threadIdx.x; i < N; i += kFinThreads) {
+    a.out_tokens[rb + i] = -1;
+    if (i < N - 1) a.path_nodes[(long long)b * (N - 1) + i] = -1;
+    if (a.p_at) a.p_at[rb + i] = 0.0f;
+  }
+  if (threadIdx.x == 0) {
+    a.num_accepted[b] = -1;
+    if (a.row_status) a.row_status[b] = err;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Tree verify (TOPK): one work item per tree.
@@ -37,6 +84,8 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
   __shared__ int s_found[kFinWaves], s_last[kFinWaves];
   __shared__ int s_jc;
   __shared__ double s_base, s_t;
+  __shared__ Partial s_leaf[kMaxChunks];
+  __shared__ int s_leafok;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_chunks = a.n_chunks;
@@ -73,6 +122,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
   const bool mine = !err0 && tid > 0 && tid < nn;
   const bool badpar = mine && (par < 0 || par >= tid);
   const bool badtok = mine && (tok < 0 || tok >= V);
+  // the nodes with children, in every wave (the lanes hold nodes 0..63):
+  // only their rows were read by the vocabulary pass
+  const bool kid_l = !err0 && lane > 0 && lane < nn && par >= 0 && par < lane;
+  const unsigned long long inner = wave_or_u64(kid_l ? 1ull << par : 0ull);
   if (!mine) {
     par = -1;
     tok = 0;
@@ -81,9 +134,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
     for (int base = wave * R; base < nn; base += kFinWaves * R) {
       const Partial q = base == wave * R ? q0 : load_part(base + sub);
       const int n = base + sub;
+      const bool used = n < nn && ((inner >> (n & 63)) & 1ull);
       RowStats rs;
-      const bool ok = merge_parts_seg(q, n < nn && part < n_parts, P, greedy, &rs);
-      if (n < nn) {
+      const bool ok = merge_parts_seg(q, used && part < n_parts, P, greedy, &rs);
+      if (used) {
         if (part == 0) {
           s_rows[n] = rs;
           s_rowok[n] = ok;
@@ -99,23 +153,16 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
   }
   __syncthreads();
   if (tid < 64) {
+    const bool read = tid < nn && ((inner >> tid) & 1ull);
     const int flags = (__ballot(badpar) ? kRowBadShape : 0) | (__ballot(badtok) ? kRowBadToken : 0) |
-                      (__ballot(tid < nn && !err0 && !s_rowok[tid < kMaxNodes ? tid : 0])
+                      (__ballot(read && !err0 && !s_rowok[tid < kMaxNodes ? tid : 0])
                            ? kRowNonFinite : 0);
     if (tid == 0) s_flags = err0 | flags;
   }
   __syncthreads();
   const int err = s_flags & kRowErrorMask;
   if (err) {
-    for (int i = tid; i < N; i += kFinThreads) {
-      a.out_tokens[rb + i] = -1;
-      if (i < N - 1) a.path_nodes[(long long)b * (N - 1) + i] = -1;
-      if (a.p_at) a.p_at[rb + i] = 0.0f;
-    }
-    if (tid == 0) {
-      a.num_accepted[b] = -1;
-      if (a.row_status) a.row_status[b] = err;
-    }
+    tree_error_row(a, b, err);
     return;
   }
 
@@ -171,6 +218,15 @@ __global__ __launch_bounds__(kFinThreads) void tree_kernel(TreeArgs a) {
   __syncthreads();
   const int stop = s_stop, depth = s_depth;
   const unsigned long long removed = s_removed;
+  if (!((inner >> stop) & 1ull)) {
+    // a leaf: its row, for the bonus draw
+    const char* lrow = (const char*)a.target + (rb + stop) * (long long)V * (DT ? 2 : 4);
+    if (!leaf_row_stats<DT>(lrow, V, n_chunks, a.vec_ok, greedy, k2, s_leaf, &s_rows[stop],
+                            &s_cm[stop * n_chunks], &s_leafok)) {
+      tree_error_row(a, b, kRowNonFinite);
+      return;
+    }
+  }
 
   int token;
   int warn = 0;
@@ -704,6 +760,8 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   __shared__ int s_found[kFinWaves], s_last[kFinWaves];
   __shared__ int s_jc;
   __shared__ double s_base, s_t;
+  __shared__ Partial s_leaf[kMaxChunks];
+  __shared__ int s_leafok;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = NC ? NC : a.n_chunks;
@@ -743,6 +801,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   const bool mine = !err0 && tid > 0 && tid < nn;
   const bool badpar = mine && (par < 0 || par >= tid);
   const bool badtok = mine && (tok < 0 || tok >= V);
+  // the nodes with children, in every wave (the lanes hold nodes 0..63):
+  // only their rows were read by the vocabulary pass
+  const bool kid_l = !err0 && lane > 0 && lane < nn && par >= 0 && par < lane;
+  const unsigned long long inner_w = wave_or_u64(kid_l ? 1ull << par : 0ull);
   if (!mine || badpar) {
     par = -1;
     tok = 0;
@@ -752,11 +814,12 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     const int r = base + sub;
     const bool draft = r >= nn;
     const int n = draft ? r - nn : r;
+    const bool used = r < n_rows && ((inner_w >> (n & 63)) & 1ull);
     RowStats rs;
     // a wave may hold target and draft rows: the greedy choice is per lane
     const bool g = draft ? gd : gt;
-    const bool ok = merge_parts_seg(q, r < n_rows && part < n_parts, P, g, &rs);
-    if (r < n_rows) {
+    const bool ok = merge_parts_seg(q, used && part < n_parts, P, g, &rs);
+    if (used) {
       if (part == 0) {
         if (draft) {
           s_qrows[n] = rs;
@@ -783,8 +846,8 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   if (tid < 64) {
     const unsigned long long inner = s_inner;
     const int n = tid < kMaxNodes ? tid : 0;
-    const bool bad_row = tid < nn && !err0 &&
-                         (!s_rowok[n] || (((inner >> n) & 1ull) && !s_qrowok[n]));
+    const bool bad_row = tid < nn && !err0 && ((inner >> n) & 1ull) &&
+                         (!s_rowok[n] || !s_qrowok[n]);
     const int flags = (__ballot(badpar) ? kRowBadShape : 0) | (__ballot(badtok) ? kRowBadToken : 0) |
                       (__ballot(bad_row) ? kRowNonFinite : 0);
     if (tid == 0) s_flags = err0 | flags;
@@ -792,15 +855,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
   __syncthreads();
   const int err = s_flags & kRowErrorMask;
   if (err) {
-    for (int i = tid; i < N; i += kFinThreads) {
-      a.out_tokens[rb + i] = -1;
-      if (i < N - 1) a.path_nodes[(long long)b * (N - 1) + i] = -1;
-      if (a.p_at) a.p_at[rb + i] = 0.0f;
-    }
-    if (tid == 0) {
-      a.num_accepted[b] = -1;
-      if (a.row_status) a.row_status[b] = err;
-    }
+    tree_error_row(a, b, err);
     return;
   }
 
@@ -922,6 +977,16 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     node = accepted;
   }
   const int stop = node;
+  if (!kids) {
+    // a leaf: its target row, for the bonus draw (d was formed before it
+    // had statistics)
+    if (!leaf_row_stats<DT>(d.xrow, V, nc, a.vec_ok, gt, kt, s_leaf, &s_rows[stop],
+                            &s_cm[stop * nc], &s_leafok)) {
+      tree_error_row(a, b, kRowNonFinite);
+      return;
+    }
+    d = wor_dist(d.xrow, d.xrow, s_rows[stop], s_qrows[stop], gt, gd, kt, kd, false);
+  }
 
   int token;
   if (gt) {

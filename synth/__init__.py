@@ -363,16 +363,26 @@ def attn_tensors(seed=4, B=64, H=32, N=64, d=128, L=4096, S_max=None):
     return q, k, v, np.full(B, L, dtype=np.int32)
 
 
+def inner_nodes(d):
+    """Nodes with children, summed over a tree batch's trees."""
+    par = np.asarray(d["parents"])
+    B, N = par.shape
+    nn = np.full(B, N) if d.get("n_nodes") is None else np.asarray(d["n_nodes"])
+    return int(sum(len({int(p) for p in par[b, 1:int(nn[b])] if p >= 0}) for b in range(B)))
+
+
 def logits_bytes(d):
-    """Algorithmic bytes of one linear/tree verify call: every logit read once."""
+    """Bytes of the logit rows one verify call must read, each once: every row
+    of a linear batch; in a tree, the target rows (and, with sampled children,
+    the draft rows) of the nodes with children.  A leaf's row, read only when
+    the walk stops at it, is not counted."""
     esize = 2 if d["dtype"] == BF16 else 4
     if d["kind"] == "linear":
         rows = d["target"].shape[0] + d["draft"].shape[0]
     elif d["kind"] == "tree_wor":
-        # every node's target row, and the draft rows of the nodes with children
-        rows = int(np.sum(d["n_nodes"])) + int(d["n_inner"])
+        rows = 2 * inner_nodes(d)
     else:
-        rows = int(np.sum(d["n_nodes"]))
+        rows = inner_nodes(d)
     return rows * d["V"] * esize
 
 

@@ -65,8 +65,23 @@ def test_partial_trees_and_error_rows():
     d["n_nodes"][7] = 0             # bad node count
     d["temp_target"] = d["temp_target"].copy()
     d["temp_target"][8] = np.nan    # bad temperature
+    d["target"] = d["target"].copy()
+    d["target"][9, int(d["parents"][9, 5])] = -np.inf   # an inner node's row: read, an error
+    # A leaf's row is read only by a walk that stops there; the walk up to a
+    # leaf reads inner rows only, so a non-finite row at the leaf a walk
+    # stops at leaves the walk as it was and makes the row an error, while one
+    # at a leaf no walk reaches changes nothing.
+    ref0 = run_oracle_tree(d)
+    b_stop = next(b for b in (10, 11) if ref0[5][b].stop_kind == "bonus")
+    d["target"][b_stop, ref0[5][b_stop].stop_node, 7] = np.nan
+    b_other = 21 - b_stop
+    unread = [n for n in range(1, d["N"]) if n not in set(d["parents"][b_other, 1:].tolist())
+              and n != ref0[5][b_other].stop_node]
+    d["target"][b_other, unread[0]] = -np.inf
     gpu, ref = check(d, "partial trees and error rows")
-    assert list(gpu["num_accepted"][[5, 6, 7, 8]]) == [-1, -1, -1, -1]
+    assert list(gpu["num_accepted"][[5, 6, 7, 8, 9, b_stop]]) == [-1] * 6
+    assert gpu["row_status"][b_stop] == ref[4][b_stop] != 0
+    assert gpu["num_accepted"][b_other] >= 0 and gpu["row_status"][b_other] & 0xFF == 0
 
 
 def test_chain_tree_equals_linear_greedy_draft():

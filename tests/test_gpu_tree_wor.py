@@ -129,13 +129,23 @@ def test_wor_partial_trees_and_error_rows():
     d["n_nodes"][7] = 0               # bad node count
     d["temp_draft"] = d["temp_draft"].copy()
     d["temp_draft"][8] = np.nan       # bad draft temperature
-    d["target"][9, 4] = -np.inf       # a node's target row without a finite maximum
+    d["target"][9, 4] = -np.inf       # an inner node's target row without a finite maximum
     d["draft"][10, 0] = -np.inf       # the root's draft row: non-finite
     leaf = int(max(c for c in range(1, 21) if c not in set(d["parents"][11, 1:].tolist())))
     d["draft"][11, leaf] = -np.inf    # a leaf's draft row is never read: fine
+    # A leaf's target row is read only by a walk that stops there (the walk up
+    # to it reads inner rows only): an error at the leaf the walk stops at,
+    # nothing at a leaf no walk reaches.
+    ref0 = run_oracle_tree(d)
+    assert ref0[5][12].stop_kind == "bonus"
+    d["target"][12, ref0[5][12].stop_node, 3] = np.nan
+    unread = [n for n in range(1, 21) if n not in set(d["parents"][13, 1:].tolist())
+              and n != ref0[5][13].stop_node]
+    d["target"][13, unread[0]] = -np.inf
     gpu, ref = check(d, "partial trees and error rows")
-    assert list(gpu["num_accepted"][[5, 6, 7, 8, 9, 10]]) == [-1] * 6
+    assert list(gpu["num_accepted"][[5, 6, 7, 8, 9, 10, 12]]) == [-1] * 7
     assert gpu["num_accepted"][11] >= 0 and gpu["row_status"][11] & 0xFF == 0
+    assert gpu["num_accepted"][13] >= 0 and gpu["row_status"][13] & 0xFF == 0
 
 
 def test_wor_chain_equals_linear():
