@@ -2,9 +2,10 @@
 //
 // One workgroup per (batch row, head); wave w owns query rows 16w..16w+15.
 // Keys stream in tiles of 64 from the cache into two LDS buffers (K and V
-// row-major), with the next three tiles' global loads in flight while the
-// current tile is multiplied, and one barrier per tile.  The V^T operand is formed on the way out of LDS by the
-// transposing read ds_read_b64_tr_b16.  Per tile and wave:
+// row-major), with the next two tiles' global loads in flight while the
+// current tile is multiplied, and one barrier per tile.  The V^T operand is
+// formed on the way out of LDS by the transposing read ds_read_b64_tr_b16.
+// Per tile and wave:
 //
 //   S^T[64 keys x 16 queries] = K_tile . Q^T    4 key blocks x 4 d-steps of
 //                                               v_mfma_f32_16x16x32_bf16
@@ -127,12 +128,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int total = L + N;
   const int n_tiles = (total + kKT - 1) / kKT;
-  // Three tiles' loads are in flight in registers (buffers A, B and C) while
-  // the current tile is multiplied out of one of the two LDS buffers.  Keys past
+  // Two tiles' loads are in flight in registers (buffers A and B) while the
+  // current tile is multiplied out of one of the two LDS buffers.  Keys past
   // the end load the last key (finite, masked to weight 0), so that no load
   // sits behind a branch: a load whose value crosses a branch join is
   // waited for there, which would drain the prefetch.
-  u32x4_t kA[4], vA[4], kB[4], vB[4], kC[4], vC[4];
+  u32x4_t kA[4], vA[4], kB[4], vB[4];
   auto load_tile = [&](u32x4_t (&kr)[4], u32x4_t (&vr)[4], int t) {
     t = min(t, n_tiles - 1);
 #pragma unroll
@@ -235,31 +236,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // Tile t is loaded into register buffer t mod 3 and multiplied out of LDS
+  // Tile t is loaded into register buffer t mod 2 and multiplied out of LDS
   // buffer t mod 2.  After tile t is multiplied, tile t + 1 goes from its
   // registers to the other LDS buffer (last read for tile t - 1, which every
   // wave finished before the previous barrier), those registers take tile
-  // t + 4, and one barrier publishes tile t + 1: three tiles' loads stay in
+  // t + 3, and one barrier publishes tile t + 1: two tiles' loads stay in
   // flight behind the one being multiplied.
   load_tile(kA, vA, 0);
   load_tile(kB, vB, 1);
-  load_tile(kC, vC, 2);
   store_tile(kA, vA, 0);
-  load_tile(kA, vA, 3);
+  load_tile(kA, vA, 2);
   __syncthreads();
 #define SV_ATTN_STEP(T, KR, VR, BUF)    \
   compute_tile((T), 1 - (BUF));          \
   if ((T) + 1 >= n_tiles) break;         \
   store_tile(KR, VR, (BUF));             \
-  load_tile(KR, VR, (T) + 4);            \
+  load_tile(KR, VR, (T) + 3);            \
   __syncthreads();
-  for (int t = 0;; t += 6) {
+  for (int t = 0;; t += 2) {
     SV_ATTN_STEP(t, kB, vB, 1)
-    SV_ATTN_STEP(t + 1, kC, vC, 0)
-    SV_ATTN_STEP(t + 2, kA, vA, 1)
-    SV_ATTN_STEP(t + 3, kB, vB, 0)
-    SV_ATTN_STEP(t + 4, kC, vC, 1)
-    SV_ATTN_STEP(t + 5, kA, vA, 0)
+    SV_ATTN_STEP(t + 1, kA, vA, 0)
   }
 #undef SV_ATTN_STEP
 
