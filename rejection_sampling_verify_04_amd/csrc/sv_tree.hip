@@ -639,9 +639,10 @@ __device__ __forceinline__ double wor_total_r(const float* s_a, const float (&rb
 }
 
 // The chunk masses of the current weights into s_mass (formed as the draw's
-// block scan forms its total); returns their sum.
+// block scan forms its total); returns their sum.  The weights replace a(v)
+// in LDS (each thread its own elements), for the draw that follows.
 template <int NC>
-__device__ __forceinline__ double wor_masses_r(const float* s_a, const float (&rb)[NC * kPerThread],
+__device__ __forceinline__ double wor_masses_r(float* s_a, const float (&rb)[NC * kPerThread],
                                                float lam, const int* ex_tok, const float* ex_lam,
                                                int nex, double* s_mass, double* s_red) {
   const int tix = opaque_tid();
@@ -653,6 +654,9 @@ __device__ __forceinline__ double wor_masses_r(const float* s_a, const float (&r
     wor_chunk_r<NC, false>(s_a, rb, c, tix, ((hit >> c) & 1u) != 0u, lam, ex_tok, ex_lam, nex, -1,
                            w, be);
     v[c] = thread_total(w);
+    float4* cw = (float4*)(s_a + c * kChunk + tix * kPerThread);
+    cw[0] = make_float4(w[0], w[1], w[2], w[3]);
+    cw[1] = make_float4(w[4], w[5], w[6], w[7]);
   }
   double t[NC];
   block_totals<NC>(v, s_red, t);
@@ -1012,6 +1016,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     for (int j = 0; j < nc; ++j) R += s_mass[j];
     R = uni(R);
     __syncthreads();
+    // every child rejected at a cached node: the chosen chunk's weights come
+    // from the cache too (the same values as from memory)
+    bool from_cache = false;
+    if constexpr (NC > 0) from_cache = kids != 0ull && cached_node == stop && R > 0.0;
     if (!(R > 0.0)) {
       // rounding emptied the weights: draw from p
       warn |= kRowWarnRZero;
@@ -1024,10 +1032,18 @@ __global__ __launch_bounds__(kFinThreads) void tree_wor_kernel(TreeArgs a) {
     const double u = word_to_uniform(verify_words(a.seed, a.step, rid, (uint32_t)stop).y);
     choose_chunk(s_mass, nc, u, &s_jc, &s_base, &s_t);
     const int jc = uni(s_jc);
-    StopVec<DT> r;
-    wor_load<DT, VEC>(d, V, jc, r);
     float w[kPerThread], be[kPerThread];
-    wor_weights<DT, VEC, false>(d, V, jc, r, lam_f32(lam), s_ex_tok, s_ex_lamf, nex, -1, w, be);
+    if (from_cache) {
+      // the weights wor_masses_r left in place of a(v) (this thread's own)
+      const float4* cw = (const float4*)(s_a + jc * kChunk + opaque_tid() * kPerThread);
+      const float4 lo = cw[0], hi = cw[1];
+      w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
+      w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+    } else {
+      StopVec<DT> r;
+      wor_load<DT, VEC>(d, V, jc, r);
+      wor_weights<DT, VEC, false>(d, V, jc, r, lam_f32(lam), s_ex_tok, s_ex_lamf, nex, -1, w, be);
+    }
     const double acc = thread_total(w);
     double total;
     const double excl = block_exclusive_scan<kFinWaves>(acc, s_scan, &total);
