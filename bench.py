@@ -110,9 +110,17 @@ def cpu_baseline_linear(d, seconds):
         rows += 1
         b += 1
     dt = time.perf_counter() - t0
+    es = 2 if d["dtype"] == 1 else 4
+    V = d["target"].shape[1] if d["target"].ndim == 2 else d["V"]
+    total = int(off[-1])
+    # the logit rows of the sampled batch rows, each read once: 2 gamma_b + 1 per row
+    sample_bytes = (2 * done_pos + rows) * V * es
     return dict(value=done_pos / dt, unit="verified draft positions/s", cores=1, kind="oracle",
+                us_per_call=dt / done_pos * total * 1e6,
+                logit_gb_per_s=sample_bytes / dt / 1e9,
                 sample="%d batch rows (%d draft positions) of the same workload in %.1f s, "
-                       "single-threaded NumPy float64" % (rows, done_pos, dt))
+                       "single-threaded NumPy float64; us_per_call scales the sample to the "
+                       "whole batch" % (rows, done_pos, dt))
 
 
 def cpu_model():
@@ -223,9 +231,12 @@ def cpu_baseline_tree(d, seconds):
         nodes += int(d["n_nodes"][b]) - 1
         rows += 1
     dt = time.perf_counter() - t0
+    total = int(np.sum(d["n_nodes"])) - B
     return dict(value=nodes / dt, unit="verified draft nodes/s", cores=1, kind="oracle",
+                us_per_call=dt / nodes * total * 1e6,
                 sample="%d trees (%d draft nodes) of the same workload in %.1f s, "
-                       "single-threaded NumPy float64" % (rows, nodes, dt))
+                       "single-threaded NumPy float64 (it reads every node's rows); "
+                       "us_per_call scales the sample to the whole batch" % (rows, nodes, dt))
 
 
 def cpu_baseline_attn(q, k, v, L, parents, seconds):
