@@ -84,6 +84,31 @@ def test_partial_trees_and_error_rows():
     assert gpu["num_accepted"][b_other] >= 0 and gpu["row_status"][b_other] & 0xFF == 0
 
 
+@pytest.mark.parametrize("B", [600, 1100])
+def test_many_trees(B):
+    """More trees than the vocabulary pass compacts (512: leaf rows are then
+    skipped as they come) and than it caches in LDS (1024), with ragged node
+    counts, an inner node's non-finite row (an error) and a non-finite row at
+    the leaf a walk stops at (an error) or at a leaf no walk reaches."""
+    d = synth.peaked_tree(seed=25 + B, B=B, N=16)
+    d["n_nodes"] = d["n_nodes"].copy()
+    d["n_nodes"][::7] = np.minimum(d["n_nodes"][::7], 3)
+    d["n_nodes"][5] = 1
+    d["target"] = d["target"].copy()
+    d["target"][10, int(d["parents"][10, 2])] = -np.inf
+    ref0 = run_oracle_tree(d)
+    stops = [b for b in range(20, B) if ref0[5][b].stop_kind == "bonus"][:2]
+    d["target"][stops[0], ref0[5][stops[0]].stop_node, 1] = np.nan
+    others = [b for b in range(20, B) if ref0[5][b].stop_kind == "reject" and b not in stops]
+    b_other = others[0]
+    unread = [n for n in range(1, int(d["n_nodes"][b_other]))
+              if n not in set(d["parents"][b_other, 1:int(d["n_nodes"][b_other])].tolist())]
+    d["target"][b_other, unread[0]] = -np.inf
+    gpu, ref = check(d, "%d trees" % B)
+    assert gpu["num_accepted"][10] == -1 and gpu["num_accepted"][stops[0]] == -1
+    assert gpu["num_accepted"][b_other] >= 0
+
+
 def test_chain_tree_equals_linear_greedy_draft():
     rng = np.random.default_rng(31)
     B, g, V = 16, 6, 3000

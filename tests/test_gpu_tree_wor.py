@@ -148,6 +148,25 @@ def test_wor_partial_trees_and_error_rows():
     assert gpu["num_accepted"][13] >= 0 and gpu["row_status"][13] & 0xFF == 0
 
 
+@pytest.mark.parametrize("B", [600, 1100])
+def test_wor_many_trees(B):
+    """SAMPLED_WOR over more trees than the vocabulary pass compacts (512) and
+    caches in LDS (1024): ragged node counts, an inner node's non-finite
+    draft row (an error) and a non-finite target row at the leaf a walk stops
+    at (an error)."""
+    d = synth.tree_wor(seed=30 + B, B=B, N=16, V=64, draft_sd=6.0, pert=1.0, dtype=synth.F32)
+    d["n_nodes"] = d["n_nodes"].copy()
+    d["n_nodes"][::9] = np.minimum(d["n_nodes"][::9], 4)
+    d["target"] = d["target"].copy()
+    d["draft"] = d["draft"].copy()
+    d["draft"][11, int(d["parents"][11, 3])] = -np.inf
+    ref0 = run_oracle_tree(d)
+    b_stop = next(b for b in range(20, B) if ref0[5][b].stop_kind == "bonus")
+    d["target"][b_stop, ref0[5][b_stop].stop_node, 2] = np.nan
+    gpu, ref = check(d, "%d SAMPLED_WOR trees" % B)
+    assert gpu["num_accepted"][11] == -1 and gpu["num_accepted"][b_stop] == -1
+
+
 def test_wor_chain_equals_linear():
     """One child per node: SAMPLED_WOR is the linear verify with the draft's q."""
     rng = np.random.default_rng(19)
