@@ -63,6 +63,25 @@ def test_ragged_fp32_five_chunks():
     check(ragged(21, gammas, 40000, synth.F32, sigma=0.5), "ragged 40000 fp32")
 
 
+@pytest.mark.parametrize("B", [700, 1100])
+def test_many_rows_five_chunks(B):
+    """More batch rows than the mass pass stages decisions for in LDS (512)
+    and, at 1100, than the vocabulary pass stages offsets for (1024): V =
+    40000 bf16 (five chunks, the pipelined mass pass), ragged gamma of 0-3,
+    with a token out of range and a bad temperature."""
+    rng = np.random.default_rng(40 + B)
+    gammas = rng.integers(0, 4, size=B)
+    d = ragged(40 + B, gammas, 40000, synth.BF16, sigma=0.5)
+    d["tokens"] = d["tokens"].copy()
+    d["temp_target"] = d["temp_target"].copy()
+    o = int(d["offsets"][B - 3])
+    if d["offsets"][B - 2] > o:
+        d["tokens"][o] = 40000                 # out of range: an error row
+    d["temp_target"][B // 2] = np.nan            # bad temperature: an error row
+    gpu, ref, s = check(d, "%d rows, V=40000 bf16" % B)
+    assert gpu["num_accepted"][B // 2] == -1
+
+
 def test_unaligned_bf16():
     check(ragged(13, [3, 5, 0, 2], 8191, synth.BF16, sigma=0.5), "8191 bf16 (scalar path)")
 
