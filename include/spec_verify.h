@@ -64,7 +64,7 @@ extern "C" {
 /* Return codes. */
 #define SV_OK 0
 #define SV_ERR_INVALID_ARG (-1) /* null pointer, bad size, dtype, N > 64, ... */
-#define SV_ERR_UNSUPPORTED (-2) /* valid request this build does not implement */
+#define SV_ERR_UNSUPPORTED (-2) /* valid request the library does not implement */
 #define SV_ERR_WORKSPACE (-3)   /* workspace missing, too small or misaligned */
 #define SV_ERR_HIP (-4)         /* a kernel launch failed */
 #define SV_ERR_SCRATCH (-5)     /* needs more than the static scratch of a _noalloc call */
