@@ -680,6 +680,7 @@ __device__ __forceinline__ double wor_fill_total(const WorDist& d, int V, float*
   constexpr int ES = StopVec<DT>::ES, EPV = StopVec<DT>::EPV, NV = StopVec<DT>::NV;
   constexpr int kGroup = NC;
   const int tix = opaque_tid();
+  const int wave_first = __builtin_amdgcn_readfirstlane(tix) & ~63;   // the wave's first thread
   double v[2] = {0.0, 0.0};
 #pragma unroll
   for (int g0 = 0; g0 < NC; g0 += kGroup) {
@@ -719,24 +720,53 @@ __device__ __forceinline__ double wor_fill_total(const WorDist& d, int V, float*
           }
         }
       }
+      // The short form first: a = 2^(x k - c) s and b likewise.  The
+      // one-hot terms (a greedy row: its exponential term is 0), the
+      // elements past V and t_cur are then set as the full form sets them,
+      // each behind a wave-uniform test, so the values are wor_weights' own.
+      float bv[kPerThread];
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e) {
-        const int idx = e0 + e;
-        const float a = fmaf(exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)), d.p_inv_s,
-                             idx == d.p_amax ? 1.0f : 0.0f);
-        const float b = fmaf(exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)), d.q_inv_s,
-                             idx == d.q_amax ? 1.0f : 0.0f);
-        av[e] = idx < V ? a : 0.0f;
-        const float bv = idx < V ? b : 0.0f;
-        rb[c * kPerThread + e] = bv;
-        w[e] = fmaxf(fmaf(-lam, bv, av[e]), 0.0f);
-        if (WANT_E) be[e] = idx == t_cur ? 0.0f : bv;
+        av[e] = exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
+        bv[e] = exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
+      }
+      const int we0 = c * kChunk + wave_first * kPerThread;   // the wave's 512 elements
+      if (d.onehot) {
+        const int dp = d.p_amax - e0, dq = d.q_amax - e0;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+          av[e] = dp == e ? 1.0f : av[e];
+          bv[e] = dq == e ? 1.0f : bv[e];
+        }
+      }
+      if (we0 + 64 * kPerThread > V) {
+        const int rem = V - e0;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+          av[e] = e < rem ? av[e] : 0.0f;
+          bv[e] = e < rem ? bv[e] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        rb[c * kPerThread + e] = bv[e];
+        w[e] = fmaxf(fmaf(-lam, bv[e], av[e]), 0.0f);
+      }
+      if (WANT_E) {
+        // the draft terms without t_cur: a copy only in the wave that holds it
+        if ((unsigned)(t_cur - we0) < 64u * kPerThread) {
+          const int dt = t_cur - e0;
+#pragma unroll
+          for (int e = 0; e < kPerThread; ++e) be[e] = dt == e ? 0.0f : bv[e];
+          v[1] += thread_total(be);
+        } else {
+          v[1] += thread_total(bv);
+        }
       }
       float4* ca = (float4*)(s_a + e0);
       ca[0] = make_float4(av[0], av[1], av[2], av[3]);
       ca[1] = make_float4(av[4], av[5], av[6], av[7]);
       v[0] += thread_total(w);
-      if (WANT_E) v[1] += thread_total(be);
     }
   }
   double t[2];
