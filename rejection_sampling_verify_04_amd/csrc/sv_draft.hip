@@ -583,6 +583,7 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   __shared__ unsigned long long s_top[kTopkSmallK];
   __shared__ float s_cval[kTopkCand];
   __shared__ int s_cidx[kTopkCand];
+  __shared__ float s_vm[kTopkSmallVecs][kTopkSmallThreads];   // each vector's maximum
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const char* row = (const char*)logits + (long long)r * V * 2;
@@ -633,13 +634,20 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   double sacc = 0.0;
 #pragma unroll
   for (int j = 0; j < kTopkSmallVecs; ++j) {
+    // a vector past V becomes four words of bf16 -inf, once
     const bool vj = valid(j);
+    const uint32_t kNegInf2 = 0xff80ff80u;
+    raw[j].x = vj ? raw[j].x : kNegInf2;
+    raw[j].y = vj ? raw[j].y : kNegInf2;
+    raw[j].z = vj ? raw[j].z : kNegInf2;
+    raw[j].w = vj ? raw[j].w : kNegInf2;
     float xv[8];
 #pragma unroll
-    for (int h = 0; h < 8; ++h) xv[h] = vj ? val(j, h) : -__builtin_huge_valf();
+    for (int h = 0; h < 8; ++h) xv[h] = val(j, h);
     float mj = xv[0];
 #pragma unroll
     for (int h = 1; h < 8; ++h) mj = fmaxf(mj, xv[h]);
+    s_vm[j][tid] = mj;   // read back by this thread only
     m = fmaxf(m, mj);
     const float cn = fmaxf(c, ceilf(mj * kc));
     sacc = sacc != 0.0 ? scale_pow2(sacc, c - cn) : 0.0;
@@ -690,12 +698,14 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     logprob[(long long)r * k + rank] = (float)lp;
   };
 
-  // the logits >= L
+  // the logits >= L; only a vector whose maximum reaches L can hold one
   uint32_t n_cand = 0u;
 #pragma unroll
   for (int j = 0; j < kTopkSmallVecs; ++j) {
+    if (s_vm[j][tid] >= L) {
 #pragma unroll
-    for (int h = 0; h < 8; ++h) n_cand += (valid(j) && val(j, h) >= L) ? 1u : 0u;
+      for (int h = 0; h < 8; ++h) n_cand += (valid(j) && val(j, h) >= L) ? 1u : 0u;
+    }
   }
   fence_raw();
   double c_tot;
@@ -706,13 +716,15 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     uint32_t at = c_pos;
 #pragma unroll
     for (int j = 0; j < kTopkSmallVecs; ++j) {
+      if (s_vm[j][tid] >= L) {
 #pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        const float x = val(j, h);
-        if (valid(j) && x >= L) {
-          s_cval[at] = x;
-          s_cidx[at] = index(j, h);
-          ++at;
+        for (int h = 0; h < 8; ++h) {
+          const float x = val(j, h);
+          if (valid(j) && x >= L) {
+            s_cval[at] = x;
+            s_cidx[at] = index(j, h);
+            ++at;
+          }
         }
       }
     }
