@@ -1,17 +1,18 @@
 // Tree- or causal-masked verify attention on MFMA (gfx950).
 //
 // One workgroup per (batch row, head); wave w owns query rows 16w..16w+15.
-// Keys stream in tiles of 64 from the cache into two LDS buffers (K and V
-// row-major), with the next two tiles' global loads in flight while the
-// current tile is multiplied, and one barrier per tile.  The V^T operand is
-// formed on the way out of LDS by the transposing read ds_read_b64_tr_b16.
-// Per tile and wave:
+// Keys stream in tiles of 32 from the cache into two LDS buffers (K and V
+// row-major), with the next tile's global loads in flight while the current
+// tile is multiplied, and one barrier per tile; at 120 VGPRs and 36 KB of
+// LDS, four workgroups share a compute unit.  The V^T operand is formed on
+// the way out of LDS by the transposing read ds_read_b64_tr_b16.  Per tile
+// and wave:
 //
-//   S^T[64 keys x 16 queries] = K_tile . Q^T    4 key blocks x 4 d-steps of
+//   S^T[32 keys x 16 queries] = K_tile . Q^T    2 key blocks x 4 d-steps of
 //                                               v_mfma_f32_16x16x32_bf16
 //   online softmax per query column (log2 domain), mask from a 64-bit
 //   ancestor set per query for the keys in [L, L+N)
-//   O^T[128 d x 16 queries] += V^T . P^T        8 d blocks x 2 key-steps
+//   O^T[128 d x 16 queries] += V^T . P^T        8 d blocks x 1 key-step
 //
 // Keeping keys (and d) on the M side of both products puts every query in
 // one lane column of the accumulator, so the running max, the rescale of O
@@ -35,7 +36,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
-constexpr int kKT = 64;               // keys per tile
+constexpr int kKT = 32;               // keys per tile
+constexpr int kKB = kKT / 16;         // 16-key blocks per tile
+constexpr int kKS = kKT / 32;         // 32-key steps of the P.V product
+constexpr int kTileVecs = kKT * kD * 2 / 16 / 256;   // 16-byte loads per thread per tile and cache
 constexpr int kKsStride = kD + 8;     // bf16 per K row in LDS (16 B pad)
 // bf16 per V row in LDS: 72 dwords, so the four rows x 32 bytes that one
 // 16-lane transposing read touches fall on 32 distinct banks
@@ -65,7 +69,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kKT * kKsStride];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * kKT * kVsStride];
   __shared__ unsigned long long s_anc[kMaxNodes];
@@ -128,16 +132,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int total = L + N;
   const int n_tiles = (total + kKT - 1) / kKT;
-  // Two tiles' loads are in flight in registers (buffers A and B) while the
-  // current tile is multiplied out of one of the two LDS buffers.  Keys past
-  // the end load the last key (finite, masked to weight 0), so that no load
-  // sits behind a branch: a load whose value crosses a branch join is
-  // waited for there, which would drain the prefetch.
-  u32x4_t kA[4], vA[4], kB[4], vB[4];
-  auto load_tile = [&](u32x4_t (&kr)[4], u32x4_t (&vr)[4], int t) {
+  // The next tile's loads are in flight in registers while the current tile
+  // is multiplied out of one of the two LDS buffers.  Keys past the end load
+  // the last key (finite, masked to weight 0), so that no load sits behind a
+  // branch: a load whose value crosses a branch join is waited for there,
+  // which would drain the prefetch.
+  u32x4_t kA[kTileVecs], vA[kTileVecs];
+  auto load_tile = [&](u32x4_t (&kr)[kTileVecs], u32x4_t (&vr)[kTileVecs], int t) {
     t = min(t, n_tiles - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kTileVecs; ++j) {
       const int ci = j * kThreads + tid;
       const int key = ci >> 4, d0 = (ci & 15) * 8;
       const int gk = min(t * kKT + key, total - 1);
@@ -146,11 +150,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       vr[j] = __builtin_nontemporal_load((const u32x4_t*)(a.v + headKV + (long long)gk * kD + d0));
     }
   };
-  auto store_tile = [&](const u32x4_t (&kr)[4], const u32x4_t (&vr)[4], int buf) {
+  auto store_tile = [&](const u32x4_t (&kr)[kTileVecs], const u32x4_t (&vr)[kTileVecs], int buf) {
     uint16_t* ks = Ks + buf * (kKT * kKsStride);
     uint16_t* vs = Vs + buf * (kKT * kVsStride);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kTileVecs; ++j) {
       const int ci = j * kThreads + tid;
       const int key = ci >> 4, d0 = (ci & 15) * 8;
       *(u32x4_t*)&ks[key * kKsStride + d0] = kr[j];
@@ -162,9 +166,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto compute_tile = [&](int t, int buf) {
     const uint16_t* ks = Ks + buf * (kKT * kKsStride);
     const uint16_t* vs = Vs + buf * (kKT * kVsStride);
-    f32x4_t s[4];
+    f32x4_t s[kKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKB; ++kb) {
       s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks_ = 0; ks_ < 4; ++ks_) {
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool need_mask = tile0 + kKT > L;
     float tmax = -__builtin_huge_valf();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = s[kb][i] * a.scale_log2;
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float alpha = exp2_hw(m_run - m_use);
     float psum = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = exp2_hw(s[kb][i] - m_use);
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
+    for (int ks2 = 0; ks2 < kKS; ++ks2) {
       // logical keys 8g..8g+7 of this key-step = physical keys
       // 32*ks2 + 4g + {0..3} and 32*ks2 + 16 + 4g + {0..3}
       const uint4 pu = make_uint4(pack_bf16x2(s[2 * ks2][0], s[2 * ks2][1]),
@@ -236,28 +240,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // Tile t is loaded into register buffer t mod 2 and multiplied out of LDS
-  // buffer t mod 2.  After tile t is multiplied, tile t + 1 goes from its
-  // registers to the other LDS buffer (last read for tile t - 1, which every
-  // wave finished before the previous barrier), those registers take tile
-  // t + 3, and one barrier publishes tile t + 1: two tiles' loads stay in
-  // flight behind the one being multiplied.
+  // Tile t is multiplied out of LDS buffer t mod 2.  After it, tile t + 1
+  // goes from the registers to the other buffer (last read for tile t - 1,
+  // which every wave finished before the previous barrier), the registers
+  // take tile t + 2, and one barrier publishes tile t + 1.  (Two 64-key tiles
+  // in flight behind the multiplied one, two workgroups per compute unit:
+  // 717 us at B=64, H=32, L=4096; this form: 696 us.)
   load_tile(kA, vA, 0);
-  load_tile(kB, vB, 1);
   store_tile(kA, vA, 0);
-  load_tile(kA, vA, 2);
+  load_tile(kA, vA, 1);
   __syncthreads();
-#define SV_ATTN_STEP(T, KR, VR, BUF)    \
-  compute_tile((T), 1 - (BUF));          \
-  if ((T) + 1 >= n_tiles) break;         \
-  store_tile(KR, VR, (BUF));             \
-  load_tile(KR, VR, (T) + 3);            \
-  __syncthreads();
-  for (int t = 0;; t += 2) {
-    SV_ATTN_STEP(t, kB, vB, 1)
-    SV_ATTN_STEP(t + 1, kA, vA, 0)
+  for (int t = 0;; ++t) {
+    compute_tile(t, t & 1);
+    if (t + 1 >= n_tiles) break;
+    store_tile(kA, vA, (t + 1) & 1);
+    load_tile(kA, vA, t + 2);
+    __syncthreads();
   }
-#undef SV_ATTN_STEP
 
   float l = l_run + __shfl_xor(l_run, 16, 64);
   l += __shfl_xor(l, 32, 64);

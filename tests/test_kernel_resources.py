@@ -73,15 +73,17 @@ def test_streaming_stats_and_finish_passes_do_not_spill():
             if name.startswith("_ZN2sv15tree_wor_kernel") and name.endswith("Li4EEEvNS_8TreeArgsE"):
                 # the SAMPLED_WOR walk with a 4-chunk cache keeps 32 draft terms per
                 # thread in registers at the 128-VGPR limit of a 1024-thread work
-                # item; a few prologue values spill (three dwords reloaded per pass)
-                assert r["spill"] <= 16, (name, r)
+                # item; two values spill
+                assert r["spill"] <= 4, (name, r)
             else:
                 assert r["spill"] == 0, (name, r)
 
 
-def test_attention_two_waves_per_simd():
+def test_attention_four_waves_per_simd():
+    """32-key tiles with one tile's loads in registers: four 256-thread work
+    items per compute unit, with no spill."""
     for name, r in kernels("sv_attn.hip", "_ZN2sv11attn_kernel").items():
-        assert r["occ"] == 2 and r["spill"] == 0, (name, r)
+        assert r["occ"] == 4 and r["spill"] == 0, (name, r)
 
 
 def test_draft_topk_small_k_four_rows_per_cu():
