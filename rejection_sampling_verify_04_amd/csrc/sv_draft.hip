@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
 // ranked (larger value first, lower id on ties).  More than kTopkCand of
 // them (ties at the top) take k rounds of a block-wide argmax instead.  The
 // softmax normaliser is formed online in the same pass as the maximum, so
-// each vector is reduced as it arrives.
+// each pair of vectors is reduced as it arrives.
 constexpr int kTopkSmallThreads = 256;
 constexpr int kTopkSmallWaves = kTopkSmallThreads / 64;
 constexpr int kTopkSmallVecs = 16;                     // 16-byte vectors per thread
@@ -623,8 +623,9 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
 
   // One pass as the vectors arrive (loads complete in issue order): the row
   // maximum and, online, the softmax normaliser: a running integer offset
-  // c = ceil(max x k2) and the sum of 2^(x k2 - c), eight terms pairwise in
-  // float32 and then in float64, rescaled by exact powers of two when c grows.
+  // c = ceil(max x k2) and the sum of 2^(x k2 - c), sixteen terms (two
+  // vectors) pairwise in float32 and then in float64, rescaled by exact
+  // powers of two when c grows.
   // No branch in this loop: a load whose value crosses a branch join is
   // waited for at the join, which would make the first vector wait for all
   // of them.  Vectors past V read as -inf; a greedy row (k2 = 0) forms its
@@ -632,36 +633,41 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   const float kc = greedy ? 1.0f : k2;
   float m = -__builtin_huge_valf(), c = -__builtin_huge_valf();
   double sacc = 0.0;
+  // two vectors per step: one offset update and one float64 add per 16 logits
 #pragma unroll
-  for (int j = 0; j < kTopkSmallVecs; ++j) {
-    // a vector past V becomes four words of bf16 -inf, once
-    const bool vj = valid(j);
-    const uint32_t kNegInf2 = 0xff80ff80u;
-    raw[j].x = vj ? raw[j].x : kNegInf2;
-    raw[j].y = vj ? raw[j].y : kNegInf2;
-    raw[j].z = vj ? raw[j].z : kNegInf2;
-    raw[j].w = vj ? raw[j].w : kNegInf2;
-    float xv[8];
+  for (int j = 0; j < kTopkSmallVecs; j += 2) {
+    float xv[16];
+    float mp = -__builtin_huge_valf();
 #pragma unroll
-    for (int h = 0; h < 8; ++h) xv[h] = val(j, h);
-    float mj = xv[0];
+    for (int q = 0; q < 2; ++q) {
+      // a vector past V becomes four words of bf16 -inf, once
+      const bool vj = valid(j + q);
+      const uint32_t kNegInf2 = 0xff80ff80u;
+      raw[j + q].x = vj ? raw[j + q].x : kNegInf2;
+      raw[j + q].y = vj ? raw[j + q].y : kNegInf2;
+      raw[j + q].z = vj ? raw[j + q].z : kNegInf2;
+      raw[j + q].w = vj ? raw[j + q].w : kNegInf2;
 #pragma unroll
-    for (int h = 1; h < 8; ++h) mj = fmaxf(mj, xv[h]);
-    s_vm[j][tid] = mj;   // read back by this thread only
-    m = fmaxf(m, mj);
-    const float cn = fmaxf(c, ceilf(mj * kc));
+      for (int h = 0; h < 8; ++h) xv[8 * q + h] = val(j + q, h);
+      float mj = xv[8 * q];
+#pragma unroll
+      for (int h = 1; h < 8; ++h) mj = fmaxf(mj, xv[8 * q + h]);
+      s_vm[j + q][tid] = mj;   // read back by this thread only
+      mp = fmaxf(mp, mj);
+    }
+    m = fmaxf(m, mp);
+    const float cn = fmaxf(c, ceilf(mp * kc));
     sacc = sacc != 0.0 ? scale_pow2(sacc, c - cn) : 0.0;
     c = cn;
     const float cu = c > -__builtin_huge_valf() ? c : 0.0f;   // all -inf so far: terms are 0
-    float t[8];
 #pragma unroll
-    for (int h = 0; h < 8; ++h) t[h] = exp2_hw(fmaf(xv[h], kc, -cu));
+    for (int h = 0; h < 16; ++h) xv[h] = exp2_hw(fmaf(xv[h], kc, -cu));
 #pragma unroll
-    for (int w2 = 4; w2 >= 1; w2 >>= 1) {
+    for (int w2 = 8; w2 >= 1; w2 >>= 1) {
 #pragma unroll
-      for (int h = 0; h < w2; ++h) t[h] = t[2 * h] + t[2 * h + 1];
+      for (int h = 0; h < w2; ++h) xv[h] = xv[2 * h] + xv[2 * h + 1];
     }
-    sacc += (double)t[0];
+    sacc += (double)xv[0];
   }
   fence_raw();
   // the waves' maxima and normalisers (sums brought to the wave's offset)
