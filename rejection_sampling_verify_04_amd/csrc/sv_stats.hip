@@ -138,10 +138,8 @@ __device__ __forceinline__ int wave_kth_bit(unsigned long long m, int k) {
 // that leaf, which forms its statistics itself.  The rows are compacted when
 // the trees' shapes fit in LDS: the units run over the used rows only (the
 // target rows of each tree's inner nodes, then their draft rows), so that
-// every wave gets an equal share of the work whatever the shapes.  With at
-// least 16 waves per tree, each tree has its own waves instead (below), and
-// the masks and the prefix over the batch are not needed.  Otherwise unused
-// rows are skipped as they come.
+// every wave gets an equal share of the work whatever the shapes.  Otherwise
+// unused rows are skipped as they come.
 template <int DT, int RING>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   __shared__ int s_i[kStatsCache + 1];
@@ -163,14 +161,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nc = (uint32_t)a.n_chunks;
   uint32_t total = (uint32_t)a.n_rows * nc;   // < 2^31 (checked by the host)
-  const uint32_t G_all = (gridDim.x - n_gblk) * kWaves;
-  // Trees with at least 16 waves each: wave g serves tree g mod B only, and
-  // builds that tree's inner-node mask itself (one load of its parents; no
-  // barrier, no prefix over the batch).  A tree's units run over its waves.
-  const bool per_tree = a.tree && a.B >= 1 && (uint32_t)a.B * 16u <= G_all;
-  const uint32_t wg = blk * kWaves + wave;
-  const int bw = per_tree ? (int)(wg % (uint32_t)a.B) : 0;
-  const uint32_t G = per_tree ? (G_all - (uint32_t)bw + (uint32_t)a.B - 1u) / (uint32_t)a.B : G_all;
+  const uint32_t G = (gridDim.x - n_gblk) * kWaves;
   const uint32_t Gq = G / nc, Gr = G - Gq * nc;
   const long long rowbytes = (long long)V * SegLoad<DT>::ES;
   auto row_ptr = [&](uint32_t r) -> const char* {
@@ -178,25 +169,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
                      : (const char*)a.rows_b + ((long long)r - a.n_a) * rowbytes;
   };
 
-  const bool cache = !per_tree && a.B <= kStatsCache;
+  const bool cache = a.B <= kStatsCache;
   // Tree rows are read only for nodes with children.
   const bool tree_q = a.tree && a.rows_b;
-  const bool compact = !per_tree && a.tree && a.B <= kInnerCache;
+  const bool compact = a.tree && a.B <= kInnerCache;
 
-  unsigned long long tmask = 0ull;   // per tree: the wave's tree's inner nodes
-  uint32_t tcnt = 0;
-  if (per_tree) {
-    const int N = a.N;
-    const int c = lane < N ? lane : N - 1;
-    const int par = a.parents[(long long)bw * N + c];
-    int nn = a.n_nodes ? load_uniform_i32(a.n_nodes + bw) : N;
-    nn = (nn >= 1 && nn <= N) ? nn : 0;   // a bad count: no row is read
-    const bool kid = lane > 0 && lane < nn && par >= 0 && par < lane;
-    tmask = wave_or_u64(kid ? 1ull << par : 0ull);
-    tcnt = (uint32_t)__popcll(tmask);
-    total = (tree_q ? 2u * tcnt : tcnt) * nc;
-  }
-  uint32_t u = per_tree ? wg / (uint32_t)a.B : wg;
+  uint32_t u = blk * kWaves + wave;
   uint32_t ur = u / nc, ch = u - ur * nc;   // ur: row in the order the units run
 
   SegLoad<DT> ring[RING];
@@ -204,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   // compacted trees, whose row map needs the inner-node masks first.  Trees
   // skipped as they come issue them for row ur; an unused tree row is still
   // allocated, so reading it is harmless.
-  if (a.vec_ok && u < total && !compact && !per_tree) {
+  if (a.vec_ok && u < total && !compact) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(ur), V, (int)ch * kChunk + r * kSubSpan);
   }
@@ -242,11 +220,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   // The row of iteration row x (once the inner masks are known): the x-th
   // used target row, then the used draft rows.
   auto row_of = [&](uint32_t x) -> uint32_t {
-    if (per_tree) {
-      const int N = a.N;
-      if (x < tcnt) return (uint32_t)(bw * N + wave_kth_bit(tmask, (int)x));
-      return (uint32_t)a.n_a + (uint32_t)(bw * N + wave_kth_bit(tmask, (int)(x - tcnt)));
-    }
     if (!compact) return x;
     const int N = a.N;
     if (x < n_t) {
@@ -288,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
   if (u >= total) return;
   uint32_t row = row_of(ur);
-  if ((compact || per_tree) && a.vec_ok) {
+  if (compact && a.vec_ok) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) ring[r].issue(row_ptr(row), V, (int)ch * kChunk + r * kSubSpan);
   }
@@ -297,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   // rows past n_nodes are not, nor the rows of nodes without children.
   // Called by whole waves.
   auto row_used = [&](uint32_t r) -> bool {
-    if (!a.tree || compact || per_tree) return true;
+    if (!a.tree || compact) return true;
     const bool is_q = r >= a.n_a;
     const uint32_t x = is_q ? r - (uint32_t)a.n_a : r;
     const uint32_t b = x / (uint32_t)a.N;

@@ -31,6 +31,17 @@ def test_tree_v32k_full():
     check(d, "tree v32k bf16")
 
 
+def test_tree_v32k_skewed_batch():
+    """The full-size batch with every eighth tree replaced by a 64-node chain
+    (63 rows with children against about 19): the chains' units beyond their
+    own waves run on the shared waves of the vocabulary pass."""
+    d = synth.tree_v32k()
+    d["parents"] = d["parents"].copy()
+    for b in range(0, d["B"], 8):
+        d["parents"][b] = np.arange(-1, d["N"] - 1, dtype=d["parents"].dtype)
+    check(d, "tree v32k bf16, chains in every eighth row")
+
+
 def test_peaked_trees_reach_depth():
     d = synth.peaked_tree()
     gpu, _ = check(d, "peaked V=64 fp32")

@@ -53,6 +53,17 @@ def test_tree_wor_v32k_full():
     check(d, "tree_wor v32k bf16")
 
 
+def test_wor_skewed_batch():
+    """SAMPLED_WOR trees of 64 nodes over V=32000 with two of sixteen replaced
+    by chains: the chains' units beyond their own waves run on the shared
+    waves of the vocabulary pass."""
+    d = synth.tree_wor(seed=41, B=16, N=64, V=32000, draft_sd=3.0, pert=0.5)
+    d["parents"] = d["parents"].copy()
+    for b in (3, 11):
+        d["parents"][b] = np.arange(-1, d["N"] - 1, dtype=d["parents"].dtype)
+    check(d, "V=32000 bf16, two chains")
+
+
 def test_peaked_wor_trees_reject_and_go_deep():
     d = synth.tree_wor(seed=11, B=48, N=21, V=64, draft_sd=6.0, pert=1.0, dtype=synth.F32)
     gpu, ref = check(d, "peaked V=64 fp32")
