@@ -563,9 +563,10 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
 // item of 256 threads per row, so that four rows share a compute unit
 // and their loads and ALU work overlap.  Each thread keeps its 16 vectors
 // (128 logits) packed in registers.  L, the k-th largest of the four waves'
-// maxima, bounds the top k from below; the logits >= L are gathered and
-// ranked (larger value first, lower id on ties).  More than kTopkCand of
-// them (ties at the top) take k rounds of a block-wide argmax instead.  The
+// maxima, bounds the top k from below; each wave gathers its logits >= L
+// and one wave ranks them all (larger value first, lower id on ties).  More
+// than kTopkWaveCand of them in one wave (ties at the top) take k rounds of
+// a block-wide argmax instead.  The
 // softmax normaliser is formed online in the same pass as the maximum, so
 // each pair of vectors is reduced as it arrives.
 constexpr int kTopkSmallThreads = 256;
@@ -573,17 +574,16 @@ constexpr int kTopkSmallWaves = kTopkSmallThreads / 64;
 constexpr int kTopkSmallVecs = 16;                     // 16-byte vectors per thread
 constexpr int kTopkSmallK = kTopkSmallWaves;           // k <= the waves' count
 constexpr int kTopkSmallMaxV = kTopkSmallVecs * kTopkSmallThreads * 8;
+constexpr int kTopkWaveCand = kTopkCand / kTopkSmallWaves;   // candidates ranked per wave
 
 __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     const void* logits, int V, int k, const float* temp, int* tokens, float* logprob) {
   __shared__ float s_wm[kTopkSmallWaves], s_wc[kTopkSmallWaves];
   __shared__ double s_ws[kTopkSmallWaves];
-  __shared__ double s_scan[kTopkSmallWaves];
   __shared__ unsigned long long s_wk[kTopkSmallWaves];
   __shared__ unsigned long long s_top[kTopkSmallK];
-  __shared__ float s_cval[kTopkCand];
-  __shared__ int s_cidx[kTopkCand];
-  __shared__ float s_vm[kTopkSmallVecs][kTopkSmallThreads];   // each vector's maximum
+  __shared__ uint32_t s_ckey[kTopkSmallWaves][kTopkWaveCand];   // each wave's candidates' keys
+  __shared__ uint32_t s_wn[kTopkSmallWaves];                      // and their count
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const char* row = (const char*)logits + (long long)r * V * 2;
@@ -633,11 +633,14 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   const float kc = greedy ? 1.0f : k2;
   float m = -__builtin_huge_valf(), c = -__builtin_huge_valf();
   double sacc = 0.0;
+  // each pair of vectors' maxima, as two bf16 (a maximum of bf16 values is one)
+  uint32_t vmp[kTopkSmallVecs / 2];
   // two vectors per step: one offset update and one float64 add per 16 logits
 #pragma unroll
   for (int j = 0; j < kTopkSmallVecs; j += 2) {
     float xv[16];
     float mp = -__builtin_huge_valf();
+    float mq[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       // a vector past V becomes four words of bf16 -inf, once
@@ -652,9 +655,10 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
       float mj = xv[8 * q];
 #pragma unroll
       for (int h = 1; h < 8; ++h) mj = fmaxf(mj, xv[8 * q + h]);
-      s_vm[j + q][tid] = mj;   // read back by this thread only
+      mq[q] = mj;
       mp = fmaxf(mp, mj);
     }
+    vmp[j / 2] = (__float_as_uint(mq[1]) & 0xFFFF0000u) | (__float_as_uint(mq[0]) >> 16);
     m = fmaxf(m, mp);
     const float cn = fmaxf(c, ceilf(mp * kc));
     sacc = sacc != 0.0 ? scale_pow2(sacc, c - cn) : 0.0;
@@ -696,62 +700,105 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   for (int w = 0; w < kTopkSmallWaves; ++w)
     S += s_ws[w] != 0.0 ? scale_pow2(s_ws[w], s_wc[w] - c_row) : 0.0;
   // the rank-th output: token and log softmax(x / T) = (x k2 - c_row) ln 2 - ln S
-  auto write_out = [&](int rank, float x, int idx) {
+  // (ln S is formed by the writing wave only, after the ranking's barrier)
+  auto write_out = [&](int rank, float x, int idx, double lnS) {
     double lp;
     if (greedy) lp = rank == 0 ? 0.0 : -__builtin_huge_val();
-    else lp = ((double)x * (double)k2 - (double)c_row) * (1.0 / kLog2e) - log(S);
+    else lp = ((double)x * (double)k2 - (double)c_row) * (1.0 / kLog2e) - lnS;
     tokens[(long long)r * k + rank] = idx;
     logprob[(long long)r * k + rank] = (float)lp;
   };
 
-  // the logits >= L; only a vector whose maximum reaches L can hold one
-  uint32_t n_cand = 0u;
+  // the logits >= L; only a vector whose maximum reaches L can hold one.
+  // Each wave gathers its own candidates into its
+  // LDS slots (ballots give the positions: no atomics, no count pass), as
+  // 32-bit keys that order them: the value's order key above the complement
+  // of the id (ids stay below 2^15), so a larger key ranks higher and -0 and
+  // +0 tie on the value.
+  uint32_t vmask = 0u;
 #pragma unroll
   for (int j = 0; j < kTopkSmallVecs; ++j) {
-    if (s_vm[j][tid] >= L) {
+    const float vm = (j & 1) ? bf16_hi(vmp[j / 2]) : bf16_lo(vmp[j / 2]);
+    vmask |= (uint32_t)(vm >= L) << j;
+  }
+  // this thread's vectors inside the row: the first n_in (0..16)
+  const int n_in = (V / 8 - tid + kTopkSmallThreads - 1) / kTopkSmallThreads;
+  vmask &= (1u << n_in) - 1u;
+  uint32_t n_w = 0u;   // the wave's candidates so far (the same in every lane)
 #pragma unroll
-      for (int h = 0; h < 8; ++h) n_cand += (valid(j) && val(j, h) >= L) ? 1u : 0u;
+  for (int j = 0; j < kTopkSmallVecs; ++j) {
+    const bool vj = (vmask >> j) & 1u;
+    if (__ballot(vj) != 0ull) {
+      // the vector's logits >= L as bits, then one slot per set bit: each
+      // round places every lane's lowest remaining bit (ballot positions)
+      uint32_t m8 = 0u;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) m8 |= (uint32_t)(val(j, h) >= L) << h;
+      m8 = vj ? m8 : 0u;
+      for (;;) {
+        const unsigned long long bal = __ballot(m8 != 0u);
+        if (bal == 0ull) break;
+        if (m8 != 0u) {
+          const int h = __builtin_ctz(m8);
+          m8 &= m8 - 1u;
+          const uint32_t at =
+              n_w + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          const int q = h >> 1;
+          const uint32_t word =
+              q == 0 ? raw[j].x : (q == 1 ? raw[j].y : (q == 2 ? raw[j].z : raw[j].w));
+          const uint32_t bits = (h & 1) ? word >> 16 : word & 0xFFFFu;
+          if (at < (uint32_t)kTopkWaveCand)
+            s_ckey[wave][at] = (key_of_bits<1>(bits) << 15) | (0x7FFFu - (uint32_t)index(j, h));
+        }
+        n_w += (uint32_t)__popcll(bal);
+      }
     }
   }
   fence_raw();
-  double c_tot;
-  const uint32_t c_pos =
-      (uint32_t)block_exclusive_scan<kTopkSmallWaves>((double)n_cand, s_scan, &c_tot);
-  const int C = (int)c_tot;
-  if (C <= kTopkCand) {
-    uint32_t at = c_pos;
+  if (lane == 0) s_wn[wave] = n_w;
+  __syncthreads();
+  uint32_t n_max = s_wn[0];
 #pragma unroll
-    for (int j = 0; j < kTopkSmallVecs; ++j) {
-      if (s_vm[j][tid] >= L) {
+  for (int w = 1; w < kTopkSmallWaves; ++w) n_max = max(n_max, s_wn[w]);
+  if (n_max <= (uint32_t)kTopkWaveCand) {
+    // one wave ranks them: k rounds of a wave-wide maximum of the keys, each
+    // below the previous winner (a key is never 0: NaN is no candidate).
+    // Lane l reads the candidates of wave l / 16, from entry l % 16 on.
+    if (wave != 0) return;
+    const double lnS = log(S);
+    const int cw = lane >> 4, e0 = lane & 15;
+    const int nw = (int)s_wn[cw];
+    const uint32_t first = e0 < nw ? s_ckey[cw][e0] : 0u;
+    uint32_t below = ~0u, top = 0u;
+    if (n_max <= 16u) {
+      // one candidate a lane at most: straight-line rounds
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-          const float x = val(j, h);
-          if (valid(j) && x >= L) {
-            s_cval[at] = x;
-            s_cidx[at] = index(j, h);
-            ++at;
-          }
+      for (int i = 0; i < kTopkSmallK; ++i) {
+        const uint32_t best = wave_max_u32(first < below ? first : 0u);
+        top = (i < k && lane == i) ? best : top;
+        below = best;
+      }
+    } else {
+      for (int i = 0; i < k; ++i) {
+        uint32_t best = first < below ? first : 0u;
+        for (int e = e0 + 16; e < nw; e += 16) {
+          const uint32_t key = s_ckey[cw][e];
+          best = (key < below && key > best) ? key : best;
         }
+        best = wave_max_u32(best);
+        top = lane == i ? best : top;
+        below = best;
       }
     }
-    __syncthreads();
-    // rank: larger value first, lower id on ties (values compare -0 == +0)
-    for (int i = tid; i < C; i += kTopkSmallThreads) {
-      const float x = s_cval[i];
-      const int idx = s_cidx[i];
-      int rank = 0;
-      for (int j = 0; j < C; ++j) {
-        const float xj = s_cval[j];
-        rank += xj > x || (xj == x && s_cidx[j] < idx);
-      }
-      if (rank < k) write_out(rank, x, idx);
-    }
+    if (lane < k && top != 0u)
+      write_out(lane, value_of_key<1>(top >> 15), (int)(0x7FFFu - (top & 0x7FFFu)), lnS);
     return;
   }
-  // More than kTopkCand logits tie at the top: k rounds of a block-wide
-  // argmax over the row, read again from memory (this path is rare), each
-  // below the previous winner, on keys (order key of the value, then the
-  // complement of the index: lower id wins a tie).
+  // More than kTopkWaveCand logits of one wave tie at the top: k rounds of
+  // a block-wide argmax over the row, read again from memory (this path is
+  // rare), each below the previous winner, on keys (order key of the value,
+  // then the complement of the index: lower id wins a tie).
   const RowKeys<1> key_at{row};
   unsigned long long below = ~0ull;
   for (int i = 0; i < k; ++i) {
@@ -773,7 +820,7 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   }
   if (tid < k) {
     const unsigned long long b = s_top[tid];
-    write_out(tid, value_of_key<1>((uint32_t)(b >> 32)), (int)(0xFFFFFFFFu - (uint32_t)b));
+    write_out(tid, value_of_key<1>((uint32_t)(b >> 32)), (int)(0xFFFFFFFFu - (uint32_t)b), log(S));
   }
 }
 
