@@ -674,31 +674,38 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     sacc += (double)xv[0];
   }
   fence_raw();
-  // the waves' maxima and normalisers (sums brought to the wave's offset)
-  const float cw = wave_max(c);
-  const double sw = wave_sum(sacc != 0.0 ? scale_pow2(sacc, c - cw) : 0.0);
+  // the waves' maxima and normalisers (sums brought to the wave's offset).
+  // A thread's offset is ceil(m kc) (the rounded product is monotone in m),
+  // so the wave's offset follows from the wave's maximum.
   m = wave_max(m);
+  const float cw = ceilf(m * kc);
+  const double sw = wave_sum(sacc != 0.0 ? scale_pow2(sacc, c - cw) : 0.0);
   if (lane == 0) {
     s_wm[wave] = m;
     s_wc[wave] = cw;
     s_ws[wave] = sw;
   }
   __syncthreads();
+  // lane w < 4 holds wave w's maximum, offset and normaliser
+  const bool wl = lane < kTopkSmallWaves;
+  const float mw = wl ? s_wm[lane] : -__builtin_huge_valf();
+  const float cwl = wl ? s_wc[lane] : -__builtin_huge_valf();
+  const double swl = wl ? s_ws[lane] : 0.0;
   // L: the largest wave maximum with at least k wave maxima at or above it
-  const float mw = lane < kTopkSmallWaves ? s_wm[lane] : -__builtin_huge_valf();
   int ge = 0;
 #pragma unroll
   for (int j = 0; j < kTopkSmallWaves; ++j)
     ge += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), j)) >= mw;
-  const float L = wave_max((lane < kTopkSmallWaves && ge >= k) ? mw : -__builtin_huge_valf());
-  // the row's normaliser: sum_v 2^(x_v k2 - c_row)
-  float c_row = s_wc[0];
+  const float L = wave_max((wl && ge >= k) ? mw : -__builtin_huge_valf());
+  // the row's normaliser: sum_v 2^(x_v k2 - c_row), the waves' sums in wave order
+  float c_row = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cwl), 0));
 #pragma unroll
-  for (int w = 1; w < kTopkSmallWaves; ++w) c_row = fmaxf(c_row, s_wc[w]);
+  for (int w = 1; w < kTopkSmallWaves; ++w)
+    c_row = fmaxf(c_row, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cwl), w)));
+  const double swr = swl != 0.0 ? scale_pow2(swl, cwl - c_row) : 0.0;
   double S = 0.0;
 #pragma unroll
-  for (int w = 0; w < kTopkSmallWaves; ++w)
-    S += s_ws[w] != 0.0 ? scale_pow2(s_ws[w], s_wc[w] - c_row) : 0.0;
+  for (int w = 0; w < kTopkSmallWaves; ++w) S += readlane_f64(swr, w);
   // the rank-th output: token and log softmax(x / T) = (x k2 - c_row) ln 2 - ln S
   // (ln S is formed by the writing wave only, after the ranking's barrier)
   auto write_out = [&](int rank, float x, int idx, double lnS) {
