@@ -751,9 +751,10 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
           const uint32_t at =
               n_w + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-          const int q = h >> 1;
-          const uint32_t word =
-              q == 0 ? raw[j].x : (q == 1 ? raw[j].y : (q == 2 ? raw[j].z : raw[j].w));
+          // the word of logit h: two selects on the bits of h / 2
+          const uint32_t w01 = (h & 2) ? raw[j].y : raw[j].x;
+          const uint32_t w23 = (h & 2) ? raw[j].w : raw[j].z;
+          const uint32_t word = (h & 4) ? w23 : w01;
           const uint32_t bits = (h & 1) ? word >> 16 : word & 0xFFFFu;
           if (at < (uint32_t)kTopkWaveCand)
             s_ckey[wave][at] = (key_of_bits<1>(bits) << 15) | (0x7FFFu - (uint32_t)index(j, h));
@@ -773,13 +774,14 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     // below the previous winner (a key is never 0: NaN is no candidate).
     // Lane l reads the candidates of wave l / 16, from entry l % 16 on.
     if (wave != 0) return;
-    const double lnS = log(S);
     const int cw = lane >> 4, e0 = lane & 15;
     const int nw = (int)s_wn[cw];
     const uint32_t first = e0 < nw ? s_ckey[cw][e0] : 0u;
     uint32_t below = ~0u, top = 0u;
+    double lnS;
     if (n_max <= 16u) {
-      // one candidate a lane at most: straight-line rounds
+      // one candidate a lane at most: straight-line rounds, ln S beside them
+      lnS = log(S);
 #pragma unroll
       for (int i = 0; i < kTopkSmallK; ++i) {
         const uint32_t best = wave_max_u32(first < below ? first : 0u);
@@ -787,6 +789,7 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
         below = best;
       }
     } else {
+      lnS = log(S);
       for (int i = 0; i < k; ++i) {
         uint32_t best = first < below ? first : 0u;
         for (int e = e0 + 16; e < nw; e += 16) {
