@@ -578,7 +578,7 @@ constexpr int kTopkWaveCand = kTopkCand / kTopkSmallWaves;   // candidates ranke
 
 __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     const void* logits, int V, int k, const float* temp, int* tokens, float* logprob) {
-  __shared__ float s_wm[kTopkSmallWaves], s_wc[kTopkSmallWaves];
+  __shared__ float s_wc[kTopkSmallWaves];
   __shared__ double s_ws[kTopkSmallWaves];
   __shared__ unsigned long long s_wk[kTopkSmallWaves];
   __shared__ unsigned long long s_top[kTopkSmallK];
@@ -674,38 +674,44 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     sacc += (double)xv[0];
   }
   fence_raw();
-  // the waves' maxima and normalisers (sums brought to the wave's offset).
-  // A thread's offset is ceil(m kc) (the rounded product is monotone in m),
-  // so the wave's offset follows from the wave's maximum.
-  m = wave_max(m);
-  const float cw = ceilf(m * kc);
-  const double sw = wave_sum(sacc != 0.0 ? scale_pow2(sacc, c - cw) : 0.0);
-  if (lane == 0) {
-    s_wm[wave] = m;
-    s_wc[wave] = cw;
-    s_ws[wave] = sw;
+  // Each wave bounds its own candidates: Lw, the k-th largest of its
+  // threads' maxima (each a bf16 value, never NaN), which at least k of the
+  // wave's logits reach.  A logit of the wave below Lw has k larger ones, so
+  // the row's top k lie among the waves' logits >= their own bounds, and no
+  // barrier comes before the gather.  Lane keys: the maximum's order key
+  // above the lane; k rounds of a wave-wide maximum, each below the last.
+  const uint32_t mkey = (key_of_bits<1>(__float_as_uint(m) >> 16) << 6) | (uint32_t)lane;
+  uint32_t below_m = ~0u, key_top = 0u, key_kth = 0u;
+#pragma unroll
+  for (int i = 0; i < kTopkSmallK; ++i) {
+    const uint32_t best = wave_max_u32(mkey < below_m ? mkey : 0u);
+    key_top = i == 0 ? best : key_top;
+    key_kth = i < k ? best : key_kth;
+    below_m = best;
   }
-  __syncthreads();
-  // lane w < 4 holds wave w's maximum, offset and normaliser
-  const bool wl = lane < kTopkSmallWaves;
-  const float mw = wl ? s_wm[lane] : -__builtin_huge_valf();
-  const float cwl = wl ? s_wc[lane] : -__builtin_huge_valf();
-  const double swl = wl ? s_ws[lane] : 0.0;
-  // L: the largest wave maximum with at least k wave maxima at or above it
-  int ge = 0;
-#pragma unroll
-  for (int j = 0; j < kTopkSmallWaves; ++j)
-    ge += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), j)) >= mw;
-  const float L = wave_max((wl && ge >= k) ? mw : -__builtin_huge_valf());
-  // the row's normaliser: sum_v 2^(x_v k2 - c_row), the waves' sums in wave order
-  float c_row = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cwl), 0));
-#pragma unroll
-  for (int w = 1; w < kTopkSmallWaves; ++w)
-    c_row = fmaxf(c_row, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cwl), w)));
-  const double swr = swl != 0.0 ? scale_pow2(swl, cwl - c_row) : 0.0;
+  const float L = value_of_key<1>(key_kth >> 6);
+  // the wave's maximum, offset and normaliser (the sum brought to the wave's
+  // offset); a thread's offset is ceil(m kc) (the rounded product is
+  // monotone in m), so the wave's offset follows from the wave's maximum
+  const float mw = value_of_key<1>(key_top >> 6);
+  const float cw = ceilf(mw * kc);
+  const double sw = wave_sum(sacc != 0.0 ? scale_pow2(sacc, c - cw) : 0.0);
+  // the row's offset and normaliser, from the waves' (after the barrier):
+  // sum_v 2^(x_v k2 - c_row), the waves' sums in wave order
+  float c_row = 0.0f;
   double S = 0.0;
+  auto row_normaliser = [&]() {
+    const bool wl = lane < kTopkSmallWaves;
+    const float cwl = wl ? s_wc[lane] : -__builtin_huge_valf();
+    const double swl = wl ? s_ws[lane] : 0.0;
+    c_row = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cwl), 0));
 #pragma unroll
-  for (int w = 0; w < kTopkSmallWaves; ++w) S += readlane_f64(swr, w);
+    for (int w = 1; w < kTopkSmallWaves; ++w)
+      c_row = fmaxf(c_row, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cwl), w)));
+    const double swr = swl != 0.0 ? scale_pow2(swl, cwl - c_row) : 0.0;
+#pragma unroll
+    for (int w = 0; w < kTopkSmallWaves; ++w) S += readlane_f64(swr, w);
+  };
   // the rank-th output: token and log softmax(x / T) = (x k2 - c_row) ln 2 - ln S
   // (ln S is formed by the writing wave only, after the ranking's barrier)
   auto write_out = [&](int rank, float x, int idx, double lnS) {
@@ -716,8 +722,8 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     logprob[(long long)r * k + rank] = (float)lp;
   };
 
-  // the logits >= L; only a vector whose maximum reaches L can hold one.
-  // Each wave gathers its own candidates into its
+  // the wave's logits >= L; only a vector whose maximum reaches L can hold
+  // one.  Each wave gathers its own candidates into its
   // LDS slots (ballots give the positions: no atomics, no count pass), as
   // 32-bit keys that order them: the value's order key above the complement
   // of the id (ids stay below 2^15), so a larger key ranks higher and -0 and
@@ -764,7 +770,11 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     }
   }
   fence_raw();
-  if (lane == 0) s_wn[wave] = n_w;
+  if (lane == 0) {
+    s_wc[wave] = cw;
+    s_ws[wave] = sw;
+    s_wn[wave] = n_w;
+  }
   __syncthreads();
   uint32_t n_max = s_wn[0];
 #pragma unroll
@@ -774,9 +784,10 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     // below the previous winner (a key is never 0: NaN is no candidate).
     // Lane l reads the candidates of wave l / 16, from entry l % 16 on.
     if (wave != 0) return;
-    const int cw = lane >> 4, e0 = lane & 15;
-    const int nw = (int)s_wn[cw];
-    const uint32_t first = e0 < nw ? s_ckey[cw][e0] : 0u;
+    row_normaliser();
+    const int cwv = lane >> 4, e0 = lane & 15;
+    const int nw = (int)s_wn[cwv];
+    const uint32_t first = e0 < nw ? s_ckey[cwv][e0] : 0u;
     uint32_t below = ~0u, top = 0u;
     double lnS;
     if (n_max <= 16u) {
@@ -793,7 +804,7 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
       for (int i = 0; i < k; ++i) {
         uint32_t best = first < below ? first : 0u;
         for (int e = e0 + 16; e < nw; e += 16) {
-          const uint32_t key = s_ckey[cw][e];
+          const uint32_t key = s_ckey[cwv][e];
           best = (key < below && key > best) ? key : best;
         }
         best = wave_max_u32(best);
@@ -809,6 +820,7 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   // a block-wide argmax over the row, read again from memory (this path is
   // rare), each below the previous winner, on keys (order key of the value,
   // then the complement of the index: lower id wins a tie).
+  row_normaliser();
   const RowKeys<1> key_at{row};
   unsigned long long below = ~0ull;
   for (int i = 0; i < k; ++i) {
