@@ -628,7 +628,8 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
   // powers of two when c grows.
   // No branch in this loop: a load whose value crosses a branch join is
   // waited for at the join, which would make the first vector wait for all
-  // of them.  Vectors past V read as -inf; a greedy row (k2 = 0) forms its
+  // of them.  A vector past V (its load reads the row's first vector) has
+  // maximum -inf and sum 0, by two selects; a greedy row (k2 = 0) forms its
   // offsets with k2 = 1 and never reads the sum.
   const float kc = greedy ? 1.0f : k2;
   float m = -__builtin_huge_valf(), c = -__builtin_huge_valf();
@@ -643,18 +644,14 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
     float mq[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      // a vector past V becomes four words of bf16 -inf, once
-      const bool vj = valid(j + q);
-      const uint32_t kNegInf2 = 0xff80ff80u;
-      raw[j + q].x = vj ? raw[j + q].x : kNegInf2;
-      raw[j + q].y = vj ? raw[j + q].y : kNegInf2;
-      raw[j + q].z = vj ? raw[j + q].z : kNegInf2;
-      raw[j + q].w = vj ? raw[j + q].w : kNegInf2;
 #pragma unroll
       for (int h = 0; h < 8; ++h) xv[8 * q + h] = val(j + q, h);
       float mj = xv[8 * q];
 #pragma unroll
       for (int h = 1; h < 8; ++h) mj = fmaxf(mj, xv[8 * q + h]);
+      // a vector past V (loaded from the row's start) counts for nothing:
+      // its maximum is -inf and its sum 0
+      mj = valid(j + q) ? mj : -__builtin_huge_valf();
       mq[q] = mj;
       mp = fmaxf(mp, mj);
     }
@@ -667,11 +664,12 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
 #pragma unroll
     for (int h = 0; h < 16; ++h) xv[h] = exp2_hw(fmaf(xv[h], kc, -cu));
 #pragma unroll
-    for (int w2 = 8; w2 >= 1; w2 >>= 1) {
+    for (int w2 = 8; w2 >= 2; w2 >>= 1) {
 #pragma unroll
       for (int h = 0; h < w2; ++h) xv[h] = xv[2 * h] + xv[2 * h + 1];
     }
-    sacc += (double)xv[0];
+    // xv[0], xv[1]: the two vectors' sums
+    sacc += (double)((valid(j) ? xv[0] : 0.0f) + (valid(j + 1) ? xv[1] : 0.0f));
   }
   fence_raw();
   // Each wave bounds its own candidates: Lw, the k-th largest of its
