@@ -655,12 +655,15 @@ __global__ __launch_bounds__(kTopkSmallThreads) void draft_topk_small_kernel(
       mq[q] = mj;
       mp = fmaxf(mp, mj);
     }
-    vmp[j / 2] = (__float_as_uint(mq[1]) & 0xFFFF0000u) | (__float_as_uint(mq[0]) >> 16);
+    // the two maxima's high halves (bytes 2, 3 of each) in one word
+    vmp[j / 2] = __builtin_amdgcn_perm(__float_as_uint(mq[1]), __float_as_uint(mq[0]), 0x07060302u);
     m = fmaxf(m, mp);
     const float cn = fmaxf(c, ceilf(mp * kc));
-    sacc = sacc != 0.0 ? scale_pow2(sacc, c - cn) : 0.0;
+    // the sum is 0 while c is -inf, so its rescale needs no test
+    sacc = scale_pow2(sacc, c - cn);
     c = cn;
-    const float cu = c > -__builtin_huge_valf() ? c : 0.0f;   // all -inf so far: terms are 0
+    // all -inf so far: the offset -FLT_MAX keeps the terms 2^-inf = 0
+    const float cu = fmaxf(c, -__FLT_MAX__);
 #pragma unroll
     for (int h = 0; h < 16; ++h) xv[h] = exp2_hw(fmaf(xv[h], kc, -cu));
 #pragma unroll
