@@ -161,6 +161,49 @@ def test_draft_topk_small_k_path(V):
     say("[control] draft top-k, small-k path V=%d ok" % V)
 
 
+def test_draft_topk_small_k_ties_within_one_wave():
+    """The small-k path bounds each wave's candidates by its own k-th largest
+    thread maximum and ranks all waves' candidates in one wave.  Ties at the
+    top placed inside one wave's logits (logit i belongs to wave
+    ((i / 8) mod 256) / 64): 16 (one ranking round per lane), 17 and 100
+    (more than one candidate per ranking lane), 300 (more than one wave's
+    256 slots: the whole-row rounds), ties split across two waves, and a
+    lower tie value in another wave."""
+    import rejection_sampling_verify_04_amd as sv
+    rng = np.random.default_rng(107)
+    R, V = 8, 32000
+    x = rng.normal(0, 2, size=(R, V)).astype(np.float32)
+    wave_of = ((np.arange(V) // 8) % 256) // 64
+
+    def put(r, w, n, val):
+        pos = rng.choice(np.flatnonzero(wave_of == w), n, replace=False)
+        x[r, pos] = val
+
+    put(0, 0, 16, 9.0)
+    put(1, 1, 17, 9.0)
+    put(2, 2, 100, 9.0)
+    put(3, 3, 300, 9.0)
+    put(4, 0, 10, 9.0)
+    put(4, 3, 10, 9.0)
+    put(5, 1, 3, 9.5)
+    put(5, 2, 40, 9.0)
+    put(6, 2, 2, 9.0)
+    put(6, 0, 2, 9.0)
+    bits = synth.bf16_bits(x)
+    vals = synth.bf16_values(bits).astype(np.float64)
+    T = np.array([1.0, 0.7, 0.0, 1.0, 1.3, 1.0, 0.0, 1.0], dtype=np.float32)
+    for k in (1, 2, 3, 4):
+        tok, lp = sv.draft_topk(logits_to_dev(bits, 1), k, temp=f32(T))
+        tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
+        for r in range(R):
+            rt, rl = OD.topk_candidates(vals[r], k, float(T[r]))
+            assert np.array_equal(tok[r], rt), (k, r, tok[r], rt)
+            fin = np.isfinite(rl)
+            assert np.array_equal(np.isfinite(lp[r]), fin), (k, r, lp[r], rl)
+            assert np.all(np.abs(lp[r][fin] - rl[fin]) <= 1e-5 * np.maximum(1.0, np.abs(rl[fin])))
+    say("[control] draft top-k, ties within one wave ok")
+
+
 def test_draft_topk_heavy_ties():
     """Rows whose top values repeat far more often than k (the whole-row path)."""
     import rejection_sampling_verify_04_amd as sv
