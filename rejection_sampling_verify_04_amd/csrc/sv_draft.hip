@@ -562,13 +562,13 @@ __global__ __launch_bounds__(kFinThreads) void tree_prune_kernel(TreePruneArgs a
 // Small top-k (k <= 4) of bf16 rows of up to 32768 logits, aligned: one work
 // item of 256 threads per row, so that four rows share a compute unit
 // and their loads and ALU work overlap.  Each thread keeps its 16 vectors
-// (128 logits) packed in registers.  L, the k-th largest of the four waves'
-// maxima, bounds the top k from below; each wave gathers its logits >= L
-// and one wave ranks them all (larger value first, lower id on ties).  More
-// than kTopkWaveCand of them in one wave (ties at the top) take k rounds of
-// a block-wide argmax instead.  The
-// softmax normaliser is formed online in the same pass as the maximum, so
-// each pair of vectors is reduced as it arrives.
+// (128 logits) packed in registers.  Each wave gathers its logits at or
+// above its own bound (the k-th largest of its threads' maxima), and after
+// one barrier one wave ranks all of them (larger value first, lower id on
+// ties).  More than kTopkWaveCand of them in one wave (ties at the top)
+// take k rounds of a block-wide argmax instead.  The softmax normaliser is
+// formed online in the same pass as the maximum, so each pair of vectors is
+// reduced as it arrives.
 constexpr int kTopkSmallThreads = 256;
 constexpr int kTopkSmallWaves = kTopkSmallThreads / 64;
 constexpr int kTopkSmallVecs = 16;                     // 16-byte vectors per thread
