@@ -235,6 +235,7 @@ template <int DT>
 __device__ __forceinline__ void stop_weights_from(const StopDist& d, int V, int chunk, int vec_ok,
                                                   uint32_t mask, const StopVec<DT>& r,
                                                   float w[kPerThread], int tix = threadIdx.x) {
+#pragma clang fp contract(off)
   constexpr int EPV = StopVec<DT>::EPV;
   const int e0 = chunk * kChunk + tix * kPerThread;
   float xp[kPerThread], xq[kPerThread];
@@ -265,19 +266,32 @@ __device__ __forceinline__ void stop_weights_from(const StopDist& d, int V, int 
       xq[e] = (need_q && idx < V) ? load_logit<DT>(d.qrow, idx) : 0.0f;
     }
   }
-  // per-element range and mask tests only where they can matter
-  const bool plain = mask == 0u && e0 + kPerThread <= V;
+  // One straight-line loop per case (the cases are uniform over the block),
+  // then the range and mask tests, behind a test of the whole wave, only
+  // where they can matter.  No product is fused into the difference, so
+  // every pass forms the same weights.
+  if (!d.residual) {
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int idx = e0 + e;
-    float p = exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
-    if (d.residual) {
-      const float q = d.q_greedy ? (idx == d.q_amax ? 1.0f : 0.0f)
-                                 : exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
-      p = fmaxf(p - q, 0.0f);
+    for (int e = 0; e < kPerThread; ++e) w[e] = exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
+  } else if (!d.q_greedy) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const float p = exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
+      const float q = exp2_hw(fmaf(xq[e], d.q_k, -d.q_c)) * d.q_inv_s;
+      w[e] = fmaxf(p - q, 0.0f);
     }
-    if (!plain && (idx >= V || ((mask >> e) & 1u))) p = 0.0f;
-    w[e] = p;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const float p = exp2_hw(fmaf(xp[e], d.p_k, -d.p_c)) * d.p_inv_s;
+      w[e] = fmaxf(p - (e0 + e == d.q_amax ? 1.0f : 0.0f), 0.0f);
+    }
+  }
+  const bool plain = mask == 0u && e0 + kPerThread <= V;
+  if (__ballot(!plain) != 0ull) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      if (!plain && (e0 + e >= V || ((mask >> e) & 1u))) w[e] = 0.0f;
   }
 }
 
